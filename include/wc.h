@@ -1,0 +1,165 @@
+/*
+ * wc.h — C ABI of libwc: lossless BF16 sign+exponent coding, exact decode,
+ * and decode fused into GEMV, on AMD Instinct MI355X (gfx950).
+ *
+ * What the operations are (page title, section):
+ *  [P2] "Compresión de pesos LLM sin pérdida vs 8-bit GGUF: ¿qué está listo
+ *       para producción?" — "¿Qué significa “sin pérdida” para los pesos de
+ *       un LLM?" (lossless = every source bit rebuilt; exact BF16 may be
+ *       rebuilt in registers or shared memory and used at once in the matrix
+ *       product) and "¿Qué demostró realmente el experimento con GLM-5.2?"
+ *       (BF16 = sign 1 + exponent 8 + mantissa 7; short codes for frequent
+ *       sign+exponent symbols; rare ones in an exact escape stream).
+ *  [P3] "Prueba de GLM-5.2 reduce la memoria BF16 en casi un 25%" —
+ *       "Cómo funciona la compresión" (K15: 9-bit symbol -> 4-bit code into a
+ *       15-entry table, exact escapes, 7-bit mantissa raw, bits/weight with
+ *       all overhead; byte-split: high byte from dictionary + code indices +
+ *       escape stream, low byte unchanged) and "Qué queda por demostrar"
+ *       (a dense 12-bit prototype rebuilt codes in registers and was timed
+ *       against a BF16 GEMV, with the escape correction kept apart).
+ *
+ * Container (all integers little-endian; every stream starts at a 16-byte
+ * aligned offset; gaps and tails are zero):
+ *   [0,128)          wc_header below
+ *   off_codes (128)  4-bit codes, ceil(n/2) bytes; weight i in byte i/2, the
+ *                    low nibble when i is even; code k < n_dict selects
+ *                    dict[k]; code 15 marks an escape
+ *   off_raw          byte-split: the low byte of every weight, n bytes;
+ *                    K15: the 7-bit mantissas as one LSB-first bitstream,
+ *                    mantissa i at stream bits [7i, 7i+7), ceil(7n/8) bytes
+ *   off_esc_pos      n_esc u32 positions (flat weight index), ascending
+ *   off_esc_sym      n_esc symbols: u8 (byte-split) or u16 (K15)
+ *   total_bytes      end of the container
+ * Symbols: byte-split s = b >> 8 (sign + exponent[7:1]); K15 s = b >> 7
+ * (sign + exponent).  A weight is rebuilt as (s << 8) | low byte, or
+ * (s << 7) | mantissa.  The dictionary holds the min(15, #distinct) most
+ * frequent symbols of the tensor, ties to the smaller symbol; its order is
+ * the code order.  Weights are the tensor's row-major flat order; a matrix
+ * W[rows][cols] multiplies as y = W x (x has cols entries).
+ *
+ * Conventions for every call:
+ *  - Device pointers (d_*) are caller-owned device memory; the library
+ *    allocates nothing and keeps no pointer after returning.  Host pointers
+ *    (h, h_out, results) are caller-owned host memory.
+ *  - d_w, d_container, d_out, d_x must be 16-byte aligned; d_y 4-byte.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  All device work is
+ *    enqueued on it in order and returns without waiting, except
+ *    wc_build_dict, which waits for `stream` once (it reads back 64 bytes).
+ *  - Return value: WC_OK or a negative WC_E_* code; nothing is enqueued when
+ *    an argument check fails.  A device fault shows up at the caller's next
+ *    synchronisation.  No call aborts or throws.
+ */
+#ifndef WC_H
+#define WC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WC_LAYOUT_BYTESPLIT 0
+#define WC_LAYOUT_K15 1
+
+#define WC_OK 0
+#define WC_E_ARG (-1)         /* null pointer, misalignment, bad size/shape */
+#define WC_E_SIZE (-2)        /* n >= 2^32, or a buffer smaller than needed */
+#define WC_E_CORRUPT (-3)     /* header fails validation */
+#define WC_E_HIP (-4)         /* a HIP call or kernel launch failed */
+#define WC_E_UNSUPPORTED (-5) /* batch outside 1..WC_MAX_BATCH */
+
+#define WC_MAGIC 0x36314357u /* bytes "WC16" */
+#define WC_VERSION 1u
+#define WC_HEADER_BYTES 128u
+#define WC_MAX_BATCH 16u
+
+/* Scratch bytes wc_build_dict and wc_encode need for n weights. */
+#define WC_WORKSPACE_BYTES(n) ((size_t)4096 + (size_t)8 * (((uint64_t)(n) + 8191u) / 8192u))
+
+/* The first 128 bytes of every container, byte for byte. */
+typedef struct wc_header {
+  uint32_t magic;       /* WC_MAGIC */
+  uint16_t version;     /* WC_VERSION */
+  uint8_t layout;       /* WC_LAYOUT_* */
+  uint8_t n_dict;       /* dictionary entries, 0..15 */
+  uint64_t n;           /* weights, < 2^32 */
+  uint64_t n_esc;       /* escape records */
+  uint16_t dict[16];    /* symbols by code; entries n_dict..15 are 0 */
+  uint64_t off_codes;   /* = 128 */
+  uint64_t off_raw;     /* = pad16(128 + ceil(n/2)) */
+  uint64_t off_esc_pos; /* = pad16(off_raw + raw bytes) */
+  uint64_t off_esc_sym; /* = pad16(off_esc_pos + 4 n_esc) */
+  uint64_t total_bytes; /* = pad16(off_esc_sym + symbol bytes) */
+  uint8_t reserved[32]; /* zero */
+} wc_header;
+
+/*
+ * Per-tensor dictionary [P3 "Cómo funciona la compresión"; P2 "¿Qué
+ * demostró…"]: counts the sign+exponent symbols of d_w[0..n) (BF16 bit
+ * patterns), takes the top 15 as the dictionary, and fills *h_out with the
+ * complete header of the container wc_encode will write (escape count,
+ * stream offsets and total size included), so the caller can allocate it.
+ * d_work: WC_WORKSPACE_BYTES(n) bytes of device scratch (contents ignored
+ * and overwritten).  Waits for `stream`.  n == 0 is allowed (empty tensor).
+ */
+int wc_build_dict(int layout, const uint16_t *d_w, uint64_t n, void *d_work,
+                  size_t work_bytes, void *stream, wc_header *h_out);
+
+/*
+ * Encode [P3 "Cómo funciona la compresión"]: writes the whole container for
+ * d_w[0..h->n) — header, codes, raw stream, escape positions and symbols —
+ * into d_container[0..h->total_bytes).  *h must be the header wc_build_dict
+ * returned for the same weights (checked for consistency; a header whose
+ * escape count does not match the data yields a container that fails to
+ * decode).  container_bytes >= h->total_bytes; d_work as for wc_build_dict.
+ */
+int wc_encode(const wc_header *h, const uint16_t *d_w, uint8_t *d_container,
+              size_t container_bytes, void *d_work, size_t work_bytes,
+              void *stream);
+
+/*
+ * Exact decode [P3 "Cómo funciona la compresión"; P2 "¿Qué significa “sin
+ * pérdida”…"]: rebuilds the n BF16 bit patterns into d_out[0..n).  *h is the
+ * host copy of the container's header (validated: WC_E_CORRUPT).  Escape
+ * records whose position lies outside the tile being decoded, or past
+ * n_esc, are ignored, so a corrupt stream body cannot make the kernel read
+ * or write outside the container and d_out.
+ */
+int wc_decode(const wc_header *h, const uint8_t *d_container,
+              size_t container_bytes, uint16_t *d_out, void *stream);
+
+/*
+ * Decode fused into GEMV [P2 "¿Qué significa “sin pérdida”…"; P3 "Qué queda
+ * por demostrar"]: y[b][r] = sum_c W[r][c] * x[b][c] with W the container's
+ * weights viewed as [rows][cols] (rows * cols == h->n), rebuilt in registers
+ * with escapes applied and never written to memory.  d_x: BF16 [batch][cols];
+ * d_y: fp32 [batch][rows].  Products are exact (BF16 x BF16), sums are fp32
+ * in an order that differs from a sequential loop.  batch in
+ * 1..WC_MAX_BATCH, else WC_E_UNSUPPORTED.
+ */
+int wc_decode_gemv(const wc_header *h, const uint8_t *d_container,
+                   size_t container_bytes, uint64_t rows, uint64_t cols,
+                   const uint16_t *d_x, uint32_t batch, float *d_y,
+                   void *stream);
+
+/*
+ * Plain BF16 GEMV, the comparison the pages time the fused kernel against
+ * [P3 "Qué queda por demostrar"]: same shapes, types and reduction tree as
+ * wc_decode_gemv, with W read as uncompressed BF16 [rows][cols].
+ */
+int wc_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols,
+                 const uint16_t *d_x, uint32_t batch, float *d_y, void *stream);
+
+/*
+ * Accounting [P3 "Cómo funciona la compresión": bits per weight with all
+ * overhead included]: *bpw = 8 * total_bytes / n (header, dictionary,
+ * streams, padding); *payload_bpw = 8 * (codes + raw + escape bytes) / n.
+ * Host only.  n == 0 -> WC_E_ARG.
+ */
+int wc_bits_per_weight(const wc_header *h, double *bpw, double *payload_bpw);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WC_H */
