@@ -1,0 +1,209 @@
+"""decode_gemv_sign_amd — Python binding of libwc (include/wc.h).
+
+Lossless BF16 sign+exponent coding on AMD MI355X: a per-tensor 15-entry
+dictionary of sign+exponent symbols, 4-bit codes, an exact escape stream,
+and the raw part kept as stored (byte-split: the low byte; K15: the 7-bit
+mantissa) — page "Prueba de GLM-5.2 reduce la memoria BF16 en casi un 25%",
+section "Cómo funciona la compresión" — with exact decode and decode fused
+into GEMV (page "Compresión de pesos LLM sin pérdida vs 8-bit GGUF: ¿qué está
+listo para producción?", section "¿Qué significa “sin pérdida” para los pesos
+de un LLM?").
+
+This module only marshals arguments: every step runs in the HIP kernels of
+libwc.so, on the caller's current torch stream.  PyTorch provides device
+memory and streams.  There is no CPU fallback: importing this package
+without a built libwc.so raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first, so libwc binds to the HIP runtime torch already uses
+
+__all__ = [
+    "BYTESPLIT", "K15", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into",
+    "encode", "decode", "decode_gemv", "gemv_bf16", "bits_per_weight", "read_header",
+    "LIB_PATH",
+]
+
+BYTESPLIT = 0
+K15 = 1
+MAX_BATCH = 16
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwc.so")
+
+_CODES = {0: "WC_OK", -1: "WC_E_ARG", -2: "WC_E_SIZE", -3: "WC_E_CORRUPT", -4: "WC_E_HIP",
+          -5: "WC_E_UNSUPPORTED"}
+
+
+class WCError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {_CODES.get(code, code)}")
+        self.code = code
+
+
+class Header(ctypes.Structure):
+    """wc_header: the first 128 bytes of every container."""
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("version", ctypes.c_uint16), ("layout", ctypes.c_uint8),
+        ("n_dict", ctypes.c_uint8), ("n", ctypes.c_uint64), ("n_esc", ctypes.c_uint64),
+        ("dict", ctypes.c_uint16 * 16), ("off_codes", ctypes.c_uint64),
+        ("off_raw", ctypes.c_uint64), ("off_esc_pos", ctypes.c_uint64),
+        ("off_esc_sym", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
+        ("reserved", ctypes.c_uint8 * 32),
+    ]
+
+    def to_bytes(self) -> bytes:
+        return ctypes.string_at(ctypes.addressof(self), ctypes.sizeof(self))
+
+    @classmethod
+    def from_bytes(cls, b: bytes) -> "Header":
+        if len(b) < 128:
+            raise ValueError("a header is 128 bytes")
+        return cls.from_buffer_copy(bytes(b[:128]))
+
+
+assert ctypes.sizeof(Header) == 128
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m decode_gemv_sign_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    U64 = ctypes.c_uint64
+    HP = ctypes.POINTER(Header)
+    lib.wc_build_dict.argtypes = [ctypes.c_int, P, U64, P, ctypes.c_size_t, P, HP]
+    lib.wc_encode.argtypes = [HP, P, P, ctypes.c_size_t, P, ctypes.c_size_t, P]
+    lib.wc_decode.argtypes = [HP, P, ctypes.c_size_t, P, P]
+    lib.wc_decode_gemv.argtypes = [HP, P, ctypes.c_size_t, U64, U64, P, ctypes.c_uint32, P, P]
+    lib.wc_gemv_bf16.argtypes = [P, U64, U64, P, ctypes.c_uint32, P, P]
+    lib.wc_bits_per_weight.argtypes = [HP, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)]
+    for f in (lib.wc_build_dict, lib.wc_encode, lib.wc_decode, lib.wc_decode_gemv,
+              lib.wc_gemv_bf16, lib.wc_bits_per_weight):
+        f.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise WCError(st, what)
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bits16(t: torch.Tensor, what: str) -> torch.Tensor:
+    """A contiguous 16-bit CUDA tensor viewed as raw BF16 bit patterns."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{what} must hold BF16 bit patterns (bfloat16, int16 or uint16)")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() else 0)
+
+
+def workspace_bytes(n: int) -> int:
+    """WC_WORKSPACE_BYTES(n)."""
+    return 4096 + 8 * ((n + 8191) // 8192)
+
+
+def _workspace(n: int, device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(n), dtype=torch.uint8, device=device)
+
+
+def build_dict(w: torch.Tensor, layout: int, work: torch.Tensor | None = None,
+               stream=None) -> Header:
+    """wc_build_dict: dictionary + complete container header for w (waits)."""
+    w = _bits16(w, "w")
+    n = w.numel()
+    if work is None:
+        work = _workspace(n, w.device)
+    h = Header()
+    _check(_lib.wc_build_dict(layout, _ptr(w), n, _ptr(work), work.numel(), _stream(stream),
+                              ctypes.byref(h)), "wc_build_dict")
+    return h
+
+
+def encode_into(h: Header, w: torch.Tensor, container: torch.Tensor,
+                work: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """wc_encode into a caller-allocated uint8 container (asynchronous)."""
+    w = _bits16(w, "w")
+    if work is None:
+        work = _workspace(w.numel(), w.device)
+    _check(_lib.wc_encode(ctypes.byref(h), _ptr(w), _ptr(container), container.numel(),
+                          _ptr(work), work.numel(), _stream(stream)), "wc_encode")
+    return container
+
+
+def encode(w: torch.Tensor, layout: int, stream=None):
+    """(header, container): dictionary, then the whole container on the device."""
+    w = _bits16(w, "w")
+    work = _workspace(w.numel(), w.device)
+    h = build_dict(w, layout, work, stream)
+    c = torch.empty(h.total_bytes, dtype=torch.uint8, device=w.device)
+    encode_into(h, w, c, work, stream)
+    return h, c
+
+
+def read_header(container: torch.Tensor) -> Header:
+    """Copy a container's first 128 bytes back to the host (synchronises)."""
+    return Header.from_bytes(container[:128].cpu().numpy().tobytes())
+
+
+def decode(h: Header, container: torch.Tensor, out: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """wc_decode: the n BF16 bit patterns (int16 tensor unless `out` is given)."""
+    if out is None:
+        out = torch.empty(h.n, dtype=torch.int16, device=container.device)
+    out = _bits16(out, "out")
+    _check(_lib.wc_decode(ctypes.byref(h), _ptr(container), container.numel(), _ptr(out),
+                          _stream(stream)), "wc_decode")
+    return out
+
+
+def decode_gemv(h: Header, container: torch.Tensor, rows: int, cols: int, x: torch.Tensor,
+                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """wc_decode_gemv: y [batch, rows] fp32 for x [batch, cols] BF16."""
+    x = _bits16(x, "x")
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    if out is None:
+        out = torch.empty((batch, rows), dtype=torch.float32, device=container.device)
+    _check(_lib.wc_decode_gemv(ctypes.byref(h), _ptr(container), container.numel(), rows, cols,
+                               _ptr(x), batch, _ptr(out), _stream(stream)), "wc_decode_gemv")
+    return out
+
+
+def gemv_bf16(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """wc_gemv_bf16: plain BF16 GEMV, W [rows, cols], x [batch, cols] -> [batch, rows]."""
+    w = _bits16(w, "w")
+    x = _bits16(x, "x")
+    rows, cols = w.shape
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    if out is None:
+        out = torch.empty((batch, rows), dtype=torch.float32, device=w.device)
+    _check(_lib.wc_gemv_bf16(_ptr(w), rows, cols, _ptr(x), batch, _ptr(out), _stream(stream)),
+           "wc_gemv_bf16")
+    return out
+
+
+def bits_per_weight(h: Header):
+    """(bits/weight with all overhead, payload bits/weight)."""
+    b = ctypes.c_double()
+    p = ctypes.c_double()
+    _check(_lib.wc_bits_per_weight(ctypes.byref(h), ctypes.byref(b), ctypes.byref(p)),
+           "wc_bits_per_weight")
+    return b.value, p.value

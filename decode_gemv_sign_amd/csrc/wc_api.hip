@@ -1,0 +1,117 @@
+// wc_api.hip — the C ABI of libwc (declared and documented in include/wc.h).
+//
+// Argument checks happen here, before anything is enqueued; kernels and
+// launch geometry live in wc_encode.hip, wc_decode.hip and wc_gemv.hip.
+// The library allocates no device or host memory: every buffer is the
+// caller's.
+#include <string.h>
+
+#include "wc_launch.h"
+
+static_assert(sizeof(wc_header) == WC_HEADER_BYTES, "wc_header must be exactly 128 bytes");
+static_assert(sizeof(wc::DictResult) == 48, "DictResult layout");
+
+namespace {
+
+int hip_status(hipError_t e) { return e == hipSuccess ? WC_OK : WC_E_HIP; }
+
+bool layout_ok(int layout) { return layout == WC_LAYOUT_BYTESPLIT || layout == WC_LAYOUT_K15; }
+
+}  // namespace
+
+extern "C" int wc_build_dict(int layout, const uint16_t* d_w, uint64_t n, void* d_work,
+                             size_t work_bytes, void* stream, wc_header* h_out) {
+  if (!h_out || !layout_ok(layout)) return WC_E_ARG;
+  if (n >= (1ull << 32)) return WC_E_SIZE;
+  if (n && (!d_w || !wc::aligned16(d_w))) return WC_E_ARG;
+  if (!d_work || !wc::aligned16(d_work)) return WC_E_ARG;
+  if (work_bytes < WC_WORKSPACE_BYTES(n)) return WC_E_SIZE;
+  hipStream_t s = (hipStream_t)stream;
+
+  wc::DictResult r;
+  memset(&r, 0, sizeof r);
+  if (n) {
+    hipError_t e = wc::launch_build_dict(layout, d_w, n, (uint8_t*)d_work, s);
+    if (e != hipSuccess) return WC_E_HIP;
+    e = hipMemcpyAsync(&r, (uint8_t*)d_work + wc::kWorkResult, sizeof r, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return WC_E_HIP;
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return WC_E_HIP;
+    if (r.n_dict > 15 || r.n_esc > n) return WC_E_HIP;  // not a valid result: the device work failed
+  }
+  wc_header h;
+  memset(&h, 0, sizeof h);
+  h.magic = WC_MAGIC;
+  h.version = WC_VERSION;
+  h.layout = (uint8_t)layout;
+  h.n_dict = (uint8_t)r.n_dict;
+  h.n = n;
+  h.n_esc = r.n_esc;
+  for (int k = 0; k < 16; ++k) h.dict[k] = k < (int)r.n_dict ? r.dict[k] : 0;
+  const wc::Geometry g = wc::geometry(layout, n, r.n_esc);
+  h.off_codes = g.off_codes;
+  h.off_raw = g.off_raw;
+  h.off_esc_pos = g.off_esc_pos;
+  h.off_esc_sym = g.off_esc_sym;
+  h.total_bytes = g.total;
+  *h_out = h;
+  return WC_OK;
+}
+
+extern "C" int wc_encode(const wc_header* h, const uint16_t* d_w, uint8_t* d_container,
+                         size_t container_bytes, void* d_work, size_t work_bytes, void* stream) {
+  if (!h || !d_container || !wc::aligned16(d_container)) return WC_E_ARG;
+  const int v = wc::validate_header(h);
+  if (v != WC_OK) return v;
+  if (h->n && (!d_w || !wc::aligned16(d_w))) return WC_E_ARG;
+  if (!d_work || !wc::aligned16(d_work)) return WC_E_ARG;
+  if (work_bytes < WC_WORKSPACE_BYTES(h->n) || container_bytes < h->total_bytes) return WC_E_SIZE;
+  return hip_status(wc::launch_encode(*h, d_w, d_container, (uint8_t*)d_work, (hipStream_t)stream));
+}
+
+extern "C" int wc_decode(const wc_header* h, const uint8_t* d_container, size_t container_bytes,
+                         uint16_t* d_out, void* stream) {
+  if (!h || !d_container || !wc::aligned16(d_container)) return WC_E_ARG;
+  const int v = wc::validate_header(h);
+  if (v != WC_OK) return v;
+  if (container_bytes < h->total_bytes) return WC_E_SIZE;
+  if (h->n && (!d_out || !wc::aligned16(d_out))) return WC_E_ARG;
+  return hip_status(wc::launch_decode(*h, d_container, d_out, (hipStream_t)stream));
+}
+
+extern "C" int wc_decode_gemv(const wc_header* h, const uint8_t* d_container,
+                              size_t container_bytes, uint64_t rows, uint64_t cols,
+                              const uint16_t* d_x, uint32_t batch, float* d_y, void* stream) {
+  if (!h || !d_container || !wc::aligned16(d_container)) return WC_E_ARG;
+  const int v = wc::validate_header(h);
+  if (v != WC_OK) return v;
+  if (container_bytes < h->total_bytes) return WC_E_SIZE;
+  if (batch < 1 || batch > WC_MAX_BATCH) return WC_E_UNSUPPORTED;
+  if (cols && rows > h->n / cols) return WC_E_ARG;
+  if (rows * cols != h->n) return WC_E_ARG;
+  if (rows && (!d_y || ((uintptr_t)d_y & 3u))) return WC_E_ARG;
+  if (rows && cols && (!d_x || !wc::aligned16(d_x))) return WC_E_ARG;
+  return hip_status(
+      wc::launch_decode_gemv(*h, d_container, rows, cols, d_x, batch, d_y, (hipStream_t)stream));
+}
+
+extern "C" int wc_gemv_bf16(const uint16_t* d_w, uint64_t rows, uint64_t cols, const uint16_t* d_x,
+                            uint32_t batch, float* d_y, void* stream) {
+  if (batch < 1 || batch > WC_MAX_BATCH) return WC_E_UNSUPPORTED;
+  if (cols && rows >= (1ull << 62) / cols) return WC_E_SIZE;
+  if (rows && (!d_y || ((uintptr_t)d_y & 3u))) return WC_E_ARG;
+  if (rows && cols && (!d_w || !d_x || !wc::aligned16(d_w) || !wc::aligned16(d_x))) return WC_E_ARG;
+  return hip_status(wc::launch_gemv_bf16(d_w, rows, cols, d_x, batch, d_y, (hipStream_t)stream));
+}
+
+extern "C" int wc_bits_per_weight(const wc_header* h, double* bpw, double* payload_bpw) {
+  if (!h || !bpw || !payload_bpw) return WC_E_ARG;
+  const int v = wc::validate_header(h);
+  if (v != WC_OK) return v;
+  if (h->n == 0) return WC_E_ARG;
+  const uint64_t payload = (h->n + 1u) / 2u + wc::raw_bytes(h->layout, h->n) + 4u * h->n_esc +
+                           wc::sym_bytes(h->layout) * h->n_esc;
+  *bpw = 8.0 * (double)h->total_bytes / (double)h->n;
+  *payload_bpw = 8.0 * (double)payload / (double)h->n;
+  return WC_OK;
+}

@@ -1,0 +1,160 @@
+// wc_common.h — library-internal definitions shared by the HIP kernels and
+// the C-ABI layer of libwc (gfx950, wave64).
+//
+// Container layout and symbol definitions follow include/wc.h, which cites
+// the pages: "Prueba de GLM-5.2 reduce la memoria BF16 en casi un 25%",
+// section "Cómo funciona la compresión" (byte-split and K15 layouts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wc.h"
+
+namespace wc {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;              // CDNA wavefront width
+constexpr int kChunk = 32;             // weights per lane per step: 16 B of codes
+constexpr int kTile = kWave * kChunk;  // weights per wave per step (2048)
+constexpr int kBlockThreads = 256;     // 4 waves per workgroup
+constexpr int kPackBlock = kBlockThreads * kChunk;  // weights per encode block (8192)
+
+// ---- container geometry (host + device) ---------------------------------
+
+__host__ __device__ inline uint64_t pad16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
+__host__ __device__ inline int sym_shift(int layout) { return layout == WC_LAYOUT_K15 ? 7 : 8; }
+__host__ __device__ inline uint64_t raw_bytes(int layout, uint64_t n) {
+  return layout == WC_LAYOUT_K15 ? (7u * n + 7u) / 8u : n;
+}
+__host__ __device__ inline uint64_t sym_bytes(int layout) { return layout == WC_LAYOUT_K15 ? 2u : 1u; }
+
+struct Geometry {
+  uint64_t off_codes, off_raw, off_esc_pos, off_esc_sym, total;
+};
+
+__host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_esc) {
+  Geometry g;
+  g.off_codes = WC_HEADER_BYTES;
+  g.off_raw = pad16(g.off_codes + (n + 1u) / 2u);
+  g.off_esc_pos = pad16(g.off_raw + raw_bytes(layout, n));
+  g.off_esc_sym = pad16(g.off_esc_pos + 4u * n_esc);
+  g.total = pad16(g.off_esc_sym + sym_bytes(layout) * n_esc);
+  return g;
+}
+
+// Dictionary as kernel argument: symbol per code, slot 15 (escape) = 0, so a
+// rebuilt escape holds only its raw bits until it is patched.
+struct Dict {
+  uint16_t sym[16];
+  uint32_t n_dict;
+};
+
+// ---- wave primitives -----------------------------------------------------
+
+__device__ inline int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ inline float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Exclusive prefix sum across the wave.
+__device__ inline uint32_t wave_excl_scan_u32(uint32_t v) {
+  const int lane = lane_id();
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// First index i in [0, count) with pos[i] >= t (count if none), found by the
+// whole wave: each round probes 64 evenly spaced entries and keeps the one
+// interval that can hold the answer.  Every round shrinks the interval, so it
+// ends even on an unsorted (corrupt) array.  Result is wave-uniform.
+__device__ inline uint64_t wave_lower_bound(const uint32_t* __restrict__ pos, uint64_t count,
+                                            uint64_t t) {
+  const int lane = lane_id();
+  uint64_t lo = 0, hi = count;
+  while (hi - lo > (uint64_t)kWave) {
+    const uint64_t step = (hi - lo + kWave - 1) / kWave;
+    const uint64_t idx = lo + (uint64_t)lane * step;
+    const bool below = idx < hi && (uint64_t)pos[idx] < t;
+    const uint64_t k = (uint64_t)__popcll(__ballot(below));
+    if (k == 0) return lo;
+    const uint64_t nlo = lo + (k - 1) * step + 1;
+    const uint64_t nhi = lo + k * step;
+    lo = nlo;
+    hi = nhi < hi ? nhi : hi;
+  }
+  const uint64_t idx = lo + (uint64_t)lane;
+  const bool below = idx < hi && (uint64_t)pos[idx] < t;
+  return lo + (uint64_t)__popcll(__ballot(below));
+}
+
+// Per-lane count of code-15 nibbles in four code dwords (32 codes).
+__device__ inline uint32_t count_escapes(const u32x4& c) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = c[q];
+    n += __popc(w & (w >> 1) & (w >> 2) & (w >> 3) & 0x11111111u);
+  }
+  return n;
+}
+
+// ---- host-side checks ----------------------------------------------------
+
+// WC_OK when *h is exactly the header the format defines for its fields.
+inline int validate_header(const wc_header* h) {
+  if (h->magic != WC_MAGIC || h->version != WC_VERSION) return WC_E_CORRUPT;
+  if (h->layout != WC_LAYOUT_BYTESPLIT && h->layout != WC_LAYOUT_K15) return WC_E_CORRUPT;
+  if (h->n_dict > 15) return WC_E_CORRUPT;
+  if (h->n >= (1ull << 32) || h->n_esc > h->n) return WC_E_CORRUPT;
+  const uint32_t nsym = h->layout == WC_LAYOUT_K15 ? 512u : 256u;
+  for (int k = 0; k < 16; ++k) {
+    if (k >= h->n_dict) {
+      if (h->dict[k] != 0) return WC_E_CORRUPT;
+      continue;
+    }
+    if (h->dict[k] >= nsym) return WC_E_CORRUPT;
+    for (int j = 0; j < k; ++j)
+      if (h->dict[j] == h->dict[k]) return WC_E_CORRUPT;
+  }
+  const Geometry g = geometry(h->layout, h->n, h->n_esc);
+  if (h->off_codes != g.off_codes || h->off_raw != g.off_raw || h->off_esc_pos != g.off_esc_pos ||
+      h->off_esc_sym != g.off_esc_sym || h->total_bytes != g.total)
+    return WC_E_CORRUPT;
+  for (int k = 0; k < 32; ++k)
+    if (h->reserved[k] != 0) return WC_E_CORRUPT;
+  return WC_OK;
+}
+
+inline Dict dict_of(const wc_header* h) {
+  Dict d;
+  for (int k = 0; k < 16; ++k) d.sym[k] = (k < h->n_dict && k < 15) ? h->dict[k] : 0;
+  d.n_dict = h->n_dict;
+  return d;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace wc

@@ -1,0 +1,341 @@
+// wc_encode.hip — per-tensor dictionary and container encode.
+//
+// Page "Compresión de pesos LLM sin pérdida vs 8-bit GGUF: ¿qué está listo
+// para producción?", section "¿Qué demostró realmente el experimento con
+// GLM-5.2?": trained weights reuse few sign+exponent combinations, so the
+// frequent symbols get short codes and the rare ones an exact escape stream.
+// Page "Prueba de GLM-5.2 reduce la memoria BF16 en casi un 25%", section
+// "Cómo funciona la compresión": a 4-bit code into a 15-entry table per
+// weight; byte-split keeps the low byte, K15 the 7-bit mantissa.
+//
+// Kernels, in stream order:
+//   build_dict: k_zero_hist -> k_hist (512 bins of b >> 7; the byte-split
+//               histogram is the pair sum) -> k_top15 (rank by count desc,
+//               symbol asc) -> 48-byte result copied to the host.
+//   encode:     k_pack (codes, raw stream, per-block escape counts, header and
+//               zero gaps) -> k_scan (exclusive scan of the block counts) ->
+//               k_emit (escape positions and symbols in weight order).
+// Every output byte is a pure function of the input, so the container is
+// byte-identical from run to run.
+#include "wc_launch.h"
+
+namespace wc {
+
+// ---- histogram -----------------------------------------------------------
+
+constexpr int kHistCopies = 16;   // replicated sub-histograms per workgroup
+constexpr int kHistStride = 513;  // odd stride: copies of a bin sit in different LDS banks
+
+__global__ void k_zero_hist(uint32_t* hist) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < 512) hist[i] = 0;
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_hist(const uint16_t* __restrict__ w, uint64_t n,
+                                                        uint32_t* __restrict__ hist) {
+  __shared__ uint32_t sub[kHistCopies * kHistStride];
+  for (int i = threadIdx.x; i < kHistCopies * kHistStride; i += kBlockThreads) sub[i] = 0;
+  __syncthreads();
+  // lanes spread over the copies, so the few very frequent symbols of a
+  // skewed tensor do not serialise on one LDS address
+  uint32_t* mine = sub + (lane_id() & (kHistCopies - 1)) * kHistStride;
+  const uint64_t stride = (uint64_t)gridDim.x * kBlockThreads;
+  const uint64_t gid = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  const uint64_t nvec = n / 8;
+  const u32x4* wv = (const u32x4*)w;
+  for (uint64_t v = gid; v < nvec; v += stride) {
+    const u32x4 d = __builtin_nontemporal_load(wv + v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      atomicAdd(mine + ((d[k] >> 7) & 0x1FFu), 1u);
+      atomicAdd(mine + (d[k] >> 23), 1u);
+    }
+  }
+  for (uint64_t i = nvec * 8 + gid; i < n; i += stride) atomicAdd(mine + (w[i] >> 7), 1u);
+  __syncthreads();
+  for (int b = threadIdx.x; b < 512; b += kBlockThreads) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) s += sub[c * kHistStride + b];
+    if (s) atomicAdd(hist + b, s);
+  }
+}
+
+// ---- top-15 --------------------------------------------------------------
+// One workgroup of 512 threads, one symbol each: rank = number of symbols
+// with a larger count, or an equal count and a smaller value.  Symbols of
+// rank < 15 with a nonzero count form the dictionary in rank order.
+
+__global__ __launch_bounds__(512) void k_top15(const uint32_t* __restrict__ hist, int layout,
+                                               uint64_t n, DictResult* __restrict__ res) {
+  __shared__ uint32_t cnt[512];
+  __shared__ uint16_t dict[16];
+  __shared__ uint32_t wsum[8];
+  __shared__ uint32_t wnum[8];
+  const int i = threadIdx.x;
+  const int nsym = layout == WC_LAYOUT_K15 ? 512 : 256;
+  uint32_t c = 0;
+  if (i < nsym) c = layout == WC_LAYOUT_K15 ? hist[i] : hist[2 * i] + hist[2 * i + 1];
+  cnt[i] = c;
+  if (i < 16) dict[i] = 0;
+  __syncthreads();
+  uint32_t rank = 0;
+  for (int j = 0; j < nsym; ++j) {
+    const uint32_t cj = cnt[j];
+    rank += (cj > c || (cj == c && j < i)) ? 1u : 0u;
+  }
+  const bool in = i < nsym && c > 0 && rank < 15;
+  if (in) dict[rank] = (uint16_t)i;
+  const uint32_t s = wave_sum_u32(in ? c : 0u);
+  const uint32_t k = wave_sum_u32(in ? 1u : 0u);
+  if (lane_id() == 0) {
+    wsum[i / kWave] = s;
+    wnum[i / kWave] = k;
+  }
+  __syncthreads();
+  if (i == 0) {
+    uint64_t covered = 0;
+    uint32_t nd = 0;
+    for (int q = 0; q < 8; ++q) {
+      covered += wsum[q];
+      nd += wnum[q];
+    }
+    res->n_dict = nd;
+    res->reserved = 0;
+    res->n_esc = n - covered;
+    for (int q = 0; q < 16; ++q) res->dict[q] = dict[q];
+  }
+}
+
+hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t* work,
+                             hipStream_t s) {
+  uint32_t* hist = (uint32_t*)(work + kWorkHist);
+  hipLaunchKernelGGL(k_zero_hist, dim3(2), dim3(256), 0, s, hist);
+  const uint64_t nvec = n / 8;
+  uint64_t blocks = (nvec + kBlockThreads - 1) / kBlockThreads;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(k_hist, dim3((unsigned)blocks), dim3(kBlockThreads), 0, s, w, n, hist);
+  hipLaunchKernelGGL(k_top15, dim3(1), dim3(512), 0, s, hist, layout, n,
+                     (DictResult*)(work + kWorkResult));
+  return hipGetLastError();
+}
+
+// ---- pack ----------------------------------------------------------------
+
+struct PackArgs {
+  const uint16_t* w;
+  uint8_t* container;
+  uint32_t* blk_cnt;
+  uint64_t n;
+  wc_header h;
+};
+
+template <int LAYOUT>
+__global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
+  __shared__ uint8_t lut[512];
+  __shared__ uint32_t wsum[kBlockThreads / kWave];
+  const int tid = threadIdx.x;
+  for (int sidx = tid; sidx < 512; sidx += kBlockThreads) lut[sidx] = 15;
+  __syncthreads();
+  if (tid < (int)a.h.n_dict) lut[a.h.dict[tid]] = (uint8_t)tid;
+  __syncthreads();
+
+  const wc_header& h = a.h;
+  uint8_t* codes = a.container + h.off_codes;
+  uint8_t* raw = a.container + h.off_raw;
+  const uint64_t raw_pad = pad16(raw_bytes(LAYOUT, a.n));
+  const uint64_t chunk = (uint64_t)blockIdx.x * kBlockThreads + (uint64_t)tid;
+  const uint64_t base = chunk * kChunk;
+  uint32_t esc = 0;
+  if (base < a.n) {
+    const uint32_t valid = a.n - base >= kChunk ? kChunk : (uint32_t)(a.n - base);
+    uint32_t wd[16];  // weights 2j (low half) and 2j+1 (high half)
+    if (valid == kChunk) {
+      const u32x4* src = (const u32x4*)(a.w + base);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 v = __builtin_nontemporal_load(src + k);
+        wd[4 * k] = v[0]; wd[4 * k + 1] = v[1]; wd[4 * k + 2] = v[2]; wd[4 * k + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t lo = (uint32_t)(2 * j) < valid ? a.w[base + 2 * j] : 0u;
+        const uint32_t hi = (uint32_t)(2 * j + 1) < valid ? a.w[base + 2 * j + 1] : 0u;
+        wd[j] = lo | (hi << 16);
+      }
+    }
+    // codes: nibble i of the chunk = code of weight i (even weight in the low nibble)
+    uint32_t cd[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const uint32_t b = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const uint32_t code = (uint32_t)i < valid ? lut[b >> (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)] : 0u;
+      esc += code == 15u ? 1u : 0u;
+      cd[i >> 3] |= code << (4 * (i & 7));
+    }
+    *(u32x4*)(codes + 16u * chunk) = u32x4{cd[0], cd[1], cd[2], cd[3]};
+    if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
+      // low bytes of weights 4m..4m+3 from two input dwords
+      uint32_t rw[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) rw[m] = __builtin_amdgcn_perm(wd[2 * m + 1], wd[2 * m], 0x06040200u);
+      if (valid < kChunk) {
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+          if ((uint32_t)i >= valid) rw[i >> 2] &= ~(0xFFu << (8 * (i & 3)));
+      }
+      const uint64_t off = 32u * chunk;
+      if (off + 16u <= raw_pad) *(u32x4*)(raw + off) = u32x4{rw[0], rw[1], rw[2], rw[3]};
+      if (off + 32u <= raw_pad) *(u32x4*)(raw + off + 16u) = u32x4{rw[4], rw[5], rw[6], rw[7]};
+    } else {
+      // mantissa i at bits [7i, 7i+7) of the chunk's 224-bit window
+      uint32_t rw[7] = {0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        const uint32_t m = (uint32_t)i < valid ? (wd[i >> 1] >> (16 * (i & 1))) & 0x7Fu : 0u;
+        const int bit = 7 * i, d = bit >> 5, s = bit & 31;
+        rw[d] |= m << s;
+        if (s > 25) rw[d + 1] |= m >> (32 - s);
+      }
+      const uint64_t off = 28u * chunk;
+#pragma unroll
+      for (int k = 0; k < 7; ++k)
+        if (off + 4u * k + 4u <= raw_pad) *(uint32_t*)(raw + off + 4u * k) = rw[k];
+    }
+  }
+  // escape count of the block
+  const uint32_t ws = wave_sum_u32(esc);
+  if (lane_id() == 0) wsum[tid / kWave] = ws;
+  __syncthreads();
+  if (tid == 0 && (uint64_t)blockIdx.x * kPackBlock < a.n) {  // n == 0 has no blocks to count
+    uint32_t t = 0;
+    for (int q = 0; q < kBlockThreads / kWave; ++q) t += wsum[q];
+    a.blk_cnt[blockIdx.x] = t;
+  }
+  // header and the zero gaps no chunk writes
+  if (blockIdx.x == 0) {
+    if (tid < 32) ((uint32_t*)a.container)[tid] = ((const uint32_t*)&a.h)[tid];
+    if (tid == 32) {
+      const uint64_t nchunks = (a.n + kChunk - 1) / kChunk;
+      const uint64_t written = LAYOUT == WC_LAYOUT_K15 ? 28u * nchunks : raw_pad;
+      for (uint64_t o = written; o < raw_pad; ++o) raw[o] = 0;
+      const uint64_t pe = h.off_esc_pos + 4u * h.n_esc;
+      for (uint64_t o = pe; o < h.off_esc_sym; ++o) a.container[o] = 0;
+      const uint64_t se = h.off_esc_sym + sym_bytes(LAYOUT) * h.n_esc;
+      for (uint64_t o = se; o < h.total_bytes; ++o) a.container[o] = 0;
+    }
+  }
+}
+
+// ---- scan of block escape counts ----------------------------------------
+
+__global__ __launch_bounds__(1024) void k_scan(const uint32_t* __restrict__ cnt,
+                                               uint32_t* __restrict__ off, uint64_t nblk) {
+  __shared__ uint32_t wtot[1024 / kWave];
+  const uint64_t tid = threadIdx.x;
+  const uint64_t seg = (nblk + 1023) / 1024;
+  const uint64_t b0 = tid * seg;
+  const uint64_t b1 = b0 + seg < nblk ? b0 + seg : nblk;
+  uint32_t s = 0;
+  for (uint64_t i = b0; i < b1; ++i) s += cnt[i];
+  const uint32_t ex = wave_excl_scan_u32(s);
+  if (lane_id() == kWave - 1) wtot[tid / kWave] = ex + s;
+  __syncthreads();
+  uint32_t wbase = 0;
+  for (uint64_t q = 0; q < tid / kWave; ++q) wbase += wtot[q];
+  uint32_t run = wbase + ex;
+  for (uint64_t i = b0; i < b1; ++i) {
+    off[i] = run;
+    run += cnt[i];
+  }
+}
+
+// ---- escape records --------------------------------------------------------
+
+struct EmitArgs {
+  const uint16_t* w;
+  uint8_t* container;
+  const uint32_t* blk_cnt;
+  const uint32_t* blk_off;
+  uint64_t n;
+  wc_header h;
+};
+
+template <int LAYOUT>
+__global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
+  __shared__ uint32_t wtot[kBlockThreads / kWave];
+  if (a.blk_cnt[blockIdx.x] == 0) return;  // whole block: no escapes
+  const int tid = threadIdx.x;
+  const uint64_t chunk = (uint64_t)blockIdx.x * kBlockThreads + (uint64_t)tid;
+  const uint64_t base = chunk * kChunk;
+  uint32_t mask = 0;  // bit i: weight base+i escapes
+  if (base < a.n) {
+    const uint32_t valid = a.n - base >= kChunk ? kChunk : (uint32_t)(a.n - base);
+    const u32x4 c = *(const u32x4*)(a.container + a.h.off_codes + 16u * chunk);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const uint32_t code = (c[i >> 3] >> (4 * (i & 7))) & 15u;
+      if (code == 15u && (uint32_t)i < valid) mask |= 1u << i;
+    }
+  }
+  const uint32_t cnt = __popc(mask);
+  const uint32_t ex = wave_excl_scan_u32(cnt);
+  if (lane_id() == kWave - 1) wtot[tid / kWave] = ex + cnt;
+  __syncthreads();
+  uint32_t wbase = 0;
+  for (int q = 0; q < tid / kWave; ++q) wbase += wtot[q];
+  uint64_t o = (uint64_t)a.blk_off[blockIdx.x] + wbase + ex;
+  uint32_t* pos = (uint32_t*)(a.container + a.h.off_esc_pos);
+  uint8_t* sym = a.container + a.h.off_esc_sym;
+  while (mask) {
+    const int i = __builtin_ctz(mask);
+    mask &= mask - 1u;
+    if (o < a.h.n_esc) {
+      const uint64_t p = base + (uint64_t)i;
+      const uint32_t s = (uint32_t)a.w[p] >> (LAYOUT == WC_LAYOUT_K15 ? 7 : 8);
+      pos[o] = (uint32_t)p;
+      if (LAYOUT == WC_LAYOUT_K15)
+        ((uint16_t*)sym)[o] = (uint16_t)s;
+      else
+        sym[o] = (uint8_t)s;
+    }
+    ++o;
+  }
+}
+
+hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
+                         hipStream_t s) {
+  const uint64_t nblk = (h.n + kPackBlock - 1) / kPackBlock;
+  uint32_t* blk_cnt = (uint32_t*)(work + kWorkBlocks);
+  uint32_t* blk_off = blk_cnt + nblk;
+  PackArgs p;
+  p.w = w;
+  p.container = container;
+  p.blk_cnt = blk_cnt;
+  p.n = h.n;
+  p.h = h;
+  // n == 0 still runs one block: it writes the header
+  const dim3 grid((unsigned)(nblk ? nblk : 1));
+  if (h.layout == WC_LAYOUT_K15)
+    hipLaunchKernelGGL(k_pack<WC_LAYOUT_K15>, grid, dim3(kBlockThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_pack<WC_LAYOUT_BYTESPLIT>, grid, dim3(kBlockThreads), 0, s, p);
+  if (h.n_esc == 0 || nblk == 0) return hipGetLastError();
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, blk_cnt, blk_off, nblk);
+  EmitArgs e;
+  e.w = w;
+  e.container = container;
+  e.blk_cnt = blk_cnt;
+  e.blk_off = blk_off;
+  e.n = h.n;
+  e.h = h;
+  if (h.layout == WC_LAYOUT_K15)
+    hipLaunchKernelGGL(k_emit<WC_LAYOUT_K15>, dim3((unsigned)nblk), dim3(kBlockThreads), 0, s, e);
+  else
+    hipLaunchKernelGGL(k_emit<WC_LAYOUT_BYTESPLIT>, dim3((unsigned)nblk), dim3(kBlockThreads), 0, s, e);
+  return hipGetLastError();
+}
+
+}  // namespace wc

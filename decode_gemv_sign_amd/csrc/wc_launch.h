@@ -1,0 +1,33 @@
+// wc_launch.h — internal launchers of libwc's kernels (host side).  Each
+// returns a hipError_t from the launch; argument checks happen in wc_api.hip.
+#pragma once
+
+#include "wc_common.h"
+
+namespace wc {
+
+// Byte offsets inside the caller's workspace (WC_WORKSPACE_BYTES(n) bytes).
+constexpr size_t kWorkHist = 0;         // u32[512] symbol counts
+constexpr size_t kWorkResult = 2048;    // DictResult
+constexpr size_t kWorkBlocks = 4096;    // u32[nblk] escape counts, then u32[nblk] offsets
+
+struct DictResult {
+  uint32_t n_dict;
+  uint32_t reserved;
+  uint64_t n_esc;
+  uint16_t dict[16];
+};
+
+hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t* work,
+                             hipStream_t s);
+hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
+                         hipStream_t s);
+hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t* out,
+                         hipStream_t s);
+hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint64_t rows,
+                              uint64_t cols, const uint16_t* x, uint32_t batch, float* y,
+                              hipStream_t s);
+hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, const uint16_t* x,
+                            uint32_t batch, float* y, hipStream_t s);
+
+}  // namespace wc

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars:
+  * encode: every container byte identical to the oracle's;
+  * decode: every weight bit-identical to the source (the pages' lossless
+    criterion: page "Prueba de GLM-5.2 reduce la memoria BF16 en casi un 25%",
+    section "Cómo funciona la compresión");
+  * GEMV: per element |y - y_ref| <= 1e-3 max(|y_ref|, 2^-10 a) against the
+    oracle's fp32 sequential sum and its fp64 sum (tests/tolerance.py), and
+    bit-exact where the exact sum is representable (one-hot x, small integers).
+Sizes: hand-derived golden containers, every BF16 bit pattern, ragged sizes
+spanning several 2048-weight tiles, and the five workloads at full size in
+the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.test_oracle import GOLDEN, expected_container, weights_of
+from tests.tolerance import assert_gemv_close
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import decode_gemv_sign_amd as wc  # noqa: E402
+
+DEV = "cuda:0"
+LAYOUTS = [wc.BYTESPLIT, wc.K15]
+
+
+def dev16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def host16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def gpu_encode(layout, w_np):
+    w = dev16(w_np.reshape(-1))
+    h, c = wc.encode(w, layout)
+    torch.cuda.synchronize()
+    return h, c
+
+
+def check_roundtrip(layout, w_np, what):
+    """GPU container == oracle container byte for byte; GPU decode exact."""
+    w_flat = np.ascontiguousarray(w_np).reshape(-1)
+    h, c = gpu_encode(layout, w_flat)
+    ref = oracle.encode(layout, w_flat)
+    got = c.cpu().numpy()
+    assert got.size == ref.size, f"{what}: container size {got.size} vs {ref.size}"
+    if not np.array_equal(got, ref):
+        bad = np.nonzero(got != ref)[0]
+        raise AssertionError(f"{what}: {bad.size} container bytes differ, first at {bad[0]} "
+                             f"(gpu {got[bad[0]]:#x}, oracle {ref[bad[0]]:#x}); "
+                             f"header says streams at codes={h.off_codes} raw={h.off_raw} "
+                             f"pos={h.off_esc_pos} sym={h.off_esc_sym}")
+    out = wc.decode(h, c)
+    torch.cuda.synchronize()
+    dec = host16(out)
+    if not np.array_equal(dec, w_flat):
+        bad = np.nonzero(dec != w_flat)[0]
+        raise AssertionError(f"{what}: {bad.size} weights differ after decode, first at "
+                             f"{bad[0]}: {dec[bad[0]]:#06x} vs {w_flat[bad[0]]:#06x}")
+    return h, c
+
+
+def oracle_gemv(W, x):
+    y32 = oracle.gemv_f32(W, x)
+    y64, a = oracle.gemv_f64(W, x)
+    return y32, y64, a
+
+
+def check_gemv(layout, W, x, h=None, c=None, what="", ref=None):
+    """Fused decode-GEMV and the plain BF16 GEMV against the oracle.  `ref`
+    may hold oracle results for a larger batch whose first rows are x."""
+    rows, cols = W.shape
+    batch = x.shape[0]
+    if h is None:
+        h, c = gpu_encode(layout, W)
+    xd = dev16(x)
+    y = wc.decode_gemv(h, c, rows, cols, xd)
+    yb = wc.gemv_bf16(dev16(W), xd)
+    torch.cuda.synchronize()
+    y32, y64, a = oracle_gemv(W, x) if ref is None else (r[:batch] for r in ref)
+    y = y.cpu().numpy()
+    yb = yb.cpu().numpy()
+    assert_gemv_close(y, y32, a, f"{what} fused vs oracle fp32")
+    assert_gemv_close(y, y64, a, f"{what} fused vs oracle fp64")
+    assert_gemv_close(yb, y64, a, f"{what} plain bf16 vs oracle fp64")
+    return y, yb
+
+
+# ------------------------------------------------------------ golden / exact
+
+@pytest.mark.parametrize("case", GOLDEN, ids=[c["name"] for c in GOLDEN])
+def test_golden_containers_on_gpu(case):
+    w = weights_of(case)
+    h, c = gpu_encode(case["layout"], w)
+    assert c.cpu().numpy().tobytes() == expected_container(case)
+    assert h.to_bytes() == expected_container(case)[:128]
+    out = wc.decode(h, c)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(out), w)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("shuffle", [None, 7])
+def test_all_bit_patterns(layout, shuffle):
+    check_roundtrip(layout, synth.all_patterns(shuffle), f"all patterns shuffle={shuffle}")
+
+
+RAGGED = [1, 2, 3, 31, 32, 33, 63, 64, 65, 2047, 2048, 2049, 6143, 8191, 8192, 8193, 20001,
+          65537, 1 << 20, (1 << 20) + 7, 3 * 8192 * 64 + 1234]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("kind", ["normal", "uniform", "few"])
+def test_ragged_sizes(layout, kind):
+    for i, n in enumerate(RAGGED):
+        check_roundtrip(layout, synth.random_bits(n, 500 + i, kind), f"{kind} n={n}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_empty_tensor(layout):
+    w = torch.empty(0, dtype=torch.int16, device=DEV)
+    h, c = wc.encode(w, layout)
+    torch.cuda.synchronize()
+    assert h.n == 0 and h.total_bytes == 128
+    assert np.array_equal(c.cpu().numpy(), oracle.encode(layout, np.zeros(0, np.uint16)))
+    out = wc.decode(h, c)
+    assert out.numel() == 0
+
+
+def test_gemv_one_hot_exact():
+    W = synth.random_bits(96 * 256, 3, "normal").reshape(96, 256)
+    for layout in LAYOUTS:
+        h, c = gpu_encode(layout, W)
+        for j in (0, 31, 32, 255):
+            x = np.zeros((1, 256), dtype=np.uint16)
+            x[0, j] = 0x3F80
+            y = wc.decode_gemv(h, c, 96, 256, dev16(x)).cpu().numpy()
+            yb = wc.gemv_bf16(dev16(W), dev16(x)).cpu().numpy()
+            exp = synth.bf16_to_f32(W[:, j])
+            assert np.array_equal(y[0].view(np.uint32), exp.view(np.uint32)), (layout, j)
+            assert np.array_equal(yb[0].view(np.uint32), exp.view(np.uint32)), (layout, j)
+
+
+def test_gemv_small_integers_exact():
+    rng = np.random.default_rng(4)
+    for rows, cols, batch in [(37, 128, 3), (64, 2048, 16), (5, 4096 + 32, 4), (7, 100, 5)]:
+        Wi = rng.integers(-8, 9, size=(rows, cols))
+        xi = rng.integers(-8, 9, size=(batch, cols))
+        W = synth.bf16_bits(Wi.astype(np.float32)).reshape(rows, cols)
+        x = synth.bf16_bits(xi.astype(np.float32)).reshape(batch, cols)
+        exp = (xi @ Wi.T).astype(np.float32)
+        for layout in LAYOUTS:
+            h, c = gpu_encode(layout, W)
+            y = wc.decode_gemv(h, c, rows, cols, dev16(x)).cpu().numpy()
+            assert np.array_equal(y, exp), (rows, cols, batch, layout)
+        yb = wc.gemv_bf16(dev16(W), dev16(x)).cpu().numpy()
+        assert np.array_equal(yb, exp)
+
+
+# ------------------------------------------------ GEMV shapes and batches
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemv_shapes_and_batches(layout):
+    cases = [(1, 32, 1), (3, 64, 2), (65, 2048, 1), (17, 2080, 3), (33, 4096, 5), (9, 6144, 16),
+             (40, 1000, 1), (11, 33, 7), (2, 1, 16), (128, 96, 4), (5, 24576, 8)]
+    for i, (rows, cols, batch) in enumerate(cases):
+        W = synth.random_bits(rows * cols, 700 + i, "normal").reshape(rows, cols)
+        # sprinkle outliers so escapes land inside GEMV tiles
+        W.reshape(-1)[::97] ^= 0x3000
+        x = synth.vectors(800 + i, batch, cols)
+        check_gemv(layout, W, x, what=f"{rows}x{cols} b={batch}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemv_escape_dense(layout):
+    # uniform bit patterns: most symbols escape; includes NaN/inf-free subset
+    rows, cols = 64, 4096
+    # uniform bit patterns with the top exponent bit cleared: |w| < 2, 256
+    # distinct sign+exponent symbols, so most weights escape
+    w = synth.random_bits(rows * cols, 901, "uniform") & np.uint16(0xBFFF)
+    W = w.reshape(rows, cols)
+    x = synth.vectors(902, 4, cols)
+    h, c = check_roundtrip(layout, W, "escape-dense")
+    assert h.n_esc > rows * cols // 2
+    check_gemv(layout, W, x, h, c, "escape-dense")
+
+
+def test_gemv_cols_zero_and_rows_zero():
+    w = torch.empty(0, dtype=torch.int16, device=DEV)
+    h, c = wc.encode(w, wc.BYTESPLIT)
+    x = torch.zeros((3, 0), dtype=torch.int16, device=DEV)
+    y = torch.full((3, 5), 7.0, device=DEV)
+    wc.decode_gemv(h, c, 5, 0, x, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+    y0 = torch.empty((3, 0), device=DEV)
+    wc.decode_gemv(h, c, 0, 17, torch.zeros((3, 17), dtype=torch.int16, device=DEV), out=y0)
+
+
+def test_error_codes():
+    W = synth.random_bits(64 * 64, 1, "normal").reshape(64, 64)
+    h, c = gpu_encode(0, W)
+    x = dev16(synth.vectors(1, 17, 64))
+    with pytest.raises(wc.WCError) as e:
+        wc.decode_gemv(h, c, 64, 64, x)
+    assert e.value.code == -5
+    with pytest.raises(wc.WCError) as e:
+        wc.decode_gemv(h, c, 32, 64, x[:1])
+    assert e.value.code == -1
+    bad = wc.Header.from_bytes(h.to_bytes())
+    bad.n_esc = bad.n + 1
+    with pytest.raises(wc.WCError) as e:
+        wc.decode(bad, c)
+    assert e.value.code == -3
+    with pytest.raises(wc.WCError) as e:
+        wc.decode(h, c[: h.total_bytes - 16])
+    assert e.value.code == -2
+    # misaligned output
+    buf = torch.empty(h.n + 8, dtype=torch.int16, device=DEV)
+    with pytest.raises(wc.WCError) as e:
+        wc.decode(h, c, out=buf[1:1 + h.n])
+    assert e.value.code == -1
+
+
+def test_determinism():
+    d = synth.square()
+    W = d["W"]
+    for layout in LAYOUTS:
+        h1, c1 = gpu_encode(layout, W)
+        h2, c2 = gpu_encode(layout, W)
+        assert torch.equal(c1, c2)
+        x = dev16(synth.vectors(2, 4, 4096))
+        y1 = wc.decode_gemv(h1, c1, 4096, 4096, x)
+        y2 = wc.decode_gemv(h1, c1, 4096, 4096, x)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+# --------------------------------------------------- the five workloads
+
+def test_workload_small():
+    d = synth.small()
+    h, c = check_roundtrip(wc.BYTESPLIT, d["W"], "small byte-split")
+    check_gemv(wc.BYTESPLIT, d["W"], d["x"], h, c, "small byte-split")
+    h, c = check_roundtrip(wc.K15, d["W"], "small K15")
+    check_gemv(wc.K15, d["W"], d["x"], h, c, "small K15")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_workload_square(layout):
+    d = synth.square()
+    h, c = check_roundtrip(layout, d["W"], "square")
+    check_gemv(layout, d["W"], d["x"], h, c, "square")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_workload_mlp(layout):
+    m = synth.mlp()
+    for name, xn in (("W1", "x1"), ("W2", "x2")):
+        h, c = check_roundtrip(layout, m[name], f"mlp {name}")
+        check_gemv(layout, m[name], m[xn], h, c, f"mlp {name}")
+
+
+@pytest.mark.parametrize("t", [0, 47, 48, 71, 72, 95])
+def test_workload_layerset_tensors(t):
+    name, a = synth.layerset_tensor(t)
+    for layout in LAYOUTS:
+        check_roundtrip(layout, a, f"layerset {name}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_workload_banded(layout):
+    d = synth.banded()
+    W = d["W"]
+    h, c = check_roundtrip(layout, W, "banded")
+    ref = oracle_gemv(W, d["X"])
+    for batch in (1, 4, 16):
+        check_gemv(layout, W, d["X"][:batch], h, c, f"banded b={batch}", ref=ref)
