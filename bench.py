@@ -1,0 +1,319 @@
+"""Benchmark of the lossless BF16 coding hot path on one MI355X.
+
+One step = the whole path over one synthetic weight tensor, for each layout
+(byte-split and K15): per-tensor dictionary (wc_build_dict, which reads 64
+bytes back to the host), container encode (wc_encode), exact decode
+(wc_decode) and decode fused into GEMV (wc_decode_gemv); then the two BF16
+GEMV comparators the fused kernel is judged against (wc_gemv_bf16 and
+torch.nn.functional.linear).  Inputs are resident in HBM before timing.
+Several copies of the input rotate from step to step so the working set
+exceeds the 256 MB last-level cache and every step streams from HBM.
+
+Printed: one JSON line.  `value` = BF16 bytes decoded exactly per second of
+whole-step wall time (2 n bytes per layout per step).  Per-kernel figures
+(HIP events on the launch stream, averaged over the timed steps) are in
+`kernels`; `roofline` describes the decode kernel (the metric's decoded-BF16
+rate); `cpu_baseline` times the CPU oracle on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("decoded BF16 GB/s (% HBM peak); fused decode-GEMV µs vs BF16 GEMV; "
+          "bits/weight")
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+LAYOUT_NAMES = {0: "byte-split", 1: "K15"}
+WORKSET_BYTES = 512 << 20  # rotate copies until the inputs span 2x the 256 MB cache
+
+WORKLOADS = {
+    "small": "1024x1024 N(0,0.02), 0.05% entries x1000; batch 1",
+    "square": "4096x4096 N(0,0.02), 1% zeros, 0.1% outliers N(0,2); batch 1",
+    "mlp": "14336x4096 + 4096x14336, row std 10^U(-4,-1); batch 1",
+    "banded": "6144x24576 N(0,0.02) + 5% escapes in 64-row bands; batch 1/4/16",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="square")
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time for the oracle baseline sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run one 256 MiB device copy first (a known-size kernel for HBM counters)")
+    return p.parse_args()
+
+
+def load_workload(name: str, batch: int):
+    import synth
+    if name == "small":
+        d = synth.small()
+        return [d["W"]], synth.vectors(synth.SEEDS["small"], batch, 1024)
+    if name == "square":
+        d = synth.square()
+        return [d["W"]], synth.vectors(synth.SEEDS["square"], batch, 4096)
+    if name == "mlp":
+        m = synth.mlp()
+        return [m["W1"], m["W2"]], None
+    if name == "banded":
+        d = synth.banded()
+        return [d["W"]], d["X"][:batch]
+    raise ValueError(name)
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+DECODE_SOURCES = ["decode_gemv_sign_amd/csrc/wc_decode.hip", "decode_gemv_sign_amd/csrc/wc_tile.h",
+                  "decode_gemv_sign_amd/csrc/wc_common.h"]
+
+
+def counter_traffic(workload: str, layout_name: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or None
+    when absent or taken on a different version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "decode_counters.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    if data.get("source_hash") != source_hash(DECODE_SOURCES):
+        return None
+    e = data.get("workloads", {}).get(workload, {}).get(layout_name)
+    return None if e is None else float(e["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(mats, xs, layouts, min_seconds: float, gpu_results):
+    """The oracle, as it stands, on the same tensors: encode, decode and GEMV per
+    layout, repeated until min_seconds have passed.  Also cross-checks the GPU
+    step's outputs against it (containers byte-identical, GEMV within bound)."""
+    import numpy as np
+
+    import oracle
+    from tests.tolerance import gemv_excess
+    oracle.build(force=False)
+    # parity of the timed GPU outputs
+    parity = True
+    for (li, mi), res in gpu_results.items():
+        W = mats[mi]
+        ref = oracle.encode(layouts[li], W)
+        if not np.array_equal(res["container"], ref):
+            parity = False
+        y64, a = oracle.gemv_f64(W, xs[mi])
+        if not np.all(gemv_excess(res["y"], y64, a) <= 1.0):
+            parity = False
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for mi, W in enumerate(mats):
+            for lay in layouts:
+                c = oracle.encode(lay, W)
+                oracle.decode(c)
+                oracle.gemv_f32(W, xs[mi])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    n_total = sum(W.size for W in mats)
+    value = 2.0 * n_total * len(layouts) * steps / el / 1e9
+    return {"value": round(value, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full steps of the same workload ({el:.1f} s): per layout, "
+                      f"oracle encode + decode + fp32 GEMV; single-threaded C",
+            "ms_per_step": round(1e3 * el / steps, 3)}, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the codec shards per tensor with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import decode_gemv_sign_amd as wc
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mats, x = load_workload(args.workload, args.batch)
+    if x is None:
+        xs = [synth.vectors(synth.SEEDS[args.workload] * 10 + i, args.batch, W.shape[1])
+              for i, W in enumerate(mats)]
+    else:
+        xs = [x]
+    layouts = [wc.BYTESPLIT, wc.K15]
+    in_bytes = sum(W.nbytes for W in mats)
+    copies = max(1, -(-WORKSET_BYTES // in_bytes))
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    Wd = [[to_dev(W.reshape(-1)) for W in mats] for _ in range(copies)]
+    Xd = [to_dev(xx) for xx in xs]
+    Xbf = [xd.view(torch.bfloat16) for xd in Xd]
+    Wbf = [[w.view(torch.bfloat16).view(W.shape) for w, W in zip(row, mats)] for row in Wd]
+    work = [torch.empty(wc.workspace_bytes(max(W.size for W in mats)), dtype=torch.uint8,
+                        device=dev) for _ in range(copies)]
+    # container sizes are fixed by the data: size them with one dictionary pass
+    hdr0 = {(li, mi): wc.build_dict(Wd[0][mi], lay, work[0]) for li, lay in enumerate(layouts)
+            for mi in range(len(mats))}
+    cont = [{k: torch.empty(h.total_bytes, dtype=torch.uint8, device=dev) for k, h in hdr0.items()}
+            for _ in range(copies)]
+    dec = [[torch.empty(W.size, dtype=torch.int16, device=dev) for W in mats] for _ in range(copies)]
+    yf = {k: torch.empty((args.batch, mats[k[1]].shape[0]), dtype=torch.float32, device=dev)
+          for k in hdr0}
+    yb = [torch.empty((args.batch, W.shape[0]), dtype=torch.float32, device=dev) for W in mats]
+    names = ["build_dict", "encode", "decode", "decode_gemv", "gemv_bf16", "torch_linear"]
+
+    def step(s, events):
+        k = s % copies
+        rec = {}
+
+        def timed(name, key, fn):
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                out = fn()
+                e1.record()
+                events.setdefault((name, key), []).append((e0, e1))
+                return out
+            return fn()
+
+        for mi in range(len(mats)):
+            for li, lay in enumerate(layouts):
+                key = (li, mi)
+                h = timed("build_dict", key, lambda: wc.build_dict(Wd[k][mi], lay, work[k]))
+                c = cont[k][key]
+                timed("encode", key, lambda: wc.encode_into(h, Wd[k][mi], c, work[k]))
+                timed("decode", key, lambda: wc.decode(h, c, out=dec[k][mi]))
+                rows, cols = mats[mi].shape
+                timed("decode_gemv", key,
+                      lambda: wc.decode_gemv(h, c, rows, cols, Xd[mi], out=yf[key]))
+                rec[key] = h
+            timed("gemv_bf16", (None, mi), lambda: wc.gemv_bf16(Wd[k][mi].view(mats[mi].shape),
+                                                                 Xd[mi], out=yb[mi]))
+            timed("torch_linear", (None, mi),
+                  lambda: torch.nn.functional.linear(Xbf[mi], Wbf[k][mi]))
+        return rec
+
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for s in range(args.warmup):
+        step(s, None)
+    events = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hdrs = None
+    for s in range(args.steps):
+        hdrs = step(args.warmup + s, events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # every copy the steps decoded must equal its input bit for bit
+    for k in range(min(copies, args.warmup + args.steps)):
+        for mi in range(len(mats)):
+            if not torch.equal(dec[k][mi], Wd[k][mi]):
+                raise SystemExit(f"decode is not exact (copy {k}, tensor {mi})")
+
+    n_total = sum(W.size for W in mats)
+    ms_step = 1e3 * wall / args.steps
+    value = 2.0 * n_total * len(layouts) / (wall / args.steps) / 1e9
+
+    def avg_us(name, key):
+        ev = events[(name, key)]
+        return 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+
+    kernels = {}
+    roofline = None
+    bpw = {}
+    for (li, mi), h in sorted(hdrs.items()):
+        lname = LAYOUT_NAMES[layouts[li]]
+        tag = lname if len(mats) == 1 else f"{lname}/W{mi + 1}"
+        rows, cols = mats[mi].shape
+        n = mats[mi].size
+        b, p = wc.bits_per_weight(h)
+        bpw[tag] = {"bpw": round(b, 4), "payload_bpw": round(p, 4),
+                    "saving": round(1 - b / 16, 5), "n_esc": int(h.n_esc),
+                    "escape_frac": round(h.n_esc / n, 6)}
+        t_dec = avg_us("decode", (li, mi))
+        dec_bytes = h.total_bytes + 2 * n
+        t_gemv = avg_us("decode_gemv", (li, mi))
+        gemv_bytes = h.total_bytes + 2 * cols * args.batch + 4 * rows * args.batch
+        t_bf = avg_us("gemv_bf16", (None, mi))
+        t_lin = avg_us("torch_linear", (None, mi))
+        kernels[tag] = {
+            "build_dict_us": round(avg_us("build_dict", (li, mi)), 2),
+            "encode_us": round(avg_us("encode", (li, mi)), 2),
+            "decode_us": round(t_dec, 2),
+            "decode_decoded_gbps": round(2 * n / t_dec / 1e3, 1),
+            "decode_hbm_gbps": round(dec_bytes / t_dec / 1e3, 1),
+            "decode_hbm_frac": round(dec_bytes / t_dec / 1e3 / HBM_PEAK_GBPS, 4),
+            "decode_gemv_us": round(t_gemv, 2),
+            "decode_gemv_hbm_gbps": round(gemv_bytes / t_gemv / 1e3, 1),
+            "gemv_bf16_us": round(t_bf, 2),
+            "torch_linear_us": round(t_lin, 2),
+            "fused_vs_best_bf16": round(t_gemv / min(t_bf, t_lin), 4),
+        }
+        if roofline is None or t_dec > roofline["_t"]:
+            roofline = {"_t": t_dec, "kernel": f"k_decode ({tag})", "bound": "hbm",
+                        "achieved": round(dec_bytes / t_dec / 1e3, 1), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(dec_bytes / t_dec / 1e3 / HBM_PEAK_GBPS, 4),
+                        "traffic": counter_traffic(args.workload, tag),
+                        "algorithmic_bytes_per_launch": int(dec_bytes)}
+    roofline.pop("_t")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}",
+                   "layouts": [LAYOUT_NAMES[l] for l in layouts], "batch": args.batch,
+                   "weights": int(n_total), "rotating_copies": copies,
+                   "value_definition": "2 bytes x weights x layouts per step / step wall time; "
+                                       "step = dictionary + encode + decode + fused GEMV per "
+                                       "layout, plus both BF16 GEMV comparators"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "bits_per_weight": bpw,
+    }
+    if not args.no_cpu_baseline:
+        gpu_results = {}
+        for (li, mi) in hdrs:
+            c = cont[(args.warmup + args.steps - 1) % copies][(li, mi)].cpu().numpy()
+            y = yf[(li, mi)].cpu().numpy()
+            gpu_results[(li, mi)] = {"container": c, "y": y}
+        cb, parity = cpu_baseline([np.ascontiguousarray(W) for W in mats], xs, layouts,
+                                  args.cpu_seconds, gpu_results)
+        out["cpu_baseline"] = cb
+        out["parity_vs_oracle"] = "ok" if parity else "FAILED"
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    if out.get("parity_vs_oracle") == "FAILED":
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

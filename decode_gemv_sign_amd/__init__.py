@@ -66,11 +66,11 @@ class Header(ctypes.Structure):
 assert ctypes.sizeof(Header) == 128
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m decode_gemv_sign_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+            f"{path} is not built; run `python -m decode_gemv_sign_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     U64 = ctypes.c_uint64
     HP = ctypes.POINTER(Header)
@@ -88,6 +88,12 @@ def _load():
 
 
 _lib = _load()
+
+
+def use_library(path: str):
+    """Bind this module to another build of libwc (e.g. a tuning variant)."""
+    global _lib
+    _lib = _load(path)
 
 
 def _check(st: int, what: str):

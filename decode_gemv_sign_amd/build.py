@@ -26,23 +26,27 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    subprocess.check_call([HIPCC, *FLAGS, "-c", src, "-o", obj])
+def _compile(src: str, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    subprocess.check_call([HIPCC, *FLAGS, *["-D" + d for d in defines], "-c", src, "-o", obj])
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile and link; `defines` (NAME=VALUE) override compile-time tuning
+    constants, `out` places the library elsewhere (for tuning sweeps)."""
+    build_dir = BUILD if out == LIB else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+    tmp = out + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    LIB_OUT = out
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", LIB_OUT)
+    return LIB_OUT
 
 
 if __name__ == "__main__":

@@ -16,7 +16,7 @@ namespace wc {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;              // CDNA wavefront width
-constexpr int kChunk = 32;             // weights per lane per step: 16 B of codes
+constexpr int kChunk = 32;             // weights per lane per tile
 constexpr int kTile = kWave * kChunk;  // weights per wave per step (2048)
 constexpr int kBlockThreads = 256;     // 4 waves per workgroup
 constexpr int kPackBlock = kBlockThreads * kChunk;  // weights per encode block (8192)
@@ -45,15 +45,28 @@ __host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_
 }
 
 // Dictionary as kernel argument: symbol per code, slot 15 (escape) = 0, so a
-// rebuilt escape holds only its raw bits until it is patched.
+// rebuilt escape holds only its raw bits until it is patched.  `hi` holds the
+// byte each code puts in a weight's high byte (the symbol for byte-split, the
+// symbol's top 8 bits for K15), `lo` (K15) the byte each code puts in the low
+// byte (0x80 when the symbol's lowest bit, exponent bit 0, is set), both
+// packed 4 codes per dword, code c in byte c % 4 of dword c / 4.
 struct Dict {
   uint16_t sym[16];
   uint32_t n_dict;
+  uint32_t hi[4];
+  uint32_t lo[4];
 };
 
 // ---- wave primitives -----------------------------------------------------
 
 __device__ inline int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Index of this wave in its workgroup, as a scalar (wave-uniform) value, so
+// everything derived from it (tile and row numbers, loop bounds) stays in
+// SGPRs and its branches are uniform.
+__device__ inline int wave_in_block() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
 
 __device__ inline uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
@@ -79,11 +92,24 @@ __device__ inline uint32_t wave_excl_scan_u32(uint32_t v) {
   return x - v;
 }
 
-// Orders this wave's LDS writes before its later LDS reads by other lanes.
+// Orders this wave's LDS accesses across lanes.  The LDS unit executes one
+// wave's instructions in issue order, so only the compiler must be kept from
+// moving memory accesses across this point: wavefront-scope fences emit no
+// wait (a workgroup-scope fence would also wait for every global load in
+// flight, including the next tile's prefetch).
 __device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Sum over the wave of a per-lane value below 64, by bit-plane ballots (scalar
+// popcounts, no cross-lane data movement).
+__device__ inline uint32_t wave_sum_small(uint32_t v) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) s += (uint32_t)__popcll(__ballot((v >> b) & 1u)) << b;
+  return s;
 }
 
 // First index i in [0, count) with pos[i] >= t (count if none), found by the
@@ -108,17 +134,6 @@ __device__ inline uint64_t wave_lower_bound(const uint32_t* __restrict__ pos, ui
   const uint64_t idx = lo + (uint64_t)lane;
   const bool below = idx < hi && (uint64_t)pos[idx] < t;
   return lo + (uint64_t)__popcll(__ballot(below));
-}
-
-// Per-lane count of code-15 nibbles in four code dwords (32 codes).
-__device__ inline uint32_t count_escapes(const u32x4& c) {
-  uint32_t n = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t w = c[q];
-    n += __popc(w & (w >> 1) & (w >> 2) & (w >> 3) & 0x11111111u);
-  }
-  return n;
 }
 
 // ---- host-side checks ----------------------------------------------------
@@ -152,6 +167,14 @@ inline Dict dict_of(const wc_header* h) {
   Dict d;
   for (int k = 0; k < 16; ++k) d.sym[k] = (k < h->n_dict && k < 15) ? h->dict[k] : 0;
   d.n_dict = h->n_dict;
+  for (int q = 0; q < 4; ++q) d.hi[q] = d.lo[q] = 0;
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t s = d.sym[k];
+    const uint32_t hb = h->layout == WC_LAYOUT_K15 ? s >> 1 : s;
+    const uint32_t lb = h->layout == WC_LAYOUT_K15 ? (s & 1u) << 7 : 0u;
+    d.hi[k / 4] |= (hb & 0xFFu) << (8 * (k % 4));
+    d.lo[k / 4] |= lb << (8 * (k % 4));
+  }
   return d;
 }
 

@@ -16,13 +16,18 @@
 
 namespace wc {
 
+#ifndef WC_DECODE_TILES_PER_WAVE
+#define WC_DECODE_TILES_PER_WAVE 4
+#endif
+constexpr uint64_t kDecodeTilesPerWave = WC_DECODE_TILES_PER_WAVE;
+
 struct DecodeArgs {
   const uint8_t* codes;
   const uint8_t* raw;
   const uint32_t* esc_pos;
   const uint8_t* esc_sym;
   uint16_t* out;
-  uint64_t n, n_esc, raw_padded, n_tiles, tiles_per_wave;
+  uint64_t n, n_esc, esc_last, raw_last, n_tiles, tiles_per_wave;
   Dict dict;
 };
 
@@ -34,47 +39,96 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   __syncthreads();
 
   const int lane = lane_id();
-  const int wib = (int)(threadIdx.x / kWave);
+  const int wib = wave_in_block();
   const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wib;
   const uint64_t t0 = wave * a.tiles_per_wave;
   const uint64_t t1 = t0 + a.tiles_per_wave < a.n_tiles ? t0 + a.tiles_per_wave : a.n_tiles;
   if (t0 >= t1) return;
 
+  // Every tile but the tensor's last is full.  Full tiles run in a software
+  // pipeline: tile t+1's loads are in flight while tile t is rebuilt, patched
+  // and stored.  Two register sets alternate (the loop is unrolled by two)
+  // and every load is issued unconditionally, at a clamped valid address
+  // when its data will not be used, so the loads in flight are the same on
+  // every path and no wait covers the prefetch.
+  const uint64_t full_tiles = a.n / kTile;
+  const uint64_t f1 = t1 < full_tiles ? t1 : full_tiles;  // end of this wave's full tiles
   uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile) : 0;
-  for (uint64_t t = t0; t < t1; ++t) {
-    const uint64_t chunk = t * kWave + (uint64_t)lane;
-    const uint64_t base = chunk * kChunk;
-    const uint32_t valid = base < a.n ? (a.n - base >= kChunk ? kChunk : (uint32_t)(a.n - base)) : 0;
-    Chunk c;
-    if (valid == kChunk) {
-      load_chunk_full<LAYOUT>(a.codes, a.raw, chunk, c);
-    } else if (valid) {
-      load_chunk_partial<LAYOUT>(a.codes, a.raw, chunk, valid, a.raw_padded, c);
-    } else {
-      c.codes = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) c.raw[k] = 0;
-    }
-    const uint32_t cnt = count_escapes(c.codes);
-    uint32_t out[16];
-    rebuild_chunk<LAYOUT>(T2, c, out);
+  EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+
+  // rebuild + escapes of tile t into out[16] (lane's 4 groups)
+  auto rebuild = [&](uint64_t t, const Lane4& l, uint32_t out[16]) {
+    uint32_t gmask;
+    const uint32_t cnt = count_escapes(l, &gmask);
+    rebuild_lane<LAYOUT>(T2, a.dict, l, out);
     if (__ballot(cnt != 0)) {
-      const uint32_t cnt_wave = wave_sum_u32(cnt);
+      const uint32_t cnt_wave = wave_sum_small(cnt);
       const uint64_t tile_start = t * kTile;
       const uint32_t tile_len = a.n - tile_start >= kTile ? kTile : (uint32_t)(a.n - tile_start);
-      patch_tile<LAYOUT>(stage[wib], out, a.esc_pos, a.esc_sym, a.n_esc, e, cnt_wave, tile_start,
-                         tile_len);
+      patch_tile<LAYOUT>(stage[wib], out, gmask, a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e, cnt_wave,
+                         tile_start, tile_len, eb);
       e += cnt_wave;
     }
-    if (valid == kChunk) {
-      u32x4* dst = (u32x4*)(a.out + base);
+    eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+  };
+
+  if (t0 < f1) {
+    auto load_full = [&](uint64_t t, Lane4& l) {
+      const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < kLaneGroups; ++k)
+        load_group<LAYOUT>(a.codes, a.raw, tc * (kTile / kGroup) + lane + kWave * k, a.raw_last,
+                           l.codes[k], l.raw[k]);
+    };
+    auto process = [&](uint64_t t, const Lane4& l) {
+      uint32_t out[16];
+      rebuild(t, l, out);
+      u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
+#pragma unroll
+      for (int k = 0; k < kLaneGroups; ++k)
         __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
-                                    dst + k);
-    } else if (valid) {
-      for (uint32_t i = 0; i < valid; ++i)
-        a.out[base + i] = (uint16_t)(out[i >> 1] >> (16u * (i & 1u)));
+                                    dst + kWave * k);
+    };
+    Lane4 la, lb;
+    load_full(t0, la);
+    for (uint64_t t = t0; t < f1; t += 2) {
+      load_full(t + 1, lb);
+      process(t, la);
+      if (t + 1 >= f1) break;
+      load_full(t + 2, la);
+      process(t + 1, lb);
+    }
+  }
+  if (t1 > full_tiles) {
+    // The tensor's partial last tile: groups past n are skipped, the group
+    // that holds the last weight has its missing codes cleared (no phantom
+    // escapes) and stores only its valid weights.
+    const uint64_t tile_start = full_tiles * kTile;
+    Lane4 l;
+    uint32_t valid[kLaneGroups];
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k) {
+      const uint64_t g = full_tiles * (kTile / kGroup) + lane + kWave * k;
+      const uint64_t w0 = g * kGroup;
+      valid[k] = w0 < a.n ? (a.n - w0 >= kGroup ? kGroup : (uint32_t)(a.n - w0)) : 0u;
+      l.codes[k] = 0;
+      l.raw[k][0] = l.raw[k][1] = 0;
+      if (valid[k]) {
+        load_group<LAYOUT>(a.codes, a.raw, g, a.raw_last, l.codes[k], l.raw[k]);
+        if (valid[k] < kGroup) l.codes[k] &= (1u << (4 * valid[k])) - 1u;
+      }
+    }
+    uint32_t out[16];
+    rebuild(full_tiles, l, out);
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k) {
+      const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;
+      if (valid[k] == kGroup) {
+        *(u32x4*)(a.out + w0) = u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]};
+      } else {
+        for (uint32_t i = 0; i < valid[k]; ++i)
+          a.out[w0 + i] = (uint16_t)(out[4 * k + (i >> 1)] >> (16u * (i & 1u)));
+      }
     }
   }
 }
@@ -90,12 +144,17 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   a.out = out;
   a.n = h.n;
   a.n_esc = h.n_esc;
-  a.raw_padded = pad16(raw_bytes(h.layout, h.n));
+  // with no escapes, the (never used) escape loads read the container header
+  a.esc_last = h.n_esc ? h.n_esc - 1 : 0;
+  if (h.n_esc == 0) {
+    a.esc_pos = (const uint32_t*)container;
+    a.esc_sym = container;
+  }
+  a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;
-  // about 16 waves per CU on 256 CUs, each over a contiguous run of tiles
-  const uint64_t max_waves = 256u * 16u;
-  const uint64_t waves0 = a.n_tiles < max_waves ? a.n_tiles : max_waves;
-  a.tiles_per_wave = (a.n_tiles + waves0 - 1) / waves0;
+  // Short runs of tiles per wave: long enough to amortise the escape-cursor
+  // search, short enough that dense escape regions spread over many waves.
+  a.tiles_per_wave = kDecodeTilesPerWave;
   const uint64_t waves = (a.n_tiles + a.tiles_per_wave - 1) / a.tiles_per_wave;
   const uint64_t wpb = kBlockThreads / kWave;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb));

@@ -10,14 +10,14 @@
 // correction and was timed against a BF16 GEMV; here the escapes are applied
 // inside the same kernel, tile by tile.
 //
-// y[b][r] = sum_c W[r][c] x[b][c].  One wave per row: per step each lane
-// rebuilds 32 consecutive weights of the row (wc_tile.h), multiplies them with
-// the matching x values by v_dot2_f32_bf16 (exact BF16 products, fp32
-// accumulate), and at the row's end the 64 lane partials are summed by
-// butterfly shuffles.  HBM-bound at batch 1 and 4: per weight bpw/8 bytes
-// of container are read (x stays in L2).
+// y[b][r] = sum_c W[r][c] x[b][c].  A wave walks 2048-weight tiles along
+// its rows: each lane rebuilds its 4 groups of 8 weights (wc_tile.h),
+// multiplies them with the matching x values by v_dot2_f32_bf16 (exact BF16
+// products, fp32 accumulate), and at the row's end the 64 lane partials are
+// summed by butterfly shuffles.  HBM-bound at batch 1 and 4: per weight bpw/8
+// bytes of container are read (x stays in L2).
 //
-// Rows whose length is not a multiple of 32 (a chunk would straddle two rows)
+// Rows whose length is not a multiple of 8 (a group would straddle two rows)
 // take the generic kernels at the end of this file: one weight per lane per
 // step, same definition, fp32 fused multiply-add.
 #include "wc_launch.h"
@@ -40,28 +40,30 @@ struct GemvArgs {
   const uint16_t* w;  // plain BF16 weights (comparator)
   const uint16_t* x;
   float* y;
-  uint64_t rows, cols, n_esc, raw_padded;
+  uint64_t rows, cols, n_esc, esc_last, raw_last, rows_per_wave;
   uint32_t batch;
   Dict dict;
 };
 
-// Multiply one lane chunk (16 weight pairs) with x[b][c0 .. c0+32) for every b.
-template <int B>
-__device__ inline void dot_chunk(const uint32_t w[16], const uint16_t* __restrict__ x,
-                                 uint64_t cols, uint64_t c0, float acc[B]) {
+// acc += the lane's 16 weight pairs (4 groups) times x[g*8 .. g*8+8) of its
+// groups, for batch row b of x (x row length `cols`).
+__device__ inline float dot_lane(const uint32_t w[16], const uint32_t xv[16], float acc) {
+  float s0 = acc, s1 = 0.0f;
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const u32x4* xp = (const u32x4*)(x + (uint64_t)b * cols + c0);
-    float s0 = acc[b], s1 = 0.0f;
+  for (int k = 0; k < 16; k += 2) {
+    s0 = dot2(w[k], xv[k], s0);
+    s1 = dot2(w[k + 1], xv[k + 1], s1);
+  }
+  return s0 + s1;
+}
+
+// x values of the lane's 4 groups (local groups lg[k] of the row) for batch row b.
+__device__ inline void load_x_lane(const uint16_t* __restrict__ x, const uint64_t lg[4],
+                                   uint32_t xv[16]) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const u32x4 xv = xp[k];
-      s0 = dot2(w[4 * k + 0], xv[0], s0);
-      s1 = dot2(w[4 * k + 1], xv[1], s1);
-      s0 = dot2(w[4 * k + 2], xv[2], s0);
-      s1 = dot2(w[4 * k + 3], xv[3], s1);
-    }
-    acc[b] = s0 + s1;
+  for (int k = 0; k < kLaneGroups; ++k) {
+    const u32x4 v = *((const u32x4*)x + lg[k]);
+    xv[4 * k] = v[0]; xv[4 * k + 1] = v[1]; xv[4 * k + 2] = v[2]; xv[4 * k + 3] = v[3];
   }
 }
 
@@ -74,6 +76,84 @@ __device__ inline void store_row(float acc[B], float* __restrict__ y, uint64_t r
   }
 }
 
+#ifndef WC_GEMV_DEPTH
+#define WC_GEMV_DEPTH 2
+#endif
+#ifndef WC_GEMV_PREFETCH_X
+#define WC_GEMV_PREFETCH_X 1
+#endif
+constexpr int kGemvDepth = WC_GEMV_DEPTH;            // tiles in the prefetch ring
+constexpr bool kGemvPrefetchX = WC_GEMV_PREFETCH_X;  // x rides in the ring at batch 1
+
+// Position (row, tile-in-row) in a wave's tile sequence.
+struct TileCursor {
+  uint64_t r, ct;
+  __device__ void next(uint64_t tpr) {
+    if (++ct == tpr) {
+      ct = 0;
+      ++r;
+    }
+  }
+};
+
+// Software pipeline over nq tiles with a ring of D register slots: tile q+D-1
+// is loaded just before tile q is processed.  The ring is unrolled, so every
+// slot index is static (no register copies, which would wait on the loads),
+// and loads past the end re-read the last tile (their data is unused), so the
+// loads in flight are the same on every path.
+template <int D, typename Slot, typename Load, typename Process>
+__device__ inline void run_ring(uint64_t nq, TileCursor start, uint64_t tpr, Load&& load,
+                                Process&& process) {
+  Slot s[D];
+  TileCursor lc = start, pc = start;
+  uint64_t lq = 0;  // index of the tile lc points at
+  auto load_next = [&](Slot& slot) {
+    load(lc, slot);
+    if (lq + 1 < nq) {
+      lc.next(tpr);
+      ++lq;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) load_next(s[i]);
+  for (uint64_t q = 0; q < nq; q += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      load_next(s[(i + D - 1) % D]);
+      if (q + i >= nq) return;
+      process(pc, s[i]);
+      pc.next(tpr);
+    }
+  }
+}
+
+// Row tile (r, ct) = groups [256 ct, 256 ct + 256) of row r; lane L takes row
+// groups lg_k = 256 ct + L + 64 k that are inside the row (a lane past the row
+// end reloads the row's last group and drops it, so every path issues the
+// same loads).
+struct RowTile {
+  uint64_t lg[kLaneGroups];  // row-local group per k (clamped)
+  uint32_t act;              // bit k: group k is inside the row
+};
+
+__device__ inline RowTile row_tile(uint64_t ct, uint64_t gpr) {
+  RowTile t;
+  t.act = 0;
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) {
+    const uint64_t g = ct * (kTile / kGroup) + (uint64_t)(lane_id() + kWave * k);
+    const bool in = g < gpr;
+    t.lg[k] = in ? g : gpr - 1;
+    t.act |= (in ? 1u : 0u) << k;
+  }
+  return t;
+}
+
+// One wave per run of `rows_per_wave` consecutive rows.  Its tiles form one
+// sequence over those rows; the loads of tile q+1 (coded weights, and x at
+// batch 1) are in flight while tile q is rebuilt, patched and multiplied, two
+// register sets alternating (the loop is unrolled by two), and the escape
+// cursor found for the run's first row is carried to its end.
 template <int LAYOUT, int B>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   __shared__ uint32_t T2[256];
@@ -81,72 +161,148 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
-  const int lane = lane_id();
-  const int wib = (int)(threadIdx.x / kWave);
-  const uint64_t r = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wib;
-  if (r >= a.rows) return;
+  const int wib = wave_in_block();
+  const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wib;
+  const uint64_t r0 = wave * a.rows_per_wave;
+  if (r0 >= a.rows) return;
+  const uint64_t r1 = r0 + a.rows_per_wave < a.rows ? r0 + a.rows_per_wave : a.rows;
+  const uint64_t gpr = a.cols / kGroup;                              // groups per row
+  const uint64_t tpr = (gpr + kTile / kGroup - 1) / (kTile / kGroup);  // tiles per row
 
-  const uint64_t cpr = a.cols / kChunk;  // chunks per row
-  const uint64_t row_start = r * a.cols;
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, row_start) : 0;
+  // x at batch 1 rides along with the weights in the prefetch ring when
+  // kGemvPrefetchX; otherwise it is read (from L2) when the tile is used.
+  constexpr bool kXpf = B == 1 && kGemvPrefetchX;
+  struct Slot {
+    Lane4 l;
+    uint32_t xv[kXpf ? 16 : 1];
+    uint32_t act;
+  };
+  auto load_tile = [&](const TileCursor& c, Slot& s) {
+    const RowTile rt = row_tile(c.ct, gpr);
+    s.act = rt.act;
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k) {
+      load_group<LAYOUT>(a.codes, a.raw, c.r * gpr + rt.lg[k], a.raw_last, s.l.codes[k], s.l.raw[k]);
+      if (!((rt.act >> k) & 1u)) s.l.codes[k] = 0;  // no weights, no escapes
+    }
+    if (kXpf) load_x_lane(a.x, rt.lg, s.xv);
+  };
+
+  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
+  EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 
-  for (uint64_t c0 = 0; c0 < cpr; c0 += kWave) {
-    const uint64_t cc = c0 + (uint64_t)lane;
-    const bool active = cc < cpr;
-    Chunk c;
-    if (active) {
-      load_chunk_full<LAYOUT>(a.codes, a.raw, row_start / kChunk + cc, c);
-    } else {
-      c.codes = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) c.raw[k] = 0;
-    }
-    const uint32_t cnt = count_escapes(c.codes);
+  auto process = [&](const TileCursor& c, const Slot& s) {
+    const RowTile rt = row_tile(c.ct, gpr);
+    uint32_t xv[kXpf ? 1 : 16];
+    if (!kXpf && B == 1) load_x_lane(a.x, rt.lg, xv);  // in flight during the rebuild
+    uint32_t gmask;
+    const uint32_t cnt = count_escapes(s.l, &gmask);
     uint32_t w[16];
-    rebuild_chunk<LAYOUT>(T2, c, w);
+    rebuild_lane<LAYOUT>(T2, a.dict, s.l, w);
     if (__ballot(cnt != 0)) {
-      const uint32_t cnt_wave = wave_sum_u32(cnt);
-      const uint64_t tile_start = row_start + c0 * kChunk;
-      const uint64_t left = a.cols - c0 * kChunk;
-      patch_tile<LAYOUT>(stage[wib], w, a.esc_pos, a.esc_sym, a.n_esc, e, cnt_wave, tile_start,
-                         left >= kTile ? kTile : (uint32_t)left);
+      const uint32_t cnt_wave = wave_sum_small(cnt);
+      const uint64_t tile_start = c.r * a.cols + c.ct * kTile;
+      const uint64_t left = a.cols - c.ct * kTile;
+      patch_tile<LAYOUT>(stage[wib], w, gmask, a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
+                         cnt_wave, tile_start, left >= kTile ? kTile : (uint32_t)left, eb);
       e += cnt_wave;
     }
-    if (active) dot_chunk<B>(w, a.x, a.cols, cc * kChunk, acc);
-  }
-  store_row<B>(acc, a.y, a.rows, r);
+    eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+    // groups outside the row contribute nothing
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k)
+      if (!((s.act >> k) & 1u)) w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = 0;
+    if (B == 1) {
+      if constexpr (kXpf)
+        acc[0] = dot_lane(w, s.xv, acc[0]);
+      else
+        acc[0] = dot_lane(w, xv, acc[0]);
+    } else {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        uint32_t xb[16];
+        load_x_lane(a.x + (uint64_t)b * a.cols, rt.lg, xb);
+        acc[b] = dot_lane(w, xb, acc[b]);
+      }
+    }
+    if (c.ct + 1 == tpr) {
+      store_row<B>(acc, a.y, a.rows, c.r);
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    }
+  };
+
+  run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, load_tile, process);
 }
 
+// The same wave/tile schedule as k_decode_gemv with W read as plain BF16
+// (16 bytes per group) and no rebuild: the comparison kernel.
 template <int B>
 __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16(GemvArgs a) {
-  const int lane = lane_id();
-  const uint64_t r = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + threadIdx.x / kWave;
-  if (r >= a.rows) return;
-  const uint64_t cpr = a.cols / kChunk;
-  const uint16_t* wr = a.w + r * a.cols;
+  const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wave_in_block();
+  const uint64_t r0 = wave * a.rows_per_wave;
+  if (r0 >= a.rows) return;
+  const uint64_t r1 = r0 + a.rows_per_wave < a.rows ? r0 + a.rows_per_wave : a.rows;
+  const uint64_t gpr = a.cols / kGroup;
+  const uint64_t tpr = (gpr + kTile / kGroup - 1) / (kTile / kGroup);
+
+  constexpr bool kXpf = B == 1 && kGemvPrefetchX;
+  struct Slot {
+    uint32_t w[16];
+    uint32_t xv[kXpf ? 16 : 1];
+    uint32_t act;
+  };
+  auto load_tile = [&](const TileCursor& c, Slot& s) {
+    const RowTile rt = row_tile(c.ct, gpr);
+    s.act = rt.act;
+    const u32x4* wr = (const u32x4*)(a.w + c.r * a.cols);
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k) {
+      const u32x4 v = __builtin_nontemporal_load(wr + rt.lg[k]);
+      s.w[4 * k] = v[0]; s.w[4 * k + 1] = v[1]; s.w[4 * k + 2] = v[2]; s.w[4 * k + 3] = v[3];
+    }
+    if (kXpf) load_x_lane(a.x, rt.lg, s.xv);
+  };
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-  for (uint64_t c0 = 0; c0 < cpr; c0 += kWave) {
-    const uint64_t cc = c0 + (uint64_t)lane;
-    if (cc < cpr) {
-      const u32x4* wp = (const u32x4*)(wr + cc * kChunk);
-      uint32_t w[16];
+  auto process = [&](const TileCursor& c, const Slot& s) {
+    const RowTile rt = row_tile(c.ct, gpr);
+    uint32_t xv[kXpf ? 1 : 16];
+    if (!kXpf && B == 1) load_x_lane(a.x, rt.lg, xv);
+    uint32_t w[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 v = __builtin_nontemporal_load(wp + k);
-        w[4 * k] = v[0]; w[4 * k + 1] = v[1]; w[4 * k + 2] = v[2]; w[4 * k + 3] = v[3];
-      }
-      dot_chunk<B>(w, a.x, a.cols, cc * kChunk, acc);
+    for (int k = 0; k < kLaneGroups; ++k) {
+      const bool in = (s.act >> k) & 1u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[4 * k + j] = in ? s.w[4 * k + j] : 0u;
     }
-  }
-  store_row<B>(acc, a.y, a.rows, r);
+    if (B == 1) {
+      if constexpr (kXpf)
+        acc[0] = dot_lane(w, s.xv, acc[0]);
+      else
+        acc[0] = dot_lane(w, xv, acc[0]);
+    } else {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        uint32_t xb[16];
+        load_x_lane(a.x + (uint64_t)b * a.cols, rt.lg, xb);
+        acc[b] = dot_lane(w, xb, acc[b]);
+      }
+    }
+    if (c.ct + 1 == tpr) {
+      store_row<B>(acc, a.y, a.rows, c.r);
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    }
+  };
+  run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, load_tile, process);
 }
 
-// ---- generic shapes (cols % 32 != 0): one weight per lane per step --------
+// ---- generic shapes (cols % 8 != 0): one weight per lane per step ---------
 
 __device__ inline float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -156,7 +312,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_generic(GemvArgs 
   if (threadIdx.x < 16) dsym[threadIdx.x] = a.dict.sym[threadIdx.x];
   __syncthreads();
   const int lane = lane_id();
-  const uint64_t r = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + threadIdx.x / kWave;
+  const uint64_t r = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wave_in_block();
   if (r >= a.rows) return;
   const uint64_t row_start = r * a.cols;
   const uint64_t n = a.rows * a.cols;
@@ -211,7 +367,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_generic(GemvArgs 
 
 __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16_generic(GemvArgs a) {
   const int lane = lane_id();
-  const uint64_t r = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + threadIdx.x / kWave;
+  const uint64_t r = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wave_in_block();
   if (r >= a.rows) return;
   float acc[WC_MAX_BATCH];
 #pragma unroll
@@ -243,8 +399,23 @@ static dim3 row_grid(uint64_t rows) {
   return dim3((unsigned)((rows + wpb - 1) / wpb));
 }
 
+// Rows per wave: enough tiles per wave (about 4) to amortise the escape
+// cursor search, while leaving many waves for the scheduler to balance.
+static uint64_t rows_per_wave(uint64_t cols) {
+  const uint64_t tpr = (cols + kTile - 1) / kTile;
+  return tpr >= 4 ? 1 : (4 + tpr - 1) / tpr;
+}
+
+static dim3 wave_grid(uint64_t rows, uint64_t rpw) {
+  const uint64_t waves = (rows + rpw - 1) / rpw;
+  const uint64_t wpb = kBlockThreads / kWave;
+  return dim3((unsigned)((waves + wpb - 1) / wpb));
+}
+
 template <int LAYOUT>
-static void launch_fused_fast(const GemvArgs& a, hipStream_t s) {
+static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
+  GemvArgs a = a0;
+  a.rows_per_wave = rows_per_wave(a.cols);
   // Batch sizes 1, 2, 4, 8 and 16 have their own kernels; other sizes run as
   // a sum of those over consecutive slices of x and y.
   uint32_t done = 0;
@@ -255,7 +426,7 @@ static void launch_fused_fast(const GemvArgs& a, hipStream_t s) {
     p.y = a.y + (uint64_t)done * a.rows;
     uint32_t b = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
     p.batch = b;
-    const dim3 g = row_grid(a.rows), t(kBlockThreads);
+    const dim3 g = wave_grid(a.rows, a.rows_per_wave), t(kBlockThreads);
     switch (b) {
       case 16: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 16>), g, t, 0, s, p); break;
       case 8: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 8>), g, t, 0, s, p); break;
@@ -288,10 +459,16 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
   a.rows = rows;
   a.cols = cols;
   a.n_esc = h.n_esc;
-  a.raw_padded = pad16(raw_bytes(h.layout, h.n));
+  // with no escapes, the (never used) escape loads read the container header
+  a.esc_last = h.n_esc ? h.n_esc - 1 : 0;
+  if (h.n_esc == 0) {
+    a.esc_pos = (const uint32_t*)container;
+    a.esc_sym = container;
+  }
+  a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
   a.batch = batch;
   a.dict = dict_of(&h);
-  if (cols % kChunk == 0) {
+  if (cols % kGroup == 0) {
     if (h.layout == WC_LAYOUT_K15)
       launch_fused_fast<WC_LAYOUT_K15>(a, s);
     else
@@ -322,10 +499,11 @@ hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, con
   a.rows = rows;
   a.cols = cols;
   a.batch = batch;
-  if (cols % kChunk != 0) {
+  if (cols % kGroup != 0) {
     hipLaunchKernelGGL(k_gemv_bf16_generic, row_grid(rows), dim3(kBlockThreads), 0, s, a);
     return hipGetLastError();
   }
+  a.rows_per_wave = rows_per_wave(cols);
   uint32_t done = 0;
   while (done < batch) {
     const uint32_t left = batch - done;
@@ -334,7 +512,7 @@ hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, con
     p.y = y + (uint64_t)done * rows;
     uint32_t b = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
     p.batch = b;
-    const dim3 g = row_grid(rows), t(kBlockThreads);
+    const dim3 g = wave_grid(rows, a.rows_per_wave), t(kBlockThreads);
     switch (b) {
       case 16: hipLaunchKernelGGL(k_gemv_bf16<16>, g, t, 0, s, p); break;
       case 8: hipLaunchKernelGGL(k_gemv_bf16<8>, g, t, 0, s, p); break;
