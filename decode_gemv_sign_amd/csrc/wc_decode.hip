@@ -34,7 +34,7 @@ struct DecodeArgs {
 template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   __shared__ uint32_t T2[256];
-  __shared__ uint32_t stage[kBlockThreads / kWave][kTile / 2];
+  __shared__ uint32_t stage[kBlockThreads / kWave][kStageDwords];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -58,10 +58,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
 
   // rebuild + escapes of tile t into out[16] (lane's 4 groups)
   auto rebuild = [&](uint64_t t, const Lane4& l, uint32_t out[16]) {
-    uint32_t gmask;
-    const uint32_t cnt = count_escapes(l, &gmask);
+    uint32_t marks[kLaneGroups];
+    const bool any = escape_marks(l, marks);
     rebuild_lane<LAYOUT>(T2, a.dict, l, out);
-    if (__ballot(cnt != 0)) {
+    if (__ballot(any)) {
+      uint32_t gmask;
+      const uint32_t cnt = count_marks(marks, &gmask);
       const uint32_t cnt_wave = wave_sum_small(cnt);
       const uint64_t tile_start = t * kTile;
       const uint32_t tile_len = a.n - tile_start >= kTile ? kTile : (uint32_t)(a.n - tile_start);
@@ -75,10 +77,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   if (t0 < f1) {
     auto load_full = [&](uint64_t t, Lane4& l) {
       const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
+      const GroupBase gb = group_base(LAYOUT, a.codes, a.raw, tc * (kTile / kGroup), a.raw_last);
 #pragma unroll
       for (int k = 0; k < kLaneGroups; ++k)
-        load_group<LAYOUT>(a.codes, a.raw, tc * (kTile / kGroup) + lane + kWave * k, a.raw_last,
-                           l.codes[k], l.raw[k]);
+        load_group<LAYOUT>(gb, (uint32_t)(lane + kWave * k), l.codes[k], l.raw[k]);
     };
     auto process = [&](uint64_t t, const Lane4& l) {
       uint32_t out[16];
@@ -106,15 +108,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     const uint64_t tile_start = full_tiles * kTile;
     Lane4 l;
     uint32_t valid[kLaneGroups];
+    const GroupBase gb = group_base(LAYOUT, a.codes, a.raw, full_tiles * (kTile / kGroup), a.raw_last);
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
-      const uint64_t g = full_tiles * (kTile / kGroup) + lane + kWave * k;
-      const uint64_t w0 = g * kGroup;
+      const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;
       valid[k] = w0 < a.n ? (a.n - w0 >= kGroup ? kGroup : (uint32_t)(a.n - w0)) : 0u;
       l.codes[k] = 0;
       l.raw[k][0] = l.raw[k][1] = 0;
       if (valid[k]) {
-        load_group<LAYOUT>(a.codes, a.raw, g, a.raw_last, l.codes[k], l.raw[k]);
+        load_group<LAYOUT>(gb, (uint32_t)(lane + kWave * k), l.codes[k], l.raw[k]);
         if (valid[k] < kGroup) l.codes[k] &= (1u << (4 * valid[k])) - 1u;
       }
     }

@@ -57,12 +57,12 @@ __device__ inline float dot_lane(const uint32_t w[16], const uint32_t xv[16], fl
   return s0 + s1;
 }
 
-// x values of the lane's 4 groups (local groups lg[k] of the row) for batch row b.
-__device__ inline void load_x_lane(const uint16_t* __restrict__ x, const uint64_t lg[4],
+// x values of the lane's 4 groups; `xt` points at the tile's first x value.
+__device__ inline void load_x_lane(const uint16_t* __restrict__ xt, const uint32_t lg[4],
                                    uint32_t xv[16]) {
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) {
-    const u32x4 v = *((const u32x4*)x + lg[k]);
+    const u32x4 v = *((const u32x4*)xt + lg[k]);
     xv[4 * k] = v[0]; xv[4 * k + 1] = v[1]; xv[4 * k + 2] = v[2]; xv[4 * k + 3] = v[3];
   }
 }
@@ -127,23 +127,26 @@ __device__ inline void run_ring(uint64_t nq, TileCursor start, uint64_t tpr, Loa
   }
 }
 
-// Row tile (r, ct) = groups [256 ct, 256 ct + 256) of row r; lane L takes row
-// groups lg_k = 256 ct + L + 64 k that are inside the row (a lane past the row
-// end reloads the row's last group and drops it, so every path issues the
-// same loads).
+// Row tile (r, ct) = groups [256 ct, 256 ct + 256) of row r; lane L takes
+// tile groups lg_k = L + 64 k that are inside the row (a lane past the row end
+// reloads the row's last group and drops it, so every path issues the same
+// loads).  Only a row's last tile can be partial (a wave-uniform test).
 struct RowTile {
-  uint64_t lg[kLaneGroups];  // row-local group per k (clamped)
+  uint32_t lg[kLaneGroups];  // tile-local group per k (clamped)
   uint32_t act;              // bit k: group k is inside the row
+  bool partial;              // some lane's group lies past the row end
 };
 
 __device__ inline RowTile row_tile(uint64_t ct, uint64_t gpr) {
   RowTile t;
+  const uint64_t left = gpr - ct * (kTile / kGroup);  // groups of the row from this tile on
+  t.partial = left < (uint64_t)(kTile / kGroup);
   t.act = 0;
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) {
-    const uint64_t g = ct * (kTile / kGroup) + (uint64_t)(lane_id() + kWave * k);
-    const bool in = g < gpr;
-    t.lg[k] = in ? g : gpr - 1;
+    const uint32_t g = (uint32_t)(lane_id() + kWave * k);
+    const bool in = !t.partial || g < left;
+    t.lg[k] = in ? g : (uint32_t)left - 1u;
     t.act |= (in ? 1u : 0u) << k;
   }
   return t;
@@ -157,7 +160,7 @@ __device__ inline RowTile row_tile(uint64_t ct, uint64_t gpr) {
 template <int LAYOUT, int B>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   __shared__ uint32_t T2[256];
-  __shared__ uint32_t stage[kBlockThreads / kWave][kTile / 2];
+  __shared__ uint32_t stage[kBlockThreads / kWave][kStageDwords];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -180,12 +183,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   auto load_tile = [&](const TileCursor& c, Slot& s) {
     const RowTile rt = row_tile(c.ct, gpr);
     s.act = rt.act;
+    const GroupBase gb =
+        group_base(LAYOUT, a.codes, a.raw, c.r * gpr + c.ct * (kTile / kGroup), a.raw_last);
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
-      load_group<LAYOUT>(a.codes, a.raw, c.r * gpr + rt.lg[k], a.raw_last, s.l.codes[k], s.l.raw[k]);
-      if (!((rt.act >> k) & 1u)) s.l.codes[k] = 0;  // no weights, no escapes
+      load_group<LAYOUT>(gb, rt.lg[k], s.l.codes[k], s.l.raw[k]);
+      if (rt.partial && !((rt.act >> k) & 1u)) s.l.codes[k] = 0;  // no weights, no escapes
     }
-    if (kXpf) load_x_lane(a.x, rt.lg, s.xv);
+    if (kXpf) load_x_lane(a.x + c.ct * kTile, rt.lg, s.xv);
   };
 
   uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
@@ -197,12 +202,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   auto process = [&](const TileCursor& c, const Slot& s) {
     const RowTile rt = row_tile(c.ct, gpr);
     uint32_t xv[kXpf ? 1 : 16];
-    if (!kXpf && B == 1) load_x_lane(a.x, rt.lg, xv);  // in flight during the rebuild
-    uint32_t gmask;
-    const uint32_t cnt = count_escapes(s.l, &gmask);
+    if (!kXpf && B == 1) load_x_lane(a.x + c.ct * kTile, rt.lg, xv);  // in flight during the rebuild
+    uint32_t marks[kLaneGroups];
+    const bool any = escape_marks(s.l, marks);
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, a.dict, s.l, w);
-    if (__ballot(cnt != 0)) {
+    if (__ballot(any)) {
+      uint32_t gmask;
+      const uint32_t cnt = count_marks(marks, &gmask);
       const uint32_t cnt_wave = wave_sum_small(cnt);
       const uint64_t tile_start = c.r * a.cols + c.ct * kTile;
       const uint64_t left = a.cols - c.ct * kTile;
@@ -212,9 +219,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     }
     eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
     // groups outside the row contribute nothing
+    if (rt.partial) {
 #pragma unroll
-    for (int k = 0; k < kLaneGroups; ++k)
-      if (!((s.act >> k) & 1u)) w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = 0;
+      for (int k = 0; k < kLaneGroups; ++k)
+        if (!((s.act >> k) & 1u)) w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = 0;
+    }
     if (B == 1) {
       if constexpr (kXpf)
         acc[0] = dot_lane(w, s.xv, acc[0]);
@@ -224,7 +233,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         uint32_t xb[16];
-        load_x_lane(a.x + (uint64_t)b * a.cols, rt.lg, xb);
+        load_x_lane(a.x + (uint64_t)b * a.cols + c.ct * kTile, rt.lg, xb);
         acc[b] = dot_lane(w, xb, acc[b]);
       }
     }
@@ -258,13 +267,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16(GemvArgs a) {
   auto load_tile = [&](const TileCursor& c, Slot& s) {
     const RowTile rt = row_tile(c.ct, gpr);
     s.act = rt.act;
-    const u32x4* wr = (const u32x4*)(a.w + c.r * a.cols);
+    const u32x4* wr = (const u32x4*)(a.w + c.r * a.cols + c.ct * kTile);
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
       const u32x4 v = __builtin_nontemporal_load(wr + rt.lg[k]);
       s.w[4 * k] = v[0]; s.w[4 * k + 1] = v[1]; s.w[4 * k + 2] = v[2]; s.w[4 * k + 3] = v[3];
     }
-    if (kXpf) load_x_lane(a.x, rt.lg, s.xv);
+    if (kXpf) load_x_lane(a.x + c.ct * kTile, rt.lg, s.xv);
   };
   float acc[B];
 #pragma unroll
@@ -272,11 +281,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16(GemvArgs a) {
   auto process = [&](const TileCursor& c, const Slot& s) {
     const RowTile rt = row_tile(c.ct, gpr);
     uint32_t xv[kXpf ? 1 : 16];
-    if (!kXpf && B == 1) load_x_lane(a.x, rt.lg, xv);
+    if (!kXpf && B == 1) load_x_lane(a.x + c.ct * kTile, rt.lg, xv);
     uint32_t w[16];
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
-      const bool in = (s.act >> k) & 1u;
+      const bool in = !rt.partial || ((s.act >> k) & 1u);
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[4 * k + j] = in ? s.w[4 * k + j] : 0u;
     }
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16(GemvArgs a) {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         uint32_t xb[16];
-        load_x_lane(a.x + (uint64_t)b * a.cols, rt.lg, xb);
+        load_x_lane(a.x + (uint64_t)b * a.cols + c.ct * kTile, rt.lg, xb);
         acc[b] = dot_lane(w, xb, acc[b]);
       }
     }

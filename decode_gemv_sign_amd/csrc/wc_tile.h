@@ -26,6 +26,7 @@ namespace wc {
 
 constexpr int kGroup = 8;                             // weights per group
 constexpr int kLaneGroups = kTile / kGroup / kWave;   // groups per lane per tile (4)
+constexpr int kStageDwords = kTile / 2;             // per-wave LDS stage: one rebuilt tile
 
 // Pair table in LDS: entry p, a byte of the code stream (low nibble = even
 // weight, high nibble = odd weight), holds both weights' symbol bits already
@@ -45,34 +46,58 @@ struct Lane4 {
   uint32_t raw[kLaneGroups][2];  // byte-split: 8 low bytes; K15: 56 mantissa bits
 };
 
-// Global group g (weights [8g, 8g + 8)).  `raw_last` is the index of the last
-// dword of the raw stream's 16-byte padded extent: a K15 group's 7 bytes start
-// at byte 7g and are covered by 3 dwords; the second and third are clamped to
-// that extent (they pass it only when the group is the stream's last and its
-// remaining bytes are not needed).
+// The streams of one tile, positioned at its first group G (weights from
+// 8G): wave-uniform base pointers that lanes offset by 32-bit group indices,
+// which lets loads use a scalar base plus a 32-bit vector offset.
+struct GroupBase {
+  const uint32_t* codes;  // code dword of group G
+  const uint8_t* raw;     // byte-split: low bytes of group G; K15: the dword holding bit 56G
+  uint32_t skew;          // K15: (7G) mod 4, the byte offset of group G in that dword
+  uint32_t raw_lim;       // K15: last dword of the raw stream's padded extent, from `raw`
+};
+
+__device__ inline GroupBase group_base(int layout, const uint8_t* codes, const uint8_t* raw,
+                                       uint64_t G, uint64_t raw_last) {
+  GroupBase b;
+  b.codes = (const uint32_t*)codes + G;
+  if (layout == WC_LAYOUT_BYTESPLIT) {
+    b.raw = raw + 8u * G;
+    b.skew = 0;
+    b.raw_lim = 0;
+  } else {
+    const uint64_t d = (7u * G) >> 2;
+    b.raw = raw + 4u * d;
+    b.skew = (uint32_t)((7u * G) & 3u);
+    b.raw_lim = (uint32_t)(raw_last - d);
+  }
+  return b;
+}
+
+// Group G + lg.  A K15 group's 7 bytes are covered by 3 dwords; the second
+// and third are clamped to the raw stream's 16-byte padded extent (they pass
+// it only when the group is the stream's last and its remaining bytes are not
+// needed).
 template <int LAYOUT>
-__device__ inline void load_group(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ raw,
-                                  uint64_t g, uint64_t raw_last, uint32_t& c, uint32_t r[2]) {
-  c = __builtin_nontemporal_load((const uint32_t*)codes + g);
+__device__ inline void load_group(const GroupBase& b, uint32_t lg, uint32_t& c, uint32_t r[2]) {
+  c = __builtin_nontemporal_load(b.codes + lg);
   if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = __builtin_nontemporal_load((const u32x2*)raw + g);
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)b.raw + lg);
     r[0] = v[0];
     r[1] = v[1];
   } else {
-    const uint64_t b = 7u * g, d = b >> 2;
-    const uint32_t s = (uint32_t)(b & 3u) * 8u;
-    const uint32_t* rd = (const uint32_t*)raw;
+    const uint32_t byte = b.skew + 7u * lg, d = byte >> 2, s = (byte & 3u) * 8u;
+    const uint32_t* rd = (const uint32_t*)b.raw;
     const uint32_t d0 = __builtin_nontemporal_load(rd + d);
-    const uint32_t d1 = __builtin_nontemporal_load(rd + (d + 1 < raw_last ? d + 1 : raw_last));
-    const uint32_t d2 = __builtin_nontemporal_load(rd + (d + 2 < raw_last ? d + 2 : raw_last));
+    const uint32_t d1 = __builtin_nontemporal_load(rd + (d + 1 < b.raw_lim ? d + 1 : b.raw_lim));
+    const uint32_t d2 = __builtin_nontemporal_load(rd + (d + 2 < b.raw_lim ? d + 2 : b.raw_lim));
     r[0] = __builtin_amdgcn_alignbit(d1, d0, s);
     r[1] = __builtin_amdgcn_alignbit(d2, d1, s);
   }
 }
 
 #ifndef WC_REBUILD_VALU
-#define WC_REBUILD_VALU 1
+#define WC_REBUILD_VALU 0
 #endif
 
 // Four codes (one per byte, 0..15) -> the four bytes `tab` holds for them.
@@ -154,16 +179,26 @@ __device__ inline void rebuild_lane(const uint32_t* __restrict__ T2, const Dict&
   }
 }
 
-// Per-lane count of code-15 nibbles (escapes) among the lane's 32 codes, and
-// in *gmask bit k set when group k holds one.
-__device__ inline uint32_t count_escapes(const Lane4& l, uint32_t* gmask) {
-  uint32_t n = 0, g = 0;
+// Code-15 (escape) marks of the lane's groups: bit 4i of esc[k] is set when
+// weight i of group k escapes.  Returns whether the lane has any.
+__device__ inline bool escape_marks(const Lane4& l, uint32_t esc[kLaneGroups]) {
+  uint32_t any = 0;
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) {
     const uint32_t w = l.codes[k];
-    const uint32_t c = __popc(w & (w >> 1) & (w >> 2) & (w >> 3) & 0x11111111u);
-    n += c;
-    g |= (c ? 1u : 0u) << k;
+    esc[k] = w & (w >> 1) & (w >> 2) & (w >> 3) & 0x11111111u;
+    any |= esc[k];
+  }
+  return any != 0;
+}
+
+// Escape count of the lane, and in *gmask bit k set when group k holds one.
+__device__ inline uint32_t count_marks(const uint32_t esc[kLaneGroups], uint32_t* gmask) {
+  uint32_t n = 0, g = 0;
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) {
+    n += __popc(esc[k]);
+    g |= (esc[k] ? 1u : 0u) << k;
   }
   *gmask = g;
   return n;
