@@ -43,7 +43,22 @@ __global__ __launch_bounds__(kBlockThreads) void k_hist(const uint16_t* __restri
   const uint64_t gid = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   const uint64_t nvec = n / 8;
   const u32x4* wv = (const u32x4*)w;
-  for (uint64_t v = gid; v < nvec; v += stride) {
+  // four 16-byte loads in flight per thread, then their 32 symbol counts
+  uint64_t v = gid;
+  for (; v + 3 * stride < nvec; v += 4 * stride) {
+    u32x4 d[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[u] = __builtin_nontemporal_load(wv + v + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        atomicAdd(mine + ((d[u][k] >> 7) & 0x1FFu), 1u);
+        atomicAdd(mine + (d[u][k] >> 23), 1u);
+      }
+    }
+  }
+  for (; v < nvec; v += stride) {
     const u32x4 d = __builtin_nontemporal_load(wv + v);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -62,35 +77,64 @@ __global__ __launch_bounds__(kBlockThreads) void k_hist(const uint16_t* __restri
 }
 
 // ---- top-15 --------------------------------------------------------------
-// One workgroup of 512 threads, one symbol each: rank = number of symbols
-// with a larger count, or an equal count and a smaller value.  Symbols of
-// rank < 15 with a nonzero count form the dictionary in rank order.
+// One workgroup of 512 threads, one symbol each.  The symbols that occur are
+// first compacted (in symbol order) into a candidate list of m entries; each
+// then counts the candidates with a larger count, or an equal count and a
+// smaller value: that count is its rank.  Symbols of rank < 15 form the
+// dictionary in rank order.  Work is m^2 compares (m is the number of
+// distinct symbols, at most 512).
 
 __global__ __launch_bounds__(512) void k_top15(const uint32_t* __restrict__ hist, int layout,
                                                uint64_t n, DictResult* __restrict__ res) {
-  __shared__ uint32_t cnt[512];
+  __shared__ __attribute__((aligned(16))) uint32_t cand_cnt[512];
+  __shared__ uint16_t cand_sym[512];
   __shared__ uint16_t dict[16];
   __shared__ uint32_t wsum[8];
   __shared__ uint32_t wnum[8];
   const int i = threadIdx.x;
+  const int wv = i / kWave;
   const int nsym = layout == WC_LAYOUT_K15 ? 512 : 256;
   uint32_t c = 0;
   if (i < nsym) c = layout == WC_LAYOUT_K15 ? hist[i] : hist[2 * i] + hist[2 * i + 1];
-  cnt[i] = c;
   if (i < 16) dict[i] = 0;
+  // compact the occurring symbols, keeping symbol order
+  const uint32_t occ = c > 0 ? 1u : 0u;
+  const uint32_t ex = wave_excl_scan_u32(occ);
+  if (lane_id() == kWave - 1) wnum[wv] = ex + occ;
+  __syncthreads();
+  uint32_t before = 0, m = 0;
+  for (int q = 0; q < 8; ++q) {
+    before += q < wv ? wnum[q] : 0u;
+    m += wnum[q];
+  }
+  const uint32_t slot = before + ex;
+  if (occ) {
+    cand_cnt[slot] = c;
+    cand_sym[slot] = (uint16_t)i;
+  }
+  for (uint32_t q = m + (uint32_t)i; q < ((m + 3u) & ~3u); q += 512) cand_cnt[q] = 0;  // pad to 4
   __syncthreads();
   uint32_t rank = 0;
-  for (int j = 0; j < nsym; ++j) {
-    const uint32_t cj = cnt[j];
-    rank += (cj > c || (cj == c && j < i)) ? 1u : 0u;
+  if (occ) {
+    const u32x4* cc4 = (const u32x4*)cand_cnt;
+    for (uint32_t j4 = 0; 4 * j4 < m; ++j4) {
+      const u32x4 q = cc4[j4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t j = 4 * j4 + (uint32_t)k;
+        // candidates before this one in the list have smaller symbols
+        rank += (j < m && (q[k] > c || (q[k] == c && j < slot))) ? 1u : 0u;
+      }
+    }
   }
-  const bool in = i < nsym && c > 0 && rank < 15;
+  const bool in = occ && rank < 15;
   if (in) dict[rank] = (uint16_t)i;
   const uint32_t s = wave_sum_u32(in ? c : 0u);
   const uint32_t k = wave_sum_u32(in ? 1u : 0u);
+  __syncthreads();  // wnum is reused below
   if (lane_id() == 0) {
-    wsum[i / kWave] = s;
-    wnum[i / kWave] = k;
+    wsum[wv] = s;
+    wnum[wv] = k;
   }
   __syncthreads();
   if (i == 0) {
@@ -131,96 +175,121 @@ struct PackArgs {
   wc_header h;
 };
 
+// Block b encodes weights [8192 b, 8192 b + 8192): 1024 groups of 8, thread t
+// taking groups t, t+256, t+512, t+768, so every 16-byte input load of a wave
+// covers 1 KB of contiguous weights.  The block's code and raw bytes are
+// assembled in a zero-filled LDS image (K15 groups are 7 bytes, unaligned)
+// and written out with aligned 16-byte stores up to each stream's padded end,
+// which also writes the streams' zero padding.
 template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
+  constexpr int kGroups = kPackBlock / 8;                                  // 1024
+  constexpr int kRawBytes = LAYOUT == WC_LAYOUT_K15 ? 7 * kGroups : 8 * kGroups;
   __shared__ uint8_t lut[512];
   __shared__ uint32_t wsum[kBlockThreads / kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t img_codes[kGroups];     // 4 KB
+  __shared__ __attribute__((aligned(16))) uint32_t img_raw[kRawBytes / 4];  // 7 or 8 KB
   const int tid = threadIdx.x;
   for (int sidx = tid; sidx < 512; sidx += kBlockThreads) lut[sidx] = 15;
+  for (int q = tid; q < kGroups; q += kBlockThreads) img_codes[q] = 0;
+  for (int q = tid; q < kRawBytes / 4; q += kBlockThreads) img_raw[q] = 0;
   __syncthreads();
   if (tid < (int)a.h.n_dict) lut[a.h.dict[tid]] = (uint8_t)tid;
   __syncthreads();
 
   const wc_header& h = a.h;
-  uint8_t* codes = a.container + h.off_codes;
-  uint8_t* raw = a.container + h.off_raw;
-  const uint64_t raw_pad = pad16(raw_bytes(LAYOUT, a.n));
-  const uint64_t chunk = (uint64_t)blockIdx.x * kBlockThreads + (uint64_t)tid;
-  const uint64_t base = chunk * kChunk;
+  const uint64_t w0 = (uint64_t)blockIdx.x * kPackBlock;  // first weight of the block
   uint32_t esc = 0;
-  if (base < a.n) {
-    const uint32_t valid = a.n - base >= kChunk ? kChunk : (uint32_t)(a.n - base);
-    uint32_t wd[16];  // weights 2j (low half) and 2j+1 (high half)
-    if (valid == kChunk) {
-      const u32x4* src = (const u32x4*)(a.w + base);
+  uint8_t* rimg = (uint8_t*)img_raw;
+  // a full block (every block but possibly the last) loads its four groups at once
+  const bool full = w0 + kPackBlock <= a.n;
+  u32x4 pre[4];
+  if (full) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 v = __builtin_nontemporal_load(src + k);
-        wd[4 * k] = v[0]; wd[4 * k + 1] = v[1]; wd[4 * k + 2] = v[2]; wd[4 * k + 3] = v[3];
-      }
+    for (int j = 0; j < 4; ++j)
+      pre[j] = __builtin_nontemporal_load((const u32x4*)(a.w + w0) + tid + kBlockThreads * j);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int g = tid + kBlockThreads * j;  // group within the block
+    const uint64_t gw = w0 + 8u * (uint64_t)g;
+    if (gw >= a.n) continue;
+    const uint32_t valid = a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
+    uint32_t wd[4];  // weights 2i (low half) and 2i+1 (high half)
+    if (full) {
+      wd[0] = pre[j][0]; wd[1] = pre[j][1]; wd[2] = pre[j][2]; wd[3] = pre[j][3];
+    } else if (valid == 8) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + gw));
+      wd[0] = v[0]; wd[1] = v[1]; wd[2] = v[2]; wd[3] = v[3];
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t lo = (uint32_t)(2 * j) < valid ? a.w[base + 2 * j] : 0u;
-        const uint32_t hi = (uint32_t)(2 * j + 1) < valid ? a.w[base + 2 * j + 1] : 0u;
-        wd[j] = lo | (hi << 16);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (uint32_t)(2 * i) < valid ? a.w[gw + 2 * i] : 0u;
+        const uint32_t hi = (uint32_t)(2 * i + 1) < valid ? a.w[gw + 2 * i + 1] : 0u;
+        wd[i] = lo | (hi << 16);
       }
     }
-    // codes: nibble i of the chunk = code of weight i (even weight in the low nibble)
-    uint32_t cd[4] = {0, 0, 0, 0};
+    // codes: nibble i = code of weight i (even weight in the low nibble)
+    uint32_t cd = 0;
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const uint32_t b = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
       const uint32_t code = (uint32_t)i < valid ? lut[b >> (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)] : 0u;
       esc += code == 15u ? 1u : 0u;
-      cd[i >> 3] |= code << (4 * (i & 7));
+      cd |= code << (4 * i);
     }
-    *(u32x4*)(codes + 16u * chunk) = u32x4{cd[0], cd[1], cd[2], cd[3]};
+    img_codes[g] = cd;
     if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
-      // low bytes of weights 4m..4m+3 from two input dwords
-      uint32_t rw[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) rw[m] = __builtin_amdgcn_perm(wd[2 * m + 1], wd[2 * m], 0x06040200u);
-      if (valid < kChunk) {
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i)
-          if ((uint32_t)i >= valid) rw[i >> 2] &= ~(0xFFu << (8 * (i & 3)));
+      // low bytes of weights 0..3 and 4..7
+      uint32_t r0 = __builtin_amdgcn_perm(wd[1], wd[0], 0x06040200u);
+      uint32_t r1 = __builtin_amdgcn_perm(wd[3], wd[2], 0x06040200u);
+      if (valid < 8) {
+        const uint64_t keep = valid ? (~0ull >> (64 - 8 * valid)) : 0ull;
+        r0 &= (uint32_t)keep;
+        r1 &= (uint32_t)(keep >> 32);
       }
-      const uint64_t off = 32u * chunk;
-      if (off + 16u <= raw_pad) *(u32x4*)(raw + off) = u32x4{rw[0], rw[1], rw[2], rw[3]};
-      if (off + 32u <= raw_pad) *(u32x4*)(raw + off + 16u) = u32x4{rw[4], rw[5], rw[6], rw[7]};
+      img_raw[2 * g] = r0;
+      img_raw[2 * g + 1] = r1;
     } else {
-      // mantissa i at bits [7i, 7i+7) of the chunk's 224-bit window
-      uint32_t rw[7] = {0, 0, 0, 0, 0, 0, 0};
+      // 8 mantissas of 7 bits = 56 bits, LSB first, at byte 7g of the image
+      uint64_t m = 0;
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
-        const uint32_t m = (uint32_t)i < valid ? (wd[i >> 1] >> (16 * (i & 1))) & 0x7Fu : 0u;
-        const int bit = 7 * i, d = bit >> 5, s = bit & 31;
-        rw[d] |= m << s;
-        if (s > 25) rw[d + 1] |= m >> (32 - s);
+      for (int i = 0; i < 8; ++i) {
+        const uint64_t mi = (uint32_t)i < valid ? (wd[i >> 1] >> (16 * (i & 1))) & 0x7Fu : 0u;
+        m |= mi << (7 * i);
       }
-      const uint64_t off = 28u * chunk;
 #pragma unroll
-      for (int k = 0; k < 7; ++k)
-        if (off + 4u * k + 4u <= raw_pad) *(uint32_t*)(raw + off + 4u * k) = rw[k];
+      for (int k = 0; k < 7; ++k) rimg[7 * g + k] = (uint8_t)(m >> (8 * k));
     }
   }
   // escape count of the block
   const uint32_t ws = wave_sum_u32(esc);
   if (lane_id() == 0) wsum[tid / kWave] = ws;
   __syncthreads();
-  if (tid == 0 && (uint64_t)blockIdx.x * kPackBlock < a.n) {  // n == 0 has no blocks to count
+  if (tid == 0 && w0 < a.n) {  // n == 0 has no blocks to count
     uint32_t t = 0;
     for (int q = 0; q < kBlockThreads / kWave; ++q) t += wsum[q];
     a.blk_cnt[blockIdx.x] = t;
   }
-  // header and the zero gaps no chunk writes
+  // the block's stream images, up to each stream's padded end
+  {
+    const uint64_t cpad = pad16((a.n + 1u) / 2u);
+    const uint64_t c0 = (uint64_t)blockIdx.x * (kGroups * 4u);
+    const uint64_t cend = c0 + kGroups * 4u < cpad ? c0 + kGroups * 4u : cpad;
+    u32x4* dst = (u32x4*)(a.container + h.off_codes + c0);
+    const u32x4* srcv = (const u32x4*)img_codes;
+    for (uint64_t q = tid; c0 + 16u * q < cend; q += kBlockThreads) dst[q] = srcv[q];
+    const uint64_t rpad = pad16(raw_bytes(LAYOUT, a.n));
+    const uint64_t r0 = (uint64_t)blockIdx.x * kRawBytes;
+    const uint64_t rend = r0 + kRawBytes < rpad ? r0 + kRawBytes : rpad;
+    u32x4* rdst = (u32x4*)(a.container + h.off_raw + r0);
+    const u32x4* rsrc = (const u32x4*)img_raw;
+    for (uint64_t q = tid; r0 + 16u * q < rend; q += kBlockThreads) rdst[q] = rsrc[q];
+  }
+  // header and the escape streams' zero gaps
   if (blockIdx.x == 0) {
     if (tid < 32) ((uint32_t*)a.container)[tid] = ((const uint32_t*)&a.h)[tid];
     if (tid == 32) {
-      const uint64_t nchunks = (a.n + kChunk - 1) / kChunk;
-      const uint64_t written = LAYOUT == WC_LAYOUT_K15 ? 28u * nchunks : raw_pad;
-      for (uint64_t o = written; o < raw_pad; ++o) raw[o] = 0;
       const uint64_t pe = h.off_esc_pos + 4u * h.n_esc;
       for (uint64_t o = pe; o < h.off_esc_sym; ++o) a.container[o] = 0;
       const uint64_t se = h.off_esc_sym + sym_bytes(LAYOUT) * h.n_esc;
