@@ -34,7 +34,7 @@ struct DecodeArgs {
 template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   __shared__ uint32_t T2[256];
-  __shared__ uint32_t stage[kBlockThreads / kWave][kStageDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kBlockThreads / kWave][kStageDwords];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -54,24 +54,27 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   const uint64_t full_tiles = a.n / kTile;
   const uint64_t f1 = t1 < full_tiles ? t1 : full_tiles;  // end of this wave's full tiles
   uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile) : 0;
-  EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
 
-  // rebuild + escapes of tile t into out[16] (lane's 4 groups)
-  auto rebuild = [&](uint64_t t, const Lane4& l, uint32_t out[16]) {
+  // Rebuild + escapes of tile t into out[16] (the lane's 4 groups).  The
+  // tile's first escape records come in `eb` (loaded while the previous tile
+  // was processed); the next tile's are issued into `eb_next` as soon as
+  // this tile's escape count is known, so they arrive during its rebuild.
+  auto rebuild = [&](uint64_t t, const Lane4& l, const EscBatch& eb, EscBatch& eb_next,
+                     uint32_t out[16]) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
+    uint32_t gmask;
+    const uint32_t cnt = count_marks(marks, &gmask);
+    const uint32_t cnt_wave = __ballot(any) ? wave_sum_small(cnt) : 0u;
+    eb_next = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave);
     rebuild_lane<LAYOUT>(T2, a.dict, l, out);
-    if (__ballot(any)) {
-      uint32_t gmask;
-      const uint32_t cnt = count_marks(marks, &gmask);
-      const uint32_t cnt_wave = wave_sum_small(cnt);
+    if (cnt_wave) {
       const uint64_t tile_start = t * kTile;
       const uint32_t tile_len = a.n - tile_start >= kTile ? kTile : (uint32_t)(a.n - tile_start);
-      patch_tile<LAYOUT>(stage[wib], out, gmask, a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e, cnt_wave,
-                         tile_start, tile_len, eb);
-      e += cnt_wave;
+      patch_tile<LAYOUT>(stage[wib], out, gmask, a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
+                         cnt_wave, tile_start, tile_len, eb);
     }
-    eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+    e += cnt_wave;
   };
 
   if (t0 < f1) {
@@ -82,24 +85,32 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
       for (int k = 0; k < kLaneGroups; ++k)
         load_group<LAYOUT>(gb, (uint32_t)(lane + kWave * k), l.codes[k], l.raw[k]);
     };
-    auto process = [&](uint64_t t, const Lane4& l) {
+    struct Slot {
+      Lane4 l;
+      EscBatch eb;
+    };
+    auto process = [&](uint64_t t, const Slot& cur, Slot& nxt) {
       uint32_t out[16];
-      rebuild(t, l, out);
+      rebuild(t, cur.l, cur.eb, nxt.eb, out);
       u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
 #pragma unroll
       for (int k = 0; k < kLaneGroups; ++k)
         __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
                                     dst + kWave * k);
     };
-    Lane4 la, lb;
-    load_full(t0, la);
-    for (uint64_t t = t0; t < f1; t += 2) {
-      load_full(t + 1, lb);
-      process(t, la);
-      if (t + 1 >= f1) break;
-      load_full(t + 2, la);
-      process(t + 1, lb);
+    // Two slots alternate (static register sets); an odd last tile runs
+    // after the loop, so no path leaves the loop body half-way.
+    Slot sa, sb;
+    sa.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+    load_full(t0, sa.l);
+    uint64_t t = t0;
+    for (; t + 1 < f1; t += 2) {
+      load_full(t + 1, sb.l);
+      process(t, sa, sb);
+      load_full(t + 2, sa.l);
+      process(t + 1, sb, sa);
     }
+    if (t < f1) process(t, sa, sb);
   }
   if (t1 > full_tiles) {
     // The tensor's partial last tile: groups past n are skipped, the group
@@ -121,7 +132,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
       }
     }
     uint32_t out[16];
-    rebuild(full_tiles, l, out);
+    const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+    EscBatch unused;
+    rebuild(full_tiles, l, eb, unused, out);
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
       const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;

@@ -1,0 +1,447 @@
+// wc_gemm.hip — decode fused into a batched GEMV on the matrix cores, and the
+// plain BF16 kernel of the same shape it is measured against.
+//
+// Page "Compresión de pesos LLM sin pérdida vs 8-bit GGUF: ¿qué está listo
+// para producción?", section "¿Qué significa “sin pérdida” para los pesos de
+// un LLM?": the coded weights stay on the GPU and the exact BF16 values are
+// rebuilt in registers right before the product.  With several input rows
+// (batch up to 16) the product is a skinny GEMM, y[b][r] = sum_c W[r][c]
+// x[b][c], and v_mfma_f32_16x16x32_bf16 computes it exactly as the scalar
+// definition does (exact BF16 products, fp32 sums) while x is reused by 16
+// weight rows at once instead of being re-read from L2 for every row.
+//
+// Block = 16 consecutive rows x all columns, S waves.  The columns are cut
+// into 128-wide chunks; at step q wave s takes chunk q*S + s, so the block
+// walks the rows left to right in lock step.  Lane l = r + 16 h of a wave
+// owns 32 consecutive weights of row r (columns 32h .. 32h+31 of the chunk,
+// 4 groups of 8): one 16-byte code load, one 32-byte (byte-split) or 28-byte
+// (K15) raw load and one 64-byte load of x row r (batch index r) per step,
+// all naturally aligned when cols is a multiple of 32.  For MFMA instance m
+// (0..3) the lane gives group m of its weights as operand A (row r) and the
+// matching 8 x values as operand B (batch column r): both operands put the
+// same column at the same (lane / 16, element) slot, so the 32-term dot
+// products are exactly the row-times-x sums over those columns.
+//
+// Escapes (page "Prueba de GLM-5.2 reduce la memoria BF16 en casi un 25%",
+// section "Cómo funciona la compresión"): the records are in position order,
+// so the records of a lane's weights are one contiguous run of the stream.
+// Each step every wave counts the code-15 marks of its chunk per row and the
+// waves swap these counts through LDS; every lane then knows the first record
+// of its own weights (row cursor + counts of the chunks and lanes to its
+// left), loads the symbols of its run as one window and writes them into the
+// placeholders of its rebuilt weights.  The row cursors start from one
+// search of the position stream per row.
+#include "wc_launch.h"
+#include "wc_tile.h"
+
+namespace wc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3a4 __attribute__((ext_vector_type(3), aligned(4)));
+
+constexpr int kMRows = 16;       // rows per block: the MFMA's M (and N = batch)
+constexpr int kStepCols = 128;   // columns per wave step
+constexpr int kLaneCols = 32;    // weights per lane per step
+
+struct GemmArgs {
+  const uint8_t* codes;
+  const uint8_t* raw;
+  const uint32_t* esc_pos;
+  const uint8_t* esc_sym;
+  const uint16_t* w;  // plain BF16 weights (comparator)
+  const uint16_t* x;
+  float* y;
+  uint64_t rows, cols, n_esc, sym_last;  // sym_last: last dword of the padded symbol stream
+  uint32_t batch, chunks;                // chunks: 128-column chunks per row
+  Dict dict;
+};
+
+__device__ inline f32x4 mfma_bf16(const uint32_t a[4], const uint32_t b[4], f32x4 c) {
+  const u32x4 av = {a[0], a[1], a[2], a[3]};
+  const u32x4 bv = {b[0], b[1], b[2], b[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                 __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+}
+
+// Barrier that orders only LDS: global loads in flight stay in flight.
+__device__ inline void block_lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Bit 8m + e of the result = bit 4e of esc[m] (weight e of group m escapes).
+__device__ inline uint32_t compress_marks(const uint32_t esc[kLaneGroups]) {
+  uint32_t M = 0;
+#pragma unroll
+  for (int m = 0; m < kLaneGroups; ++m) {
+    uint32_t t = esc[m];
+    t = (t | (t >> 3)) & 0x03030303u;
+    t = (t | (t >> 6)) & 0x000F000Fu;
+    t = (t | (t >> 12)) & 0xFFu;
+    M |= t << (8 * m);
+  }
+  return M;
+}
+
+template <int LAYOUT, bool PLAIN>
+struct GemmSlot {
+  uint32_t c[kLaneGroups];                                     // codes, group m in c[m]
+  uint32_t wr[PLAIN ? 16 : (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)];  // raw part, or plain BF16
+  uint32_t xv[16];                                             // 32 x values of batch row r
+};
+
+template <int LAYOUT, bool PLAIN, int S>
+__global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
+  constexpr bool kK15 = LAYOUT == WC_LAYOUT_K15;
+  constexpr int kWinDwords = kK15 ? 17 : 9;  // a lane's symbol window: 32 symbols + alignment
+  constexpr int kSymBytes = kK15 ? 2 : 1;
+  __shared__ uint32_t T2[PLAIN ? 1 : 256];
+  // rebuilt weights of lanes with escapes (16 dwords per lane); the final sums
+  __shared__ __attribute__((aligned(16))) uint32_t stage[S][kWave * (PLAIN ? 4 : 16)];
+  __shared__ uint32_t win[PLAIN ? 1 : S][PLAIN ? 1 : kWave * kWinDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t xcnt[2][kMRows][S];  // escapes per row in each wave's chunk
+  __shared__ uint64_t erow0[kMRows];
+  if constexpr (!PLAIN) build_pair_table<LAYOUT>(T2, a.dict);
+
+  const int lane = lane_id(), r = lane & 15, h = lane >> 4;
+  const int s = wave_in_block();
+  const uint64_t r0 = (uint64_t)blockIdx.x * kMRows;
+  const bool row_ok = r0 + r < a.rows;
+  // Lane l feeds x row r (batch column r of the product); lanes past the
+  // batch re-read row 0, and their output columns are dropped.
+  const bool x_ok = (uint32_t)r < a.batch;
+  const uint32_t n_steps = (a.chunks + S - 1) / S;
+  const bool esc = !PLAIN && a.n_esc != 0;
+
+  // Row cursors: first record at or after each row's start.
+  if (esc) {
+    for (int rr = s; rr < kMRows; rr += S) {
+      const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
+      const uint64_t e = wave_lower_bound(a.esc_pos, a.n_esc, t);
+      if (lane == 0) erow0[rr] = e;
+    }
+  }
+  __syncthreads();  // pair table and cursors (nothing is in flight yet)
+  uint64_t e_row = esc ? erow0[r] : 0;
+
+  // Addresses: a wave-uniform base (the block's first row, the step's
+  // chunk) plus a per-lane 32-bit offset (row r, columns 32h), so every load
+  // is a scalar base + vector offset.  Lanes whose columns lie past the row
+  // end (only in a partial last chunk) or whose row lies past the matrix
+  // re-read valid data of their own wave and are masked later.
+  const uint32_t r_c = row_ok ? (uint32_t)r : (uint32_t)(a.rows - 1 - r0);
+  const uint32_t lane_elt = r_c * (uint32_t)a.cols + (uint32_t)(kLaneCols * h);  // element offset
+  const uint32_t lane_elt0 = r_c * (uint32_t)a.cols;                            // columns 0..31
+  const uint32_t x_elt = (x_ok ? (uint32_t)r : 0u) * (uint32_t)a.cols + (uint32_t)(kLaneCols * h);
+  const uint32_t x_elt0 = (x_ok ? (uint32_t)r : 0u) * (uint32_t)a.cols;
+  const uint64_t blk_elt = r0 * a.cols;  // first weight of the block
+
+  // Whether the lane's 32 columns at step q are inside the row.
+  auto lane_ok = [&](uint32_t q) -> bool {
+    const uint32_t j = q * S + (uint32_t)s;
+    return j < a.chunks && (uint64_t)j * kStepCols + (uint64_t)(kLaneCols * h) < a.cols;
+  };
+
+  // Whether the 32-column block u of the step-q chunk is inside the rows
+  // (wave-uniform).
+  auto block_ok = [&](uint32_t q, int u) -> bool {
+    const uint32_t j = q * S + (uint32_t)s;
+    return j < a.chunks && (uint64_t)j * kStepCols + (uint64_t)(32 * u) < a.cols;
+  };
+
+  using Slot = GemmSlot<LAYOUT, PLAIN>;
+  auto load = [&](uint32_t q, Slot& sl) {
+    const uint32_t j = q * S + (uint32_t)s;
+    const uint32_t jc = j < a.chunks ? j : a.chunks - 1;
+    const bool ok = lane_ok(q);
+    const uint64_t base = blk_elt + (uint64_t)jc * kStepCols;  // uniform, a multiple of 32
+    const uint32_t le = ok ? lane_elt : lane_elt0;               // multiple of 32
+    const uint32_t xe = ok ? x_elt : x_elt0;
+    if constexpr (PLAIN) {
+      // plain BF16, interleaved: group 4u + h of the chunk for instance u, so
+      // each load reads 64 contiguous bytes of every row; a 32-column block
+      // past the row end re-reads block 0 (its product is skipped)
+      const u32x4* wp = (const u32x4*)(a.w + base);
+      const u32x4* xq = (const u32x4*)(a.x + (uint64_t)jc * kStepCols);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t g = (block_ok(q, u) ? 4u * u : 0u) + (uint32_t)h;
+        const u32x4 v = __builtin_nontemporal_load(wp + (lane_elt0 / 8 + g));
+        sl.wr[4 * u] = v[0]; sl.wr[4 * u + 1] = v[1]; sl.wr[4 * u + 2] = v[2]; sl.wr[4 * u + 3] = v[3];
+        const u32x4 xv = *(xq + (x_elt0 / 8 + g));
+        sl.xv[4 * u] = xv[0]; sl.xv[4 * u + 1] = xv[1]; sl.xv[4 * u + 2] = xv[2]; sl.xv[4 * u + 3] = xv[3];
+      }
+      return;
+    } else {
+      const u32x4 cv = __builtin_nontemporal_load((const u32x4*)(a.codes + base / 2) + le / 32);
+      sl.c[0] = cv[0]; sl.c[1] = cv[1]; sl.c[2] = cv[2]; sl.c[3] = cv[3];
+      if constexpr (kK15) {
+        const uint32_t* rp = (const uint32_t*)(a.raw + 7 * (base / 8)) + 7 * (le / 32);  // 28 bytes
+        const u32x4 v0 = __builtin_nontemporal_load((const u32x4a4*)rp);
+        const u32x3 v1 = __builtin_nontemporal_load((const u32x3a4*)(rp + 4));
+        sl.wr[0] = v0[0]; sl.wr[1] = v0[1]; sl.wr[2] = v0[2]; sl.wr[3] = v0[3];
+        sl.wr[4] = v1[0]; sl.wr[5] = v1[1]; sl.wr[6] = v1[2];
+      } else {
+        const u32x4* rp = (const u32x4*)(a.raw + base) + le / 16;
+        const u32x4 v0 = __builtin_nontemporal_load(rp), v1 = __builtin_nontemporal_load(rp + 1);
+        sl.wr[0] = v0[0]; sl.wr[1] = v0[1]; sl.wr[2] = v0[2]; sl.wr[3] = v0[3];
+        sl.wr[4] = v1[0]; sl.wr[5] = v1[1]; sl.wr[6] = v1[2]; sl.wr[7] = v1[3];
+      }
+    }
+    const u32x4* xp = (const u32x4*)(a.x + (uint64_t)jc * kStepCols) + xe / 8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 v = *(xp + u);
+      sl.xv[4 * u] = v[0]; sl.xv[4 * u + 1] = v[1]; sl.xv[4 * u + 2] = v[2]; sl.xv[4 * u + 3] = v[3];
+    }
+  };
+
+  // One step: rebuild (and patch) the lane's 32 weights of step q from `cur`,
+  // issue step q+1's loads into `nxt`, multiply.
+  auto step = [&](uint32_t q, Slot& cur, Slot& nxt, f32x4& acc) {
+    const bool ok = lane_ok(q);
+    // Every lane of the wave is inside its row unless the chunk is the
+    // row's partial last one or lies past it (a wave-uniform test); lanes
+    // outside contribute zero weights and zero x.
+    const bool full = (uint64_t)(q * S + (uint32_t)s + 1) * kStepCols <= a.cols;
+    const uint32_t cmask = (ok && row_ok) ? ~0u : 0u;  // codes of rows past the end count no escapes
+    uint32_t wv[16];
+    uint32_t gmask = 0, M = 0;
+    bool rebuilt = false;
+    if constexpr (!PLAIN) {
+      Lane4 l;
+#pragma unroll
+      for (int m = 0; m < kLaneGroups; ++m) l.codes[m] = cur.c[m] & cmask;
+      uint32_t marks[kLaneGroups];
+      escape_marks(l, marks);
+      const uint32_t cnt = count_marks(marks, &gmask);
+      if (esc) {
+        M = compress_marks(marks);
+        // escapes of this row in the lanes to the left (same wave), and the row's total
+        const uint32_t c0 = __shfl(cnt, r, kWave), c1 = __shfl(cnt, r + 16, kWave);
+        const uint32_t c2 = __shfl(cnt, r + 32, kWave), c3 = __shfl(cnt, r + 48, kWave);
+        const uint32_t ex = (h > 0 ? c0 : 0u) + (h > 1 ? c1 : 0u) + (h > 2 ? c2 : 0u);
+        if (h == 0) xcnt[q & 1][r][s] = c0 + c1 + c2 + c3;
+        block_lds_barrier();
+        uint32_t pre = 0, tot = 0;
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+          const uint32_t v = xcnt[q & 1][r][t];
+          pre += t < s ? v : 0u;
+          tot += v;
+        }
+        const uint64_t e_l = e_row + pre + ex;  // first record of this lane's weights
+        e_row += tot;
+        if (__ballot(cnt != 0)) {
+          // symbol window: the dwords holding records e_l .. e_l+31, its end
+          // clamped to the stream's padded end (its start may then fall in
+          // the preceding streams of the container, which is harmless)
+          const int64_t byte = (int64_t)(e_l * kSymBytes);
+          int64_t b = byte >> 2;
+          const int64_t bmax = (int64_t)a.sym_last - (kWinDwords - 1);
+          b = b < bmax ? b : bmax;
+          const uint32_t off = (uint32_t)(byte - 4 * b);
+          uint32_t wd[kWinDwords];
+          if (cnt != 0) {
+            const uint32_t* sp = (const uint32_t*)a.esc_sym + b;
+#pragma unroll
+            for (int u = 0; u + 4 <= kWinDwords; u += 4) {
+              const u32x4 v = *(const u32x4a4*)(sp + u);
+              wd[u] = v[0]; wd[u + 1] = v[1]; wd[u + 2] = v[2]; wd[u + 3] = v[3];
+            }
+            wd[kWinDwords - 1] = sp[kWinDwords - 1];
+          }
+          Lane4 lr;
+#pragma unroll
+          for (int m = 0; m < kLaneGroups; ++m) {
+            lr.codes[m] = l.codes[m];
+            if constexpr (kK15) {
+              // group m's 56 bits start at byte 7m of the lane's 28 bytes
+              const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
+              lr.raw[m][0] = __builtin_amdgcn_alignbit(cur.wr[d + 1], cur.wr[d], sh);
+              lr.raw[m][1] = __builtin_amdgcn_alignbit(d + 2 < 7 ? cur.wr[d + 2] : 0u, cur.wr[d + 1], sh);
+            } else {
+              lr.raw[m][0] = cur.wr[2 * m];
+              lr.raw[m][1] = cur.wr[2 * m + 1];
+            }
+          }
+          rebuild_lane<LAYOUT>(T2, a.dict, lr, wv);
+          uint32_t* st = stage[s];
+          uint32_t* wl = win[s] + lane * kWinDwords;
+          if (cnt != 0) {
+#pragma unroll
+            for (int u = 0; u < kWinDwords; ++u) wl[u] = wd[u];
+          }
+          stage_store(st, wv, gmask);
+          wave_lds_sync();
+          // the k-th record of the lane goes to its k-th marked weight
+          const uint8_t* wb = (const uint8_t*)wl;
+          for (uint32_t k0 = 0; __ballot(M != 0); k0 += 8) {
+            uint32_t sym[8], wi[8];
+            uint32_t mm = M;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              wi[u] = mm ? (uint32_t)__builtin_ctz(mm) : 32u;
+              mm &= mm - 1u;
+              const uint32_t p = off + (k0 + u) * kSymBytes;
+              sym[u] = 0;
+              if (wi[u] < 32u)
+                sym[u] = kK15 ? (uint32_t)(*(const uint16_t*)(wb + p) & 0x1FFu) : (uint32_t)wb[p];
+            }
+            M = mm;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              if (wi[u] < 32u) {
+                // weight i = 8 g + e of the lane: stage dword 4 (lane + 64 g) + e / 2
+                const uint32_t g = wi[u] >> 3, e = wi[u] & 7u;
+                const uint32_t dw = 4u * ((uint32_t)lane + (uint32_t)kWave * g) + (e >> 1);
+                if (kK15)
+                  atomicOr(st + dw, (sym[u] << 7) << (16u * (e & 1u)));
+                else
+                  ((uint8_t*)st)[4u * dw + 2u * (e & 1u) + 1u] = (uint8_t)sym[u];
+              }
+            }
+          }
+          wave_lds_sync();
+          stage_load(st, wv, gmask);
+          wave_lds_sync();
+          rebuilt = true;
+        }
+      }
+    }
+    load(q + 1, nxt);
+    if constexpr (!PLAIN) {
+      if (!rebuilt) {
+        Lane4 lr;
+#pragma unroll
+        for (int m = 0; m < kLaneGroups; ++m) {
+          lr.codes[m] = cur.c[m] & cmask;
+          if constexpr (kK15) {
+            const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
+            lr.raw[m][0] = __builtin_amdgcn_alignbit(cur.wr[d + 1], cur.wr[d], sh);
+            lr.raw[m][1] = __builtin_amdgcn_alignbit(d + 2 < 7 ? cur.wr[d + 2] : 0u, cur.wr[d + 1], sh);
+          } else {
+            lr.raw[m][0] = cur.wr[2 * m];
+            lr.raw[m][1] = cur.wr[2 * m + 1];
+          }
+        }
+        rebuild_lane<LAYOUT>(T2, a.dict, lr, wv);
+      }
+    }
+    // Operands of blocks past the row end are zeroed with masks rather than
+    // skipped, so the four products are issued on every path (no branch
+    // joins between matrix-core results).
+    const uint32_t* wsrc = PLAIN ? cur.wr : wv;
+    uint32_t wm[16], xm[16];
+#pragma unroll
+    for (int m = 0; m < kLaneGroups; ++m) {
+      const uint32_t km = PLAIN ? (block_ok(q, m) ? ~0u : 0u) : (ok ? ~0u : 0u);
+#pragma unroll
+      for (int k = 4 * m; k < 4 * m + 4; ++k) {
+        wm[k] = full ? wsrc[k] : wsrc[k] & km;
+        xm[k] = full ? cur.xv[k] : cur.xv[k] & km;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kLaneGroups; ++m) acc = mfma_bf16(wm + 4 * m, xm + 4 * m, acc);
+  };
+
+  // Two register sets alternate, each with its own accumulator (so no
+  // accumulator is copied inside the loop); an odd last step runs after the
+  // loop, so no path leaves the loop body half-way (which would make the
+  // compiler wait for the prefetch at the loop head).
+  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  Slot s0, s1;
+  load(0, s0);
+  for (uint32_t q = 0; q + 1 < n_steps; q += 2) {
+    step(q, s0, s1, acc0);
+    step(q + 1, s1, s0, acc1);
+  }
+  if (n_steps & 1u) step(n_steps - 1, s0, s1, acc0);
+  // Matrix-core results are read by vector instructions only after this
+  // many idle cycles (more than the longest product needs to retire).
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc0), "+v"(acc1));
+  const f32x4 acc = acc0 + acc1;
+
+  // Sum the S waves' partial tiles.  Lane l holds rows 4h .. 4h+3 of the
+  // block for batch column r.
+  float* red = (float*)stage[0];
+  block_lds_barrier();
+  *((f32x4*)(red + 4 * (s * kWave + lane))) = acc;
+  block_lds_barrier();
+  if (s == 0) {
+    f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < S; ++u) t += *((const f32x4*)(red + 4 * (u * kWave + lane)));
+    if (x_ok) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint64_t row = r0 + 4 * h + v;
+        if (row < a.rows) a.y[(uint64_t)r * a.rows + row] = t[v];
+      }
+    }
+  }
+}
+
+// ---- launchers -----------------------------------------------------------
+
+#ifndef WC_GEMM_SLICES
+#define WC_GEMM_SLICES 8
+#endif
+
+template <int LAYOUT, bool PLAIN>
+static void launch_mfma(const GemmArgs& a, hipStream_t s) {
+  const dim3 g((unsigned)((a.rows + kMRows - 1) / kMRows));
+  constexpr int S = WC_GEMM_SLICES;
+  hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, PLAIN, S>), g, dim3(kWave * S), 0, s, a);
+}
+
+static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint32_t batch,
+                          float* y) {
+  GemmArgs a = {};
+  a.x = x;
+  a.y = y;
+  a.rows = rows;
+  a.cols = cols;
+  a.batch = batch;
+  a.chunks = (uint32_t)((cols + kStepCols - 1) / kStepCols);
+  return a;
+}
+
+bool gemm_mfma_fits(uint64_t rows, uint64_t cols, uint32_t batch) {
+  return rows > 0 && cols > 0 && cols % kLaneCols == 0 && batch >= 1 && batch <= kMRows &&
+         cols / kStepCols < (1ull << 31);
+}
+
+hipError_t launch_decode_gemm_mfma(const wc_header& h, const uint8_t* container, uint64_t rows,
+                                   uint64_t cols, const uint16_t* x, uint32_t batch, float* y,
+                                   hipStream_t s) {
+  GemmArgs a = gemm_args(rows, cols, x, batch, y);
+  a.codes = container + h.off_codes;
+  a.raw = container + h.off_raw;
+  a.esc_pos = (const uint32_t*)(container + h.off_esc_pos);
+  a.esc_sym = container + h.off_esc_sym;
+  a.n_esc = h.n_esc;
+  // last dword of the symbol stream's 16-byte padded extent (the container's end)
+  a.sym_last = (h.total_bytes - h.off_esc_sym) / 4 - 1;
+  a.dict = dict_of(&h);
+  if (h.layout == WC_LAYOUT_K15)
+    launch_mfma<WC_LAYOUT_K15, false>(a, s);
+  else
+    launch_mfma<WC_LAYOUT_BYTESPLIT, false>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_mfma(const uint16_t* w, uint64_t rows, uint64_t cols,
+                                 const uint16_t* x, uint32_t batch, float* y, hipStream_t s) {
+  GemmArgs a = gemm_args(rows, cols, x, batch, y);
+  a.w = w;
+  launch_mfma<WC_LAYOUT_BYTESPLIT, true>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace wc

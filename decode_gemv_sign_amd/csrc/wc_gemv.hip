@@ -100,11 +100,14 @@ struct TileCursor {
 // is loaded just before tile q is processed.  The ring is unrolled, so every
 // slot index is static (no register copies, which would wait on the loads),
 // and loads past the end re-read the last tile (their data is unused), so the
-// loads in flight are the same on every path.
-template <int D, typename Slot, typename Load, typename Process>
-__device__ inline void run_ring(uint64_t nq, TileCursor start, uint64_t tpr, Load&& load,
-                                Process&& process) {
+// loads in flight are the same on every path.  process(cursor, slot, next)
+// may also fill fields of the next tile's slot that the load does not touch
+// (the next tile's first escape records).
+template <int D, typename Slot, typename Init, typename Load, typename Process>
+__device__ inline void run_ring(uint64_t nq, TileCursor start, uint64_t tpr, Init&& init,
+                                Load&& load, Process&& process) {
   Slot s[D];
+  init(s[0]);
   TileCursor lc = start, pc = start;
   uint64_t lq = 0;  // index of the tile lc points at
   auto load_next = [&](Slot& slot) {
@@ -121,7 +124,7 @@ __device__ inline void run_ring(uint64_t nq, TileCursor start, uint64_t tpr, Loa
     for (int i = 0; i < D; ++i) {
       load_next(s[(i + D - 1) % D]);
       if (q + i >= nq) return;
-      process(pc, s[i]);
+      process(pc, s[i], s[(i + 1) % D]);
       pc.next(tpr);
     }
   }
@@ -160,7 +163,7 @@ __device__ inline RowTile row_tile(uint64_t ct, uint64_t gpr) {
 template <int LAYOUT, int B>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   __shared__ uint32_t T2[256];
-  __shared__ uint32_t stage[kBlockThreads / kWave][kStageDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kBlockThreads / kWave][kStageDwords];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -179,6 +182,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     Lane4 l;
     uint32_t xv[kXpf ? 16 : 1];
     uint32_t act;
+    EscBatch eb;  // the tile's first escape records
   };
   auto load_tile = [&](const TileCursor& c, Slot& s) {
     const RowTile rt = row_tile(c.ct, gpr);
@@ -194,30 +198,30 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   };
 
   uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
-  EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 
-  auto process = [&](const TileCursor& c, const Slot& s) {
+  auto process = [&](const TileCursor& c, const Slot& s, Slot& sn) {
     const RowTile rt = row_tile(c.ct, gpr);
     uint32_t xv[kXpf ? 1 : 16];
     if (!kXpf && B == 1) load_x_lane(a.x + c.ct * kTile, rt.lg, xv);  // in flight during the rebuild
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(s.l, marks);
+    uint32_t gmask;
+    const uint32_t cnt = count_marks(marks, &gmask);
+    const uint32_t cnt_wave = __ballot(any) ? wave_sum_small(cnt) : 0u;
+    // the next tile's first records, in flight while this tile is rebuilt
+    sn.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave);
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, a.dict, s.l, w);
-    if (__ballot(any)) {
-      uint32_t gmask;
-      const uint32_t cnt = count_marks(marks, &gmask);
-      const uint32_t cnt_wave = wave_sum_small(cnt);
+    if (cnt_wave) {
       const uint64_t tile_start = c.r * a.cols + c.ct * kTile;
       const uint64_t left = a.cols - c.ct * kTile;
       patch_tile<LAYOUT>(stage[wib], w, gmask, a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
-                         cnt_wave, tile_start, left >= kTile ? kTile : (uint32_t)left, eb);
-      e += cnt_wave;
+                         cnt_wave, tile_start, left >= kTile ? kTile : (uint32_t)left, s.eb);
     }
-    eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+    e += cnt_wave;
     // groups outside the row contribute nothing
     if (rt.partial) {
 #pragma unroll
@@ -244,7 +248,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     }
   };
 
-  run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, load_tile, process);
+  auto init = [&](Slot& s0) {
+    s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+  };
+  run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, init, load_tile, process);
 }
 
 // The same wave/tile schedule as k_decode_gemv with W read as plain BF16
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16(GemvArgs a) {
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-  auto process = [&](const TileCursor& c, const Slot& s) {
+  auto process = [&](const TileCursor& c, const Slot& s, Slot&) {
     const RowTile rt = row_tile(c.ct, gpr);
     uint32_t xv[kXpf ? 1 : 16];
     if (!kXpf && B == 1) load_x_lane(a.x + c.ct * kTile, rt.lg, xv);
@@ -308,7 +315,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16(GemvArgs a) {
       for (int b = 0; b < B; ++b) acc[b] = 0.0f;
     }
   };
-  run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, load_tile, process);
+  run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, [](Slot&) {}, load_tile,
+                             process);
 }
 
 // ---- generic shapes (cols % 8 != 0): one weight per lane per step ---------
@@ -403,6 +411,13 @@ __global__ void k_fill_zero(float* y, uint64_t count) {
 
 // ---- launchers -----------------------------------------------------------
 
+// Batches from this size on take the matrix-core kernels of wc_gemm.hip
+// (when cols is a multiple of 32).
+#ifndef WC_MFMA_MIN_BATCH
+#define WC_MFMA_MIN_BATCH 8
+#endif
+constexpr uint32_t kMfmaMinBatch = WC_MFMA_MIN_BATCH;
+
 static dim3 row_grid(uint64_t rows) {
   const uint64_t wpb = kBlockThreads / kWave;
   return dim3((unsigned)((rows + wpb - 1) / wpb));
@@ -457,6 +472,8 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
                        count);
     return hipGetLastError();
   }
+  if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
+    return launch_decode_gemm_mfma(h, container, rows, cols, x, batch, y, s);
   GemvArgs a;
   a.codes = container + h.off_codes;
   a.raw = container + h.off_raw;
@@ -501,6 +518,8 @@ hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, con
                        count);
     return hipGetLastError();
   }
+  if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
+    return launch_gemm_bf16_mfma(w, rows, cols, x, batch, y, s);
   GemvArgs a = {};
   a.w = w;
   a.x = x;

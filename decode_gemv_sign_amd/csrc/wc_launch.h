@@ -27,6 +27,13 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
 hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint64_t rows,
                               uint64_t cols, const uint16_t* x, uint32_t batch, float* y,
                               hipStream_t s);
+// Matrix-core paths (wc_gemm.hip): cols a multiple of 32, batch 1..16.
+bool gemm_mfma_fits(uint64_t rows, uint64_t cols, uint32_t batch);
+hipError_t launch_decode_gemm_mfma(const wc_header& h, const uint8_t* container, uint64_t rows,
+                                   uint64_t cols, const uint16_t* x, uint32_t batch, float* y,
+                                   hipStream_t s);
+hipError_t launch_gemm_bf16_mfma(const uint16_t* w, uint64_t rows, uint64_t cols,
+                                 const uint16_t* x, uint32_t batch, float* y, hipStream_t s);
 hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, const uint16_t* x,
                             uint32_t batch, float* y, hipStream_t s);
 

@@ -73,10 +73,11 @@ __device__ inline GroupBase group_base(int layout, const uint8_t* codes, const u
   return b;
 }
 
-// Group G + lg.  A K15 group's 7 bytes are covered by 3 dwords; the second
-// and third are clamped to the raw stream's 16-byte padded extent (they pass
-// it only when the group is the stream's last and its remaining bytes are not
-// needed).
+// Group G + lg.  A K15 group's 7 bytes lie in the 3 dwords that start at
+// the dword holding its first byte, read with one 12-byte load; near the
+// stream's end that window is moved back so it ends inside the stream's
+// 16-byte padded extent (the group's bytes then start one or two dwords
+// later in it, and only those inside the stream are used).
 template <int LAYOUT>
 __device__ inline void load_group(const GroupBase& b, uint32_t lg, uint32_t& c, uint32_t r[2]) {
   c = __builtin_nontemporal_load(b.codes + lg);
@@ -86,13 +87,18 @@ __device__ inline void load_group(const GroupBase& b, uint32_t lg, uint32_t& c, 
     r[0] = v[0];
     r[1] = v[1];
   } else {
-    const uint32_t byte = b.skew + 7u * lg, d = byte >> 2, s = (byte & 3u) * 8u;
-    const uint32_t* rd = (const uint32_t*)b.raw;
-    const uint32_t d0 = __builtin_nontemporal_load(rd + d);
-    const uint32_t d1 = __builtin_nontemporal_load(rd + (d + 1 < b.raw_lim ? d + 1 : b.raw_lim));
-    const uint32_t d2 = __builtin_nontemporal_load(rd + (d + 2 < b.raw_lim ? d + 2 : b.raw_lim));
-    r[0] = __builtin_amdgcn_alignbit(d1, d0, s);
-    r[1] = __builtin_amdgcn_alignbit(d2, d1, s);
+    typedef uint32_t u32x3a4 __attribute__((ext_vector_type(3), aligned(4)));
+    const uint32_t byte = b.skew + 7u * lg, d = byte >> 2, sh = (byte & 3u) * 8u;
+    const int32_t dc = (int32_t)d + 2 <= (int32_t)b.raw_lim ? (int32_t)d : (int32_t)b.raw_lim - 2;
+    const u32x3a4 v = __builtin_nontemporal_load((const u32x3a4*)((const uint32_t*)b.raw + dc));
+    // the group's first byte sits in window dword d - dc (0, or 1..2 when the
+    // window was moved back; then only bytes inside the stream are used)
+    const uint32_t mv = (uint32_t)((int32_t)d - dc);
+    const uint32_t w0 = mv == 0 ? v[0] : (mv == 1 ? v[1] : v[2]);
+    const uint32_t w1 = mv == 0 ? v[1] : (mv == 1 ? v[2] : 0u);
+    const uint32_t w2 = mv == 0 ? v[2] : 0u;
+    r[0] = __builtin_amdgcn_alignbit(w1, w0, sh);
+    r[1] = __builtin_amdgcn_alignbit(w2, w1, sh);
   }
 }
 
