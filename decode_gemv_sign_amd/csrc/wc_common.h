@@ -103,13 +103,16 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Sum over the wave of a per-lane value below 64, by bit-plane ballots (scalar
-// popcounts, no cross-lane data movement).
-__device__ inline uint32_t wave_sum_small(uint32_t v) {
-  uint32_t s = 0;
-#pragma unroll
-  for (int b = 0; b < 6; ++b) s += (uint32_t)__popcll(__ballot((v >> b) & 1u)) << b;
-  return s;
+// Sum over the wave (DPP shifts within rows of 16 lanes, row totals
+// broadcast to the following rows, result read from the last lane).
+__device__ inline uint32_t wave_total(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
 // First index i in [0, count) with pos[i] >= t (count if none), found by the

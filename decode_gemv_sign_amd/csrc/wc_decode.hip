@@ -28,6 +28,7 @@ struct DecodeArgs {
   const uint8_t* esc_sym;
   uint16_t* out;
   uint64_t n, n_esc, esc_last, raw_last, n_tiles, tiles_per_wave;
+  uint64_t sym_last;  // last dword of the symbol stream's padded extent
   Dict dict;
 };
 
@@ -53,7 +54,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   // every path and no wait covers the prefetch.
   const uint64_t full_tiles = a.n / kTile;
   const uint64_t f1 = t1 < full_tiles ? t1 : full_tiles;  // end of this wave's full tiles
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile) : 0;
+  uint64_t e = 0;  // escape cursor, found once the first tile's loads are in flight
+  auto find_cursor = [&]() { e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile) : 0; };
 
   // Rebuild + escapes of tile t into out[16] (the lane's 4 groups).  The
   // tile's first escape records come in `eb` (loaded while the previous tile
@@ -63,15 +65,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
                      uint32_t out[16]) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
-    uint32_t gmask;
-    const uint32_t cnt = count_marks(marks, &gmask);
-    const uint32_t cnt_wave = __ballot(any) ? wave_sum_small(cnt) : 0u;
+    const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     eb_next = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave);
     rebuild_lane<LAYOUT>(T2, a.dict, l, out);
-    if (cnt_wave) {
+    if (cnt_wave > kDenseMin) {
+      patch_tile_windows<LAYOUT>(l, out, a.esc_sym, a.sym_last, e);
+    } else if (cnt_wave) {
       const uint64_t tile_start = t * kTile;
       const uint32_t tile_len = a.n - tile_start >= kTile ? kTile : (uint32_t)(a.n - tile_start);
-      patch_tile<LAYOUT>(stage[wib], out, gmask, a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
+      patch_tile<LAYOUT>(stage[wib], out, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
                          cnt_wave, tile_start, tile_len, eb);
     }
     e += cnt_wave;
@@ -101,8 +103,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     // Two slots alternate (static register sets); an odd last tile runs
     // after the loop, so no path leaves the loop body half-way.
     Slot sa, sb;
-    sa.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
     load_full(t0, sa.l);
+    find_cursor();
+    sa.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
     uint64_t t = t0;
     for (; t + 1 < f1; t += 2) {
       load_full(t + 1, sb.l);
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     }
     if (t < f1) process(t, sa, sb);
   }
+  if (t0 >= f1) find_cursor();  // a wave with only the partial last tile
   if (t1 > full_tiles) {
     // The tensor's partial last tile: groups past n are skipped, the group
     // that holds the last weight has its missing codes cleared (no phantom
@@ -166,6 +170,7 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
     a.esc_sym = container;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
+  a.sym_last = (h.total_bytes - h.off_esc_sym) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;
   // Short runs of tiles per wave: long enough to amortise the escape-cursor
   // search, short enough that dense escape regions spread over many waves.

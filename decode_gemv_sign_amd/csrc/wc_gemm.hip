@@ -73,12 +73,12 @@ __device__ inline void block_lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Bit 8m + e of the result = bit 4e of esc[m] (weight e of group m escapes).
+// Bit 8m + e of the result = bit 4e + 3 of esc[m] (weight e of group m escapes).
 __device__ inline uint32_t compress_marks(const uint32_t esc[kLaneGroups]) {
   uint32_t M = 0;
 #pragma unroll
   for (int m = 0; m < kLaneGroups; ++m) {
-    uint32_t t = esc[m];
+    uint32_t t = esc[m] >> 3;  // bit 4e
     t = (t | (t >> 3)) & 0x03030303u;
     t = (t | (t >> 6)) & 0x000F000Fu;
     t = (t | (t >> 12)) & 0xFFu;
@@ -117,16 +117,6 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   const uint32_t n_steps = (a.chunks + S - 1) / S;
   const bool esc = !PLAIN && a.n_esc != 0;
 
-  // Row cursors: first record at or after each row's start.
-  if (esc) {
-    for (int rr = s; rr < kMRows; rr += S) {
-      const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
-      const uint64_t e = wave_lower_bound(a.esc_pos, a.n_esc, t);
-      if (lane == 0) erow0[rr] = e;
-    }
-  }
-  __syncthreads();  // pair table and cursors (nothing is in flight yet)
-  uint64_t e_row = esc ? erow0[r] : 0;
 
   // Addresses: a wave-uniform base (the block's first row, the step's
   // chunk) plus a per-lane 32-bit offset (row r, columns 32h), so every load
@@ -200,6 +190,8 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
     }
   };
 
+  uint64_t e_row = 0;  // escape cursor of row r (set once the searches are done)
+
   // One step: rebuild (and patch) the lane's 32 weights of step q from `cur`,
   // issue step q+1's loads into `nxt`, multiply.
   auto step = [&](uint32_t q, Slot& cur, Slot& nxt, f32x4& acc) {
@@ -218,7 +210,8 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
       for (int m = 0; m < kLaneGroups; ++m) l.codes[m] = cur.c[m] & cmask;
       uint32_t marks[kLaneGroups];
       escape_marks(l, marks);
-      const uint32_t cnt = count_marks(marks, &gmask);
+      const uint32_t cnt = count_marks(marks);
+      gmask = group_mask(marks);
       if (esc) {
         M = compress_marks(marks);
         // escapes of this row in the lanes to the left (same wave), and the row's total
@@ -356,7 +349,17 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   // compiler wait for the prefetch at the loop head).
   f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
   Slot s0, s1;
-  load(0, s0);
+  load(0, s0);  // in flight during the cursor searches
+  // Row cursors: first record at or after each row's start.
+  if (esc) {
+    for (int rr = s; rr < kMRows; rr += S) {
+      const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
+      const uint64_t e = wave_lower_bound(a.esc_pos, a.n_esc, t);
+      if (lane == 0) erow0[rr] = e;
+    }
+  }
+  block_lds_barrier();  // pair table and cursors (the first loads stay in flight)
+  e_row = esc ? erow0[r] : 0;
   for (uint32_t q = 0; q + 1 < n_steps; q += 2) {
     step(q, s0, s1, acc0);
     step(q + 1, s1, s0, acc1);

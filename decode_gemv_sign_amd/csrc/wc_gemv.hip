@@ -41,6 +41,7 @@ struct GemvArgs {
   const uint16_t* x;
   float* y;
   uint64_t rows, cols, n_esc, esc_last, raw_last, rows_per_wave;
+  uint64_t sym_last;  // last dword of the symbol stream's padded extent
   uint32_t batch;
   Dict dict;
 };
@@ -97,7 +98,8 @@ struct TileCursor {
 };
 
 // Software pipeline over nq tiles with a ring of D register slots: tile q+D-1
-// is loaded just before tile q is processed.  The ring is unrolled, so every
+// is loaded just before tile q is processed.  init(slot 0) runs once the
+// first tiles' loads are issued (it may wait on memory of its own).  The ring is unrolled, so every
 // slot index is static (no register copies, which would wait on the loads),
 // and loads past the end re-read the last tile (their data is unused), so the
 // loads in flight are the same on every path.  process(cursor, slot, next)
@@ -107,7 +109,6 @@ template <int D, typename Slot, typename Init, typename Load, typename Process>
 __device__ inline void run_ring(uint64_t nq, TileCursor start, uint64_t tpr, Init&& init,
                                 Load&& load, Process&& process) {
   Slot s[D];
-  init(s[0]);
   TileCursor lc = start, pc = start;
   uint64_t lq = 0;  // index of the tile lc points at
   auto load_next = [&](Slot& slot) {
@@ -119,6 +120,7 @@ __device__ inline void run_ring(uint64_t nq, TileCursor start, uint64_t tpr, Ini
   };
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) load_next(s[i]);
+  init(s[0]);  // after the first loads are in flight
   for (uint64_t q = 0; q < nq; q += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     if (kXpf) load_x_lane(a.x + c.ct * kTile, rt.lg, s.xv);
   };
 
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
+  uint64_t e = 0;  // escape cursor: found in init, while the first tile loads
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
@@ -208,17 +210,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     if (!kXpf && B == 1) load_x_lane(a.x + c.ct * kTile, rt.lg, xv);  // in flight during the rebuild
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(s.l, marks);
-    uint32_t gmask;
-    const uint32_t cnt = count_marks(marks, &gmask);
-    const uint32_t cnt_wave = __ballot(any) ? wave_sum_small(cnt) : 0u;
+    const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     // the next tile's first records, in flight while this tile is rebuilt
     sn.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave);
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, a.dict, s.l, w);
-    if (cnt_wave) {
+    if (cnt_wave > kDenseMin) {
+      patch_tile_windows<LAYOUT>(s.l, w, a.esc_sym, a.sym_last, e);
+    } else if (cnt_wave) {
       const uint64_t tile_start = c.r * a.cols + c.ct * kTile;
       const uint64_t left = a.cols - c.ct * kTile;
-      patch_tile<LAYOUT>(stage[wib], w, gmask, a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
+      patch_tile<LAYOUT>(stage[wib], w, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
                          cnt_wave, tile_start, left >= kTile ? kTile : (uint32_t)left, s.eb);
     }
     e += cnt_wave;
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   };
 
   auto init = [&](Slot& s0) {
+    e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
     s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
   };
   run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, init, load_tile, process);
@@ -425,9 +428,12 @@ static dim3 row_grid(uint64_t rows) {
 
 // Rows per wave: enough tiles per wave (about 4) to amortise the escape
 // cursor search, while leaving many waves for the scheduler to balance.
+#ifndef WC_GEMV_MIN_TILES
+#define WC_GEMV_MIN_TILES 4
+#endif
 static uint64_t rows_per_wave(uint64_t cols) {
   const uint64_t tpr = (cols + kTile - 1) / kTile;
-  return tpr >= 4 ? 1 : (4 + tpr - 1) / tpr;
+  return tpr >= WC_GEMV_MIN_TILES ? 1 : (WC_GEMV_MIN_TILES + tpr - 1) / tpr;
 }
 
 static dim3 wave_grid(uint64_t rows, uint64_t rpw) {
@@ -492,6 +498,7 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
     a.esc_sym = container;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
+  a.sym_last = (h.total_bytes - h.off_esc_sym) / 4 - 1;
   a.batch = batch;
   a.dict = dict_of(&h);
   if (cols % kGroup == 0) {

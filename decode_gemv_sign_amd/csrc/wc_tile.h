@@ -185,29 +185,38 @@ __device__ inline void rebuild_lane(const uint32_t* __restrict__ T2, const Dict&
   }
 }
 
-// Code-15 (escape) marks of the lane's groups: bit 4i of esc[k] is set when
-// weight i of group k escapes.  Returns whether the lane has any.
+// Code-15 (escape) marks of the lane's groups: bit 4i + 3 of esc[k] is set
+// when weight i of group k escapes (the low three bits of a nibble carry into
+// its bit 3 only when they are all set, and bit 3 itself must be set).
+// Returns whether the lane has any.
+__device__ inline uint32_t nibble15(uint32_t c) {
+  return ((c & 0x77777777u) + 0x11111111u) & c & 0x88888888u;
+}
+
 __device__ inline bool escape_marks(const Lane4& l, uint32_t esc[kLaneGroups]) {
   uint32_t any = 0;
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) {
-    const uint32_t w = l.codes[k];
-    esc[k] = w & (w >> 1) & (w >> 2) & (w >> 3) & 0x11111111u;
+    esc[k] = nibble15(l.codes[k]);
     any |= esc[k];
   }
   return any != 0;
 }
 
-// Escape count of the lane, and in *gmask bit k set when group k holds one.
-__device__ inline uint32_t count_marks(const uint32_t esc[kLaneGroups], uint32_t* gmask) {
-  uint32_t n = 0, g = 0;
+// Escape count of the lane.
+__device__ inline uint32_t count_marks(const uint32_t esc[kLaneGroups]) {
+  uint32_t n = 0;
 #pragma unroll
-  for (int k = 0; k < kLaneGroups; ++k) {
-    n += __popc(esc[k]);
-    g |= (esc[k] ? 1u : 0u) << k;
-  }
-  *gmask = g;
+  for (int k = 0; k < kLaneGroups; ++k) n += (uint32_t)__popc(esc[k]);
   return n;
+}
+
+// Bit k set when group k holds an escape.
+__device__ inline uint32_t group_mask(const uint32_t esc[kLaneGroups]) {
+  uint32_t g = 0;
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) g |= (esc[k] ? 1u : 0u) << k;
+  return g;
 }
 
 // First escape records a tile may need, loaded with the tile's own data so a
@@ -219,7 +228,7 @@ struct EscBatch {
 };
 
 template <int LAYOUT>
-__device__ inline uint32_t load_sym(const uint8_t* __restrict__ esc_sym, uint64_t idx) {
+__device__ inline uint32_t load_sym(const uint8_t* __restrict__ esc_sym, uint32_t idx) {
   if (LAYOUT == WC_LAYOUT_BYTESPLIT) return esc_sym[idx];
   return ((const uint16_t*)esc_sym)[idx] & 0x1FFu;
 }
@@ -228,13 +237,14 @@ __device__ inline uint32_t load_sym(const uint8_t* __restrict__ esc_sym, uint64_
 // clamped to `last` (n_esc - 1, or 0 with the stream pointers aimed at the
 // container header when there are no escapes) and its result discarded, so
 // every path issues the same loads and no wait is widened by a branch.
+// Record indices and positions fit in 32 bits (n < 2^32).
 template <int LAYOUT>
 __device__ inline EscBatch load_esc(const uint32_t* __restrict__ esc_pos,
                                     const uint8_t* __restrict__ esc_sym, uint64_t n_esc,
                                     uint64_t last, uint64_t e) {
-  const uint64_t idx = e + (uint64_t)lane_id();
-  const bool ok = idx < n_esc;
-  const uint64_t ic = ok ? idx : last;
+  const uint32_t idx = (uint32_t)e + (uint32_t)lane_id();
+  const bool ok = e + (uint64_t)lane_id() < n_esc;
+  const uint32_t ic = ok ? idx : (uint32_t)last;
   const uint32_t p = esc_pos[ic];
   const uint32_t sy = load_sym<LAYOUT>(esc_sym, ic);
   EscBatch b;
@@ -247,9 +257,11 @@ __device__ inline EscBatch load_esc(const uint32_t* __restrict__ esc_pos,
 template <int LAYOUT>
 __device__ inline void apply_escape(uint32_t* __restrict__ stage, uint32_t pos, uint32_t sym,
                                     uint64_t tile_start, uint32_t tile_len) {
-  const uint64_t p = (uint64_t)pos - tile_start;  // wraps when before the tile
-  if (p < tile_len) {
-    const uint32_t v = (sym << (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)) << (16u * (uint32_t)(p & 1u));
+  // positions are below 2^32; a record past the stream (pos 0xFFFFFFFF) or
+  // before the tile wraps to a large offset
+  const uint32_t p = pos - (uint32_t)tile_start;
+  if (pos != 0xFFFFFFFFu && p < tile_len) {
+    const uint32_t v = (sym << (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)) << (16u * (p & 1u));
     atomicOr(stage + (p >> 1), v);
   }
 }
@@ -301,7 +313,7 @@ __device__ inline void patch_stage(uint32_t* __restrict__ stage,
       const uint32_t j = j0 + (uint32_t)(u * kWave + lane);
       const uint64_t idx = e0 + j;
       const bool ok = j < cnt && idx < n_esc;
-      const uint64_t ic = ok ? idx : last;
+      const uint32_t ic = ok ? (uint32_t)idx : (uint32_t)last;
       const uint32_t p = esc_pos[ic];
       sym[u] = load_sym<LAYOUT>(esc_sym, ic);
       pos[u] = ok ? p : 0xFFFFFFFFu;
@@ -325,6 +337,179 @@ __device__ inline void patch_tile(uint32_t* __restrict__ stage, uint32_t out[16]
   wave_lds_sync();
   stage_load(stage, out, gmask);
   wave_lds_sync();  // the stage is reused by this wave's next tile
+}
+
+// ---- dense escape tiles: per-group symbol windows -----------------------
+//
+// When a tile holds more escapes than one wave-wide batch of records, each
+// group reads its own records instead: the records are in position order, so
+// group g's records start at the tile's first record plus the escape count of
+// groups 0 .. g-1 (a prefix sum over the wave), and are consecutive.  The
+// group loads that run of symbols as one window and writes the k-th symbol
+// into its k-th code-15 weight, all in registers.
+
+// Inclusive prefix sum over the wave: shifts within rows of 16 lanes, then
+// the row totals broadcast to the following rows (DPP).
+__device__ inline uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Bit i set: weight i of the group has code 15.
+__device__ inline uint32_t group_esc_bits(uint32_t c) {
+  uint32_t t = nibble15(c) >> 3;  // bit 4i
+  t = (t | (t >> 3)) & 0x03030303u;
+  t = (t | (t >> 6)) & 0x000F000Fu;
+  return (t | (t >> 12)) & 0xFFu;
+}
+
+// Ranks of a group's code-15 weights: byte j of rl (rh) = number of code-15
+// weights before weight j (4 + j); byte j of ml (mh) = 0xFF when weight j
+// (4 + j) has code 15, else 0.
+__device__ inline void escape_ranks(uint32_t m, uint32_t& rl, uint32_t& rh, uint32_t& ml,
+                                    uint32_t& mh) {
+  const uint32_t sl = ((m & 15u) * 0x00204081u) & 0x01010101u;  // byte j = bit j
+  const uint32_t sh = (((m >> 4) & 15u) * 0x00204081u) & 0x01010101u;
+  const uint32_t il = sl * 0x01010101u;  // inclusive prefix per byte (at most 4: no carries)
+  const uint32_t ih = sh * 0x01010101u + (il >> 24) * 0x01010101u;
+  rl = il - sl;
+  rh = ih - sh;
+  ml = sl * 0xFFu;
+  mh = sh * 0xFFu;
+}
+
+#ifndef WC_WIN_PASS
+#define WC_WIN_PASS 4
+#endif
+constexpr int kWinPass = WC_WIN_PASS;  // groups whose windows are in flight together
+#ifndef WC_DENSE_MIN
+#define WC_DENSE_MIN 64
+#endif
+constexpr uint32_t kDenseMin = WC_DENSE_MIN;  // tiles with more escapes take the window path
+
+template <int LAYOUT>
+struct WinDwords {
+  static constexpr int value = LAYOUT == WC_LAYOUT_K15 ? 5 : 3;  // 8 symbols + alignment
+};
+
+// Write group k's symbols (window w, byte offset off of the first symbol)
+// into the zero placeholders of its rebuilt weights out[0..3].
+template <int LAYOUT>
+__device__ inline void expand_window(uint32_t m, const uint32_t (&w)[WinDwords<LAYOUT>::value],
+                                     uint32_t off, uint32_t out[4]) {
+  constexpr int W = WinDwords<LAYOUT>::value;
+  // shift the window so that the first symbol starts at byte 0
+  uint32_t d[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) d[i] = w[i];
+  const uint32_t s = off >> 2, sh = (off & 3u) * 8u;
+  if (__ballot(s != 0)) {  // only windows moved back from the stream's end
+#pragma unroll
+    for (int t = 0; t < W - 1; ++t) {
+      const bool mv = s > (uint32_t)t;
+#pragma unroll
+      for (int i = 0; i < W; ++i) d[i] = mv ? (i + 1 < W ? d[i + 1] : 0u) : d[i];
+    }
+  }
+  uint32_t rl, rh, ml, mh;
+  escape_ranks(m, rl, rh, ml, mh);
+  if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
+    const uint32_t a0 = __builtin_amdgcn_alignbit(d[1], d[0], sh);
+    const uint32_t a1 = __builtin_amdgcn_alignbit(d[2], d[1], sh);
+    // byte j of hl (hh) = symbol of weight j (4 + j), 0 when it is not an escape
+    const uint32_t hl = __builtin_amdgcn_perm(a1, a0, (rl & ml) | (0x0C0C0C0Cu & ~ml));
+    const uint32_t hh = __builtin_amdgcn_perm(a1, a0, (rh & mh) | (0x0C0C0C0Cu & ~mh));
+    out[0] |= __builtin_amdgcn_perm(0u, hl, 0x010C000Cu);
+    out[1] |= __builtin_amdgcn_perm(0u, hl, 0x030C020Cu);
+    out[2] |= __builtin_amdgcn_perm(0u, hh, 0x010C000Cu);
+    out[3] |= __builtin_amdgcn_perm(0u, hh, 0x030C020Cu);
+  } else {
+    uint32_t a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // weights 2j, 2j+1: their ranks and marks, each byte doubled
+      const uint32_t R = j < 2 ? rl : rh, Mk = j < 2 ? ml : mh;
+      const uint32_t ps = (j & 1) ? 0x03030202u : 0x01010000u;
+      const uint32_t rb = __builtin_amdgcn_perm(0u, R, ps);
+      const uint32_t mb = __builtin_amdgcn_perm(0u, Mk, ps);
+      // byte selectors of symbol halfword (rank mod 4) in a 2-dword half
+      const uint32_t hs = ((rb & 0x03030303u) << 1) | 0x01000100u;
+      const uint32_t sel = (hs & mb) | (0x0C0C0C0Cu & ~mb);
+      const uint32_t lo = __builtin_amdgcn_perm(a[1], a[0], sel);  // symbols 0..3
+      const uint32_t hi = __builtin_amdgcn_perm(a[3], a[2], sel);  // symbols 4..7
+      const uint32_t hm = ((rb >> 2) & 0x01010101u) * 0xFFu;        // rank >= 4
+      const uint32_t v = (hi & hm) | (lo & ~hm);
+      out[j] |= (v & 0x01FF01FFu) << 7;
+    }
+  }
+}
+
+// Patch a tile from per-group windows.  `e` = index of the tile's first
+// record; `sym_last` = last dword of the symbol stream's 16-byte padded
+// extent (windows are moved back so they end there; their start may then
+// fall in the preceding streams of the container).
+template <int LAYOUT>
+__device__ inline void patch_tile_windows(const Lane4& l, uint32_t out[16],
+                                          const uint8_t* __restrict__ esc_sym, uint64_t sym_last,
+                                          uint64_t e) {
+  constexpr int W = WinDwords<LAYOUT>::value;
+  constexpr uint64_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  uint32_t m[kLaneGroups], c[kLaneGroups];
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) {
+    m[k] = group_esc_bits(l.codes[k]);
+    c[k] = (uint32_t)__popc(m[k]);
+  }
+  // first record of each group relative to the tile's (groups L + 64k in
+  // tile order: all of k = 0, then k = 1, ...); counts packed two per dword
+  const uint32_t p01 = c[0] | (c[1] << 16), p23 = c[2] | (c[3] << 16);
+  const uint32_t i01 = wave_incl_scan_dpp(p01), i23 = wave_incl_scan_dpp(p23);
+  const uint32_t t01 = (uint32_t)__builtin_amdgcn_readlane((int)i01, kWave - 1);
+  const uint32_t t23 = (uint32_t)__builtin_amdgcn_readlane((int)i23, kWave - 1);
+  const uint32_t x01 = i01 - p01, x23 = i23 - p23;
+  uint32_t first[kLaneGroups];
+  first[0] = x01 & 0xFFFFu;
+  first[1] = (t01 & 0xFFFFu) + (x01 >> 16);
+  first[2] = (t01 & 0xFFFFu) + (t01 >> 16) + (x23 & 0xFFFFu);
+  first[3] = (t01 & 0xFFFFu) + (t01 >> 16) + (t23 & 0xFFFFu) + (x23 >> 16);
+  // windows are loaded and applied kWinPass groups at a time (fewer live
+  // registers for smaller passes)
+#pragma unroll
+  for (int k0 = 0; k0 < kLaneGroups; k0 += kWinPass) {
+    uint32_t w[kWinPass][W], off[kWinPass];
+#pragma unroll
+    for (int u = 0; u < kWinPass; ++u) {
+      const int k = k0 + u;
+      const uint64_t byte = (e + first[k]) * kSymBytes;
+      int64_t b = (int64_t)(byte >> 2);
+      const int64_t bmax = (int64_t)sym_last - (W - 1);
+      b = b < bmax ? b : bmax;
+      off[u] = (uint32_t)(byte - 4 * (uint64_t)b);
+      if (c[k]) {
+        const uint32_t* sp = (const uint32_t*)esc_sym + b;
+        if constexpr (W == 3) {
+          typedef uint32_t u32x3a4 __attribute__((ext_vector_type(3), aligned(4)));
+          const u32x3a4 v = *(const u32x3a4*)sp;
+          w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2];
+        } else {
+          typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+          const u32x4a4 v = *(const u32x4a4*)sp;
+          w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
+          w[u][W - 1] = sp[W - 1];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kWinPass; ++u)
+      if (c[k0 + u]) expand_window<LAYOUT>(m[k0 + u], w[u], off[u], out + 4 * (k0 + u));
+  }
 }
 
 }  // namespace wc
