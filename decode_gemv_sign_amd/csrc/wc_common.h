@@ -139,6 +139,33 @@ __device__ inline uint64_t wave_lower_bound(const uint32_t* __restrict__ pos, ui
   return lo + (uint64_t)__popcll(__ballot(below));
 }
 
+// ---- global -> LDS loads and explicit waits --------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void glb_void_t;
+
+// 16 bytes per lane from `src` (per lane) into LDS at dst + 16 * lane (dst
+// wave-uniform).  Completion is counted by vmcnt; the compiler does not
+// track the LDS write, so readers wait explicitly (wait_vm).
+__device__ inline void lds_dma16(const void* src, uint32_t* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+
+// 4 bytes per lane into LDS at dst + 4 * lane.
+__device__ inline void lds_dma4(const void* src, uint32_t* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (other counters left alone), N <= 63.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// s_waitcnt lgkmcnt(0).
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // ---- host-side checks ----------------------------------------------------
 
 // WC_OK when *h is exactly the header the format defines for its fields.

@@ -11,6 +11,8 @@
 // advanced by each tile's code-15 count.  Tiles without escapes (a wave-wide
 // ballot) store straight from registers with 16-byte non-temporal stores;
 // tiles with escapes are patched in LDS first (wc_tile.h).
+#include <type_traits>
+
 #include "wc_launch.h"
 #include "wc_tile.h"
 
@@ -20,6 +22,13 @@ namespace wc {
 #define WC_DECODE_TILES_PER_WAVE 4
 #endif
 constexpr uint64_t kDecodeTilesPerWave = WC_DECODE_TILES_PER_WAVE;
+#ifndef WC_DECODE_DMA
+#define WC_DECODE_DMA 1
+#endif
+#ifndef WC_DECODE_RING
+#define WC_DECODE_RING 2
+#endif
+constexpr int kDecodeRing = WC_DECODE_RING;  // LDS tile buffers per wave
 
 struct DecodeArgs {
   const uint8_t* codes;
@@ -35,7 +44,16 @@ struct DecodeArgs {
 template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   __shared__ uint32_t T2[256];
+#if WC_DECODE_DMA
+  // per wave: a ring of tile buffers filled by global->LDS loads
+  // 4 KB per slot: codes 1 KB + raw 2 KB, and the whole slot doubles as the
+  // escape stage of the tile just read from it
+  __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][kStageDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][kStageDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring2[kDecodeRing > 2 ? kBlockThreads / kWave : 1][kStageDwords];
+#else
   __shared__ __attribute__((aligned(16))) uint32_t stage[kBlockThreads / kWave][kStageDwords];
+#endif
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -61,24 +79,181 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   // tile's first escape records come in `eb` (loaded while the previous tile
   // was processed); the next tile's are issued into `eb_next` as soon as
   // this tile's escape count is known, so they arrive during its rebuild.
-  auto rebuild = [&](uint64_t t, const Lane4& l, const EscBatch& eb, EscBatch& eb_next,
-                     uint32_t out[16]) {
+  // `async`: eb was loaded by load_esc_async (flag ok_cur) and eb_next is
+  // loaded the same way (flag ok_next); the batch is awaited explicitly.
+  // `issue_next(e_next)` starts the next tile's first-records load as soon
+  // as this tile's escape count is known (it arrives during the rebuild).
+  auto rebuild = [&](uint64_t t, const Lane4& l, const EscBatch& eb, auto&& issue_next,
+                     uint32_t out[16], uint32_t* stg) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
-    eb_next = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave);
+    issue_next(e + cnt_wave);
     rebuild_lane<LAYOUT>(T2, a.dict, l, out);
     if (cnt_wave > kDenseMin) {
       patch_tile_windows<LAYOUT>(l, out, a.esc_sym, a.sym_last, e);
     } else if (cnt_wave) {
       const uint64_t tile_start = t * kTile;
       const uint32_t tile_len = a.n - tile_start >= kTile ? kTile : (uint32_t)(a.n - tile_start);
-      patch_tile<LAYOUT>(stage[wib], out, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
+      patch_tile<LAYOUT>(stg, out, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
                          cnt_wave, tile_start, tile_len, eb);
     }
     e += cnt_wave;
   };
 
+#if WC_DECODE_DMA
+  if (t0 < f1) {
+    // Full tiles stream through a ring of kDecodeRing LDS buffers: each is
+    // filled by three 16-byte-per-lane global->LDS loads (codes 1 KB, raw
+    // 2 KB or 1.75 KB), kDecodeRing - 1 tiles ahead, and read back in the
+    // group mapping.  The loads need no registers, so the ring depth does not
+    // cost occupancy.  Their completion is awaited with explicit counts of
+    // the vector-memory instructions issued after them (per tile: 3 ring
+    // loads, 2 escape-record loads, 4 stores; extra loads on escape-heavy
+    // paths only make the wait longer).
+    constexpr int R = kDecodeRing;
+    constexpr uint32_t kRawTile = LAYOUT == WC_LAYOUT_K15 ? 7 * kTile / 8 : kTile;
+    auto dma_tile = [&](uint64_t t, uint32_t* buf) {
+      const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
+      const uint8_t* cp = a.codes + tc * (kTile / 2);
+      const uint8_t* rp = a.raw + tc * kRawTile;
+      const uint32_t o2 = 1024u + 16u * (uint32_t)lane;
+      lds_dma16(cp + 16 * lane, buf);
+      lds_dma16(rp + 16 * lane, buf + 256);
+      lds_dma16(rp + (o2 + 16u <= kRawTile ? o2 : kRawTile - 16u), buf + 512);
+    };
+    // Tile reads in the group mapping, as hand-written LDS loads (outputs
+    // early-clobber: the block reads its address registers after writing
+    // results; the
+    // explicit vmcnt waits above order them after the ring loads; the
+    // compiler, which cannot tell the ring slots apart, would wait for
+    // every ring load in flight).
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    auto read_tile = [&](const uint32_t* buf, Lane4& l) {
+      const uint32_t cb = lds_addr(buf) + 4u * (uint32_t)lane;  // code of group L at dword L
+      u32x2 c01, c23;
+      if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
+        const uint32_t rb = lds_addr(buf) + 1024u + 8u * (uint32_t)lane;  // raw of group L
+        u32x4 r01, r23;
+        asm volatile(
+            "ds_read2st64_b32 %0, %4 offset1:1\n\t"
+            "ds_read2st64_b32 %1, %4 offset0:2 offset1:3\n\t"
+            "ds_read2st64_b64 %2, %5 offset1:1\n\t"
+            "ds_read2st64_b64 %3, %5 offset0:2 offset1:3\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(c01), "=&v"(c23), "=&v"(r01), "=&v"(r23)
+            : "v"(cb), "v"(rb)
+            : "memory");
+        l.raw[0][0] = r01[0]; l.raw[0][1] = r01[1]; l.raw[1][0] = r01[2]; l.raw[1][1] = r01[3];
+        l.raw[2][0] = r23[0]; l.raw[2][1] = r23[1]; l.raw[3][0] = r23[2]; l.raw[3][1] = r23[3];
+      } else {
+        // group L + 64k starts at raw byte 7L + 448k: dwords d0 + 112k + {0,1,2}
+        const uint32_t byte = 7u * (uint32_t)lane, sh = (byte & 3u) * 8u;
+        const uint32_t rb = lds_addr(buf) + 1024u + 4u * (byte >> 2);
+        uint32_t w[12];
+        asm volatile(
+            "ds_read2st64_b32 %0, %14 offset1:1\n\t"
+            "ds_read2st64_b32 %1, %14 offset0:2 offset1:3\n\t"
+            "ds_read_b32 %2, %15\n\t"
+            "ds_read_b32 %3, %15 offset:4\n\t"
+            "ds_read_b32 %4, %15 offset:8\n\t"
+            "ds_read_b32 %5, %15 offset:448\n\t"
+            "ds_read_b32 %6, %15 offset:452\n\t"
+            "ds_read_b32 %7, %15 offset:456\n\t"
+            "ds_read_b32 %8, %15 offset:896\n\t"
+            "ds_read_b32 %9, %15 offset:900\n\t"
+            "ds_read_b32 %10, %15 offset:904\n\t"
+            "ds_read_b32 %11, %15 offset:1344\n\t"
+            "ds_read_b32 %12, %15 offset:1348\n\t"
+            "ds_read_b32 %13, %15 offset:1352\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(c01), "=&v"(c23), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]),
+              "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7]), "=&v"(w[8]), "=&v"(w[9]),
+              "=&v"(w[10]), "=&v"(w[11])
+            : "v"(cb), "v"(rb)
+            : "memory");
+#pragma unroll
+        for (int k = 0; k < kLaneGroups; ++k) {
+          l.raw[k][0] = __builtin_amdgcn_alignbit(w[3 * k + 1], w[3 * k], sh);
+          l.raw[k][1] = __builtin_amdgcn_alignbit(w[3 * k + 2], w[3 * k + 1], sh);
+        }
+      }
+      l.codes[0] = c01[0]; l.codes[1] = c01[1]; l.codes[2] = c23[0]; l.codes[3] = c23[1];
+    };
+    // The first escape records of a tile (lane j: record e + j) also come
+    // through the ring: its position and the dword holding its symbol land
+    // in the last kilobyte of the tile's slot (dwords 768.. and 832..), and
+    // are read back (before the slot becomes the tile's stage) after the same
+    // explicit wait as the tile.
+    constexpr uint32_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+    auto dma_eb = [&](uint64_t e0, uint32_t* buf) {
+      const uint64_t idx = e0 + (uint64_t)lane;
+      const uint32_t ic = idx < a.n_esc ? (uint32_t)idx : (uint32_t)a.esc_last;
+      lds_dma4(a.esc_pos + ic, buf + 768);
+      lds_dma4(a.esc_sym + ((ic * kSymBytes) & ~3u), buf + 832);
+    };
+    auto read_eb = [&](const uint32_t* buf, uint64_t e0) {
+      const uint32_t ad = lds_addr(buf) + 4u * (uint32_t)lane;
+      uint32_t p, w;
+      asm volatile("ds_read_b32 %0, %2 offset:3072\n\tds_read_b32 %1, %2 offset:3328\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(p), "=&v"(w) : "v"(ad) : "memory");
+      const uint64_t idx = e0 + (uint64_t)lane;
+      const uint32_t ic = idx < a.n_esc ? (uint32_t)idx : (uint32_t)a.esc_last;
+      EscBatch b;
+      b.pos = idx < a.n_esc ? p : 0xFFFFFFFFu;
+      b.sym = (w >> (8u * ((ic * kSymBytes) & 3u))) & (LAYOUT == WC_LAYOUT_K15 ? 0x1FFu : 0xFFu);
+      return b;
+    };
+    uint32_t* const s0 = ring0[wib];
+    uint32_t* const s1 = ring1[wib];
+    uint32_t* const s2 = ring2[kDecodeRing > 2 ? wib : 0];
+    auto slot_buf = [&](auto slc) -> uint32_t* {
+      constexpr int sl = decltype(slc)::value % R;
+      return sl == 0 ? s0 : (sl == 1 ? s1 : s2);
+    };
+    find_cursor();
+    dma_eb(e, s0);
+    dma_tile(t0, s0);
+    if (R > 2) dma_tile(t0 + 1, s1);
+    uint64_t t = t0;
+    // Per tile, in order: 3 ring loads (tile t + R - 1), then during the
+    // rebuild 2 record loads (tile t + 1, into its slot), then 4 stores.
+    auto step = [&](auto slc, uint32_t j) {
+      constexpr int sl = decltype(slc)::value;
+      wait_lgkm0();  // tile t-1's LDS reads and stage writes are done before it is refilled
+      dma_tile(t + R - 1, slot_buf(std::integral_constant<int, sl + R - 1>{}));
+      // wait for tile t's ring loads and its record loads.  The record
+      // loads are the younger ones (issued during tile t-1, after tile t's
+      // ring loads) and 7 instructions follow them: tile t-1's 4 stores and
+      // the 3 ring loads just issued.  The first tile's records come before
+      // its ring loads, which are followed by the other R - 1 tiles' loads.
+      if (j == 0) wait_vm<3 * (R - 1)>();
+      else wait_vm<7>();
+      Lane4 l;
+      uint32_t* buf = slot_buf(slc);
+      read_tile(buf, l);
+      const EscBatch eb = read_eb(buf, e);
+      uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
+      uint32_t out[16];
+      rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf);
+      u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
+#pragma unroll
+      for (int k = 0; k < kLaneGroups; ++k)
+        __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
+                                    dst + kWave * k);
+      ++t;
+    };
+    while (t + R <= f1) {
+      step(std::integral_constant<int, 0>{}, (uint32_t)(t - t0));
+      step(std::integral_constant<int, 1>{}, (uint32_t)(t - t0));
+      if constexpr (R > 2) step(std::integral_constant<int, 2>{}, (uint32_t)(t - t0));
+    }
+    if (t < f1) step(std::integral_constant<int, 0>{}, (uint32_t)(t - t0));
+    if (t < f1) step(std::integral_constant<int, 1>{}, (uint32_t)(t - t0));
+    wait_vm<0>();  // the ring's last (unused) loads land before the stage is reused
+    wait_lgkm0();
+  }
+#else
   if (t0 < f1) {
     auto load_full = [&](uint64_t t, Lane4& l) {
       const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
@@ -93,7 +268,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     };
     auto process = [&](uint64_t t, const Slot& cur, Slot& nxt) {
       uint32_t out[16];
-      rebuild(t, cur.l, cur.eb, nxt.eb, out);
+      rebuild(t, cur.l, cur.eb, [&](uint64_t en) {
+        nxt.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, en);
+      }, out, stage[wib]);
       u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
 #pragma unroll
       for (int k = 0; k < kLaneGroups; ++k)
@@ -115,6 +292,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     }
     if (t < f1) process(t, sa, sb);
   }
+#endif
   if (t0 >= f1) find_cursor();  // a wave with only the partial last tile
   if (t1 > full_tiles) {
     // The tensor's partial last tile: groups past n are skipped, the group
@@ -137,8 +315,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     }
     uint32_t out[16];
     const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
-    EscBatch unused;
-    rebuild(full_tiles, l, eb, unused, out);
+#if WC_DECODE_DMA
+    rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib]);
+#else
+    rebuild(full_tiles, l, eb, [](uint64_t) {}, out, stage[wib]);
+#endif
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
       const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;

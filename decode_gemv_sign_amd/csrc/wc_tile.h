@@ -253,6 +253,16 @@ __device__ inline EscBatch load_esc(const uint32_t* __restrict__ esc_pos,
   return b;
 }
 
+// The stage is accessed with hand-written LDS instructions: the compiler
+// would otherwise wait for every outstanding vector-memory operation before
+// the first LDS store (it cannot tell the stage apart from the global->LDS
+// ring buffers of the decode kernel).  A wave's LDS instructions execute in
+// order, so stores are visible to the wave's later loads; loads wait for
+// their own data (lgkmcnt) before returning.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // OR one escape symbol into its zero placeholder in the wave's LDS stage.
 template <int LAYOUT>
 __device__ inline void apply_escape(uint32_t* __restrict__ stage, uint32_t pos, uint32_t sym,
@@ -262,7 +272,7 @@ __device__ inline void apply_escape(uint32_t* __restrict__ stage, uint32_t pos, 
   const uint32_t p = pos - (uint32_t)tile_start;
   if (pos != 0xFFFFFFFFu && p < tile_len) {
     const uint32_t v = (sym << (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)) << (16u * (p & 1u));
-    atomicOr(stage + (p >> 1), v);
+    asm volatile("ds_or_b32 %0, %1" : : "v"(lds_addr(stage + (p >> 1))), "v"(v) : "memory");
   }
 }
 
@@ -273,19 +283,24 @@ __device__ inline void apply_escape(uint32_t* __restrict__ stage, uint32_t pos, 
 // records patch only those, so the rest stay in registers.
 __device__ inline void stage_store(uint32_t* __restrict__ stage, const uint32_t out[16],
                                    uint32_t gmask) {
-  u32x4* st = (u32x4*)stage + lane_id();
+  const uint32_t base = lds_addr(stage) + 16u * (uint32_t)lane_id();
 #pragma unroll
-  for (int k = 0; k < kLaneGroups; ++k)
-    if ((gmask >> k) & 1u) st[kWave * k] = u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]};
+  for (int k = 0; k < kLaneGroups; ++k) {
+    if ((gmask >> k) & 1u) {
+      const u32x4 v = {out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]};
+      asm volatile("ds_write_b128 %0, %1" : : "v"(base + 1024u * k), "v"(v) : "memory");
+    }
+  }
 }
 
 __device__ inline void stage_load(const uint32_t* __restrict__ stage, uint32_t out[16],
                                   uint32_t gmask) {
-  const u32x4* st = (const u32x4*)stage + lane_id();
+  const uint32_t base = lds_addr(stage) + 16u * (uint32_t)lane_id();
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) {
     if ((gmask >> k) & 1u) {
-      const u32x4 v = st[kWave * k];
+      u32x4 v;
+      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(base + 1024u * k) : "memory");
       out[4 * k] = v[0]; out[4 * k + 1] = v[1]; out[4 * k + 2] = v[2]; out[4 * k + 3] = v[3];
     }
   }
