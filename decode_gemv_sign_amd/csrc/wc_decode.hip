@@ -103,106 +103,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
 
 #if WC_DECODE_DMA
   if (t0 < f1) {
-    // Full tiles stream through a ring of kDecodeRing LDS buffers: each is
-    // filled by three 16-byte-per-lane global->LDS loads (codes 1 KB, raw
-    // 2 KB or 1.75 KB), kDecodeRing - 1 tiles ahead, and read back in the
-    // group mapping.  The loads need no registers, so the ring depth does not
-    // cost occupancy.  Their completion is awaited with explicit counts of
-    // the vector-memory instructions issued after them (per tile: 3 ring
-    // loads, 2 escape-record loads, 4 stores; extra loads on escape-heavy
-    // paths only make the wait longer).
+    // Full tiles stream through a ring of kDecodeRing LDS slots (wc_tile.h
+    // ring_*), kDecodeRing - 1 tiles ahead.  The loads need no registers, so
+    // the ring depth does not cost occupancy.  Their completion is awaited
+    // with explicit counts of the vector-memory instructions issued after
+    // them (per tile: 3 ring loads, 2 escape-record loads, 4 stores; extra
+    // loads on escape-heavy paths only make the wait longer).
     constexpr int R = kDecodeRing;
-    constexpr uint32_t kRawTile = LAYOUT == WC_LAYOUT_K15 ? 7 * kTile / 8 : kTile;
     auto dma_tile = [&](uint64_t t, uint32_t* buf) {
       const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
-      const uint8_t* cp = a.codes + tc * (kTile / 2);
-      const uint8_t* rp = a.raw + tc * kRawTile;
-      const uint32_t o2 = 1024u + 16u * (uint32_t)lane;
-      lds_dma16(cp + 16 * lane, buf);
-      lds_dma16(rp + 16 * lane, buf + 256);
-      lds_dma16(rp + (o2 + 16u <= kRawTile ? o2 : kRawTile - 16u), buf + 512);
+      ring_load_tile<LAYOUT>(a.codes, a.raw, tc * (kTile / kGroup), buf);
     };
-    // Tile reads in the group mapping, as hand-written LDS loads (outputs
-    // early-clobber: the block reads its address registers after writing
-    // results; the
-    // explicit vmcnt waits above order them after the ring loads; the
-    // compiler, which cannot tell the ring slots apart, would wait for
-    // every ring load in flight).
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    auto read_tile = [&](const uint32_t* buf, Lane4& l) {
-      const uint32_t cb = lds_addr(buf) + 4u * (uint32_t)lane;  // code of group L at dword L
-      u32x2 c01, c23;
-      if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
-        const uint32_t rb = lds_addr(buf) + 1024u + 8u * (uint32_t)lane;  // raw of group L
-        u32x4 r01, r23;
-        asm volatile(
-            "ds_read2st64_b32 %0, %4 offset1:1\n\t"
-            "ds_read2st64_b32 %1, %4 offset0:2 offset1:3\n\t"
-            "ds_read2st64_b64 %2, %5 offset1:1\n\t"
-            "ds_read2st64_b64 %3, %5 offset0:2 offset1:3\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(c01), "=&v"(c23), "=&v"(r01), "=&v"(r23)
-            : "v"(cb), "v"(rb)
-            : "memory");
-        l.raw[0][0] = r01[0]; l.raw[0][1] = r01[1]; l.raw[1][0] = r01[2]; l.raw[1][1] = r01[3];
-        l.raw[2][0] = r23[0]; l.raw[2][1] = r23[1]; l.raw[3][0] = r23[2]; l.raw[3][1] = r23[3];
-      } else {
-        // group L + 64k starts at raw byte 7L + 448k: dwords d0 + 112k + {0,1,2}
-        const uint32_t byte = 7u * (uint32_t)lane, sh = (byte & 3u) * 8u;
-        const uint32_t rb = lds_addr(buf) + 1024u + 4u * (byte >> 2);
-        uint32_t w[12];
-        asm volatile(
-            "ds_read2st64_b32 %0, %14 offset1:1\n\t"
-            "ds_read2st64_b32 %1, %14 offset0:2 offset1:3\n\t"
-            "ds_read_b32 %2, %15\n\t"
-            "ds_read_b32 %3, %15 offset:4\n\t"
-            "ds_read_b32 %4, %15 offset:8\n\t"
-            "ds_read_b32 %5, %15 offset:448\n\t"
-            "ds_read_b32 %6, %15 offset:452\n\t"
-            "ds_read_b32 %7, %15 offset:456\n\t"
-            "ds_read_b32 %8, %15 offset:896\n\t"
-            "ds_read_b32 %9, %15 offset:900\n\t"
-            "ds_read_b32 %10, %15 offset:904\n\t"
-            "ds_read_b32 %11, %15 offset:1344\n\t"
-            "ds_read_b32 %12, %15 offset:1348\n\t"
-            "ds_read_b32 %13, %15 offset:1352\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(c01), "=&v"(c23), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]),
-              "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7]), "=&v"(w[8]), "=&v"(w[9]),
-              "=&v"(w[10]), "=&v"(w[11])
-            : "v"(cb), "v"(rb)
-            : "memory");
-#pragma unroll
-        for (int k = 0; k < kLaneGroups; ++k) {
-          l.raw[k][0] = __builtin_amdgcn_alignbit(w[3 * k + 1], w[3 * k], sh);
-          l.raw[k][1] = __builtin_amdgcn_alignbit(w[3 * k + 2], w[3 * k + 1], sh);
-        }
-      }
-      l.codes[0] = c01[0]; l.codes[1] = c01[1]; l.codes[2] = c23[0]; l.codes[3] = c23[1];
-    };
-    // The first escape records of a tile (lane j: record e + j) also come
-    // through the ring: its position and the dword holding its symbol land
-    // in the last kilobyte of the tile's slot (dwords 768.. and 832..), and
-    // are read back (before the slot becomes the tile's stage) after the same
-    // explicit wait as the tile.
-    constexpr uint32_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+    auto read_tile = [&](const uint32_t* buf, Lane4& l) { ring_read_tile<LAYOUT>(buf, l); };
     auto dma_eb = [&](uint64_t e0, uint32_t* buf) {
-      const uint64_t idx = e0 + (uint64_t)lane;
-      const uint32_t ic = idx < a.n_esc ? (uint32_t)idx : (uint32_t)a.esc_last;
-      lds_dma4(a.esc_pos + ic, buf + 768);
-      lds_dma4(a.esc_sym + ((ic * kSymBytes) & ~3u), buf + 832);
+      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e0, buf);
     };
     auto read_eb = [&](const uint32_t* buf, uint64_t e0) {
-      const uint32_t ad = lds_addr(buf) + 4u * (uint32_t)lane;
-      uint32_t p, w;
-      asm volatile("ds_read_b32 %0, %2 offset:3072\n\tds_read_b32 %1, %2 offset:3328\n\ts_waitcnt lgkmcnt(0)"
-                   : "=&v"(p), "=&v"(w) : "v"(ad) : "memory");
-      const uint64_t idx = e0 + (uint64_t)lane;
-      const uint32_t ic = idx < a.n_esc ? (uint32_t)idx : (uint32_t)a.esc_last;
-      EscBatch b;
-      b.pos = idx < a.n_esc ? p : 0xFFFFFFFFu;
-      b.sym = (w >> (8u * ((ic * kSymBytes) & 3u))) & (LAYOUT == WC_LAYOUT_K15 ? 0x1FFu : 0xFFu);
-      return b;
+      return ring_read_esc<LAYOUT>(buf, e0, a.n_esc, a.esc_last);
     };
     uint32_t* const s0 = ring0[wib];
     uint32_t* const s1 = ring1[wib];

@@ -257,6 +257,114 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, init, load_tile, process);
 }
 
+// k_decode_gemv for rows of whole tiles (cols a multiple of 2048): the coded
+// tiles and their first escape records stream through a two-slot LDS ring
+// filled by global->LDS loads (wc_tile.h ring_*), one tile ahead, instead
+// of the register ring.  At batch 1, x for the next tile rides in
+// registers; larger batches read x when the tile is used.  Completion of the
+// ring loads is awaited with explicit vmcnt counts over the per-tile
+// instruction sequence: 3 ring loads + (batch 1) 4 x loads, then during the
+// tile 2 record loads, then at a row's end its output stores (extra loads on
+// escape-heavy paths and the stores only lengthen a wait).
+template <int LAYOUT, int B>
+__global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) {
+  __shared__ uint32_t T2[256];
+  __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][kRingSlotDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][kRingSlotDwords];
+  build_pair_table<LAYOUT>(T2, a.dict);
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int wib = wave_in_block();
+  const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wib;
+  const uint64_t r0 = wave * a.rows_per_wave;
+  if (r0 >= a.rows) return;
+  const uint64_t r1 = r0 + a.rows_per_wave < a.rows ? r0 + a.rows_per_wave : a.rows;
+  const uint64_t gpr = a.cols / kGroup;
+  const uint64_t tpr = a.cols / kTile;  // whole tiles
+  const uint64_t nq = (r1 - r0) * tpr;
+  uint32_t* const s0 = ring0[wib];
+  uint32_t* const s1 = ring1[wib];
+
+  constexpr bool kXpf = B == 1;
+  uint32_t lg[kLaneGroups];
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) lg[k] = (uint32_t)lane + kWave * k;
+  // tile q of the wave: row r0 + q / tpr, tile q % tpr of the row; past the
+  // end the last tile is reloaded (its data is unused)
+  TileCursor lc{r0, 0};
+  uint64_t lq = 0;
+  auto load_next = [&](uint32_t* buf, uint32_t xv[16]) {
+    ring_load_tile<LAYOUT>(a.codes, a.raw, lc.r * gpr + lc.ct * (kTile / kGroup), buf);
+    if (kXpf) load_x_lane(a.x + lc.ct * kTile, lg, xv);
+    if (lq + 1 < nq) {
+      lc.next(tpr);
+      ++lq;
+    }
+  };
+
+  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
+  float acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+  uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
+  ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e, s0);
+  load_next(s0, x0);
+  TileCursor pc{r0, 0};
+
+  auto step = [&](uint64_t q, uint32_t* buf, uint32_t* nbuf, uint32_t xv[16], uint32_t xn[16]) {
+    wait_lgkm0();  // the previous tile's LDS reads and stage writes are done
+    load_next(nbuf, xn);
+    // this tile's ring loads and (younger) record loads: after the records
+    // come the previous tile's output stores (if any), this step's 3 ring
+    // loads and (batch 1) 4 x loads; the first tile's records come before
+    // its ring loads and x loads
+    if (q == 0) wait_vm<kXpf ? 11 : 3>();
+    else wait_vm<kXpf ? 7 : 3>();
+    Lane4 l;
+    ring_read_tile<LAYOUT>(buf, l);
+    const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, a.n_esc, a.esc_last);
+    uint32_t xb1[kXpf ? 1 : 16];
+    if (!kXpf && B == 1) load_x_lane(a.x + pc.ct * kTile, lg, xb1);
+    uint32_t marks[kLaneGroups];
+    const bool any = escape_marks(l, marks);
+    const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
+    ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave, nbuf);
+    uint32_t w[16];
+    rebuild_lane<LAYOUT>(T2, a.dict, l, w);
+    if (cnt_wave > kDenseMin) {
+      patch_tile_windows<LAYOUT>(l, w, a.esc_sym, a.sym_last, e);
+    } else if (cnt_wave) {
+      patch_tile<LAYOUT>(buf, w, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
+                         cnt_wave, pc.r * a.cols + pc.ct * kTile, kTile, eb);
+    }
+    e += cnt_wave;
+    if (B == 1) {
+      acc[0] = dot_lane(w, kXpf ? xv : xb1, acc[0]);
+    } else {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        uint32_t xb[16];
+        load_x_lane(a.x + (uint64_t)b * a.cols + pc.ct * kTile, lg, xb);
+        acc[b] = dot_lane(w, xb, acc[b]);
+      }
+    }
+    if (pc.ct + 1 == tpr) {
+      store_row<B>(acc, a.y, a.rows, pc.r);
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    }
+    pc.next(tpr);
+  };
+  uint64_t q = 0;
+  for (; q + 1 < nq; q += 2) {
+    step(q, s0, s1, x0, x1);
+    step(q + 1, s1, s0, x1, x0);
+  }
+  if (q < nq) step(q, s0, s1, x0, x1);
+  wait_vm<0>();  // the ring's last (unused) loads land before the wave ends
+}
+
 // The same wave/tile schedule as k_decode_gemv with W read as plain BF16
 // (16 bytes per group) and no rebuild: the comparison kernel.
 template <int B>
@@ -420,6 +528,11 @@ __global__ void k_fill_zero(float* y, uint64_t count) {
 #define WC_MFMA_MIN_BATCH 8
 #endif
 constexpr uint32_t kMfmaMinBatch = WC_MFMA_MIN_BATCH;
+// Rows of whole tiles take the LDS-ring kernel.
+#ifndef WC_GEMV_RING
+#define WC_GEMV_RING 1
+#endif
+constexpr bool kGemvRing = WC_GEMV_RING;
 
 static dim3 row_grid(uint64_t rows) {
   const uint64_t wpb = kBlockThreads / kWave;
@@ -457,12 +570,21 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
     uint32_t b = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
     p.batch = b;
     const dim3 g = wave_grid(a.rows, a.rows_per_wave), t(kBlockThreads);
-    switch (b) {
-      case 16: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 16>), g, t, 0, s, p); break;
-      case 8: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 8>), g, t, 0, s, p); break;
-      case 4: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 4>), g, t, 0, s, p); break;
-      case 2: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 2>), g, t, 0, s, p); break;
-      default: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 1>), g, t, 0, s, p); break;
+    // (batches of 8 and 16 with whole-tile rows take the matrix-core kernel)
+    if (kGemvRing && a.cols % kTile == 0 && b <= 4) {
+      switch (b) {
+        case 4: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4>), g, t, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2>), g, t, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1>), g, t, 0, s, p); break;
+      }
+    } else {
+      switch (b) {
+        case 16: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 16>), g, t, 0, s, p); break;
+        case 8: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 8>), g, t, 0, s, p); break;
+        case 4: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 4>), g, t, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 2>), g, t, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 1>), g, t, 0, s, p); break;
+      }
     }
     done += b;
   }

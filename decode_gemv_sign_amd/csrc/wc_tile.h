@@ -354,6 +354,120 @@ __device__ inline void patch_tile(uint32_t* __restrict__ stage, uint32_t out[16]
   wave_lds_sync();  // the stage is reused by this wave's next tile
 }
 
+// ---- LDS ring of tiles ----------------------------------------------------
+//
+// A ring slot (4 KB per wave) holds one tile as loaded by global->LDS loads:
+// codes at bytes [0, 1024), raw part at [1024, 3072) (K15 uses 1792 bytes),
+// and the tile's first 64 escape records at [3072, 3584): positions at
+// dwords 768.., and at dwords 832.. the dword holding each symbol.  The
+// loads count in vmcnt and the compiler does not track their LDS writes, so
+// users await them with explicit counts before reading the slot, and read it
+// with hand-written LDS instructions.  Once read, the slot can serve as the
+// tile's escape stage.
+
+constexpr uint32_t kRingSlotDwords = 1024;
+
+// Tile whose first group is G (a multiple of 256, so every window below is
+// 16-byte aligned): 3 instructions.
+template <int LAYOUT>
+__device__ inline void ring_load_tile(const uint8_t* codes, const uint8_t* raw, uint64_t G,
+                                      uint32_t* buf) {
+  constexpr uint32_t kRawTile = LAYOUT == WC_LAYOUT_K15 ? 7 * kTile / 8 : kTile;
+  const uint32_t lane = (uint32_t)lane_id();
+  const uint8_t* cp = codes + 4 * G;
+  const uint8_t* rp = raw + (LAYOUT == WC_LAYOUT_K15 ? 7 * G : 8 * G);
+  const uint32_t o2 = 1024u + 16u * lane;  // K15: lanes past 1792 bytes re-read the last 16
+  lds_dma16(cp + 16 * lane, buf);
+  lds_dma16(rp + 16 * lane, buf + 256);
+  lds_dma16(rp + (o2 + 16u <= kRawTile ? o2 : kRawTile - 16u), buf + 512);
+}
+
+// The slot's tile in the group mapping (lane L: groups L + 64k).
+template <int LAYOUT>
+__device__ inline void ring_read_tile(const uint32_t* buf, Lane4& l) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const uint32_t lane = (uint32_t)lane_id();
+  const uint32_t cb = lds_addr(buf) + 4u * lane;  // code of group L at dword L
+  u32x2 c01, c23;
+  if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
+    const uint32_t rb = lds_addr(buf) + 1024u + 8u * lane;  // raw of group L
+    u32x4 r01, r23;
+    // outputs early-clobber: the block reads its address registers after
+    // writing results
+    asm volatile(
+        "ds_read2st64_b32 %0, %4 offset1:1\n\t"
+        "ds_read2st64_b32 %1, %4 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b64 %2, %5 offset1:1\n\t"
+        "ds_read2st64_b64 %3, %5 offset0:2 offset1:3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c01), "=&v"(c23), "=&v"(r01), "=&v"(r23)
+        : "v"(cb), "v"(rb)
+        : "memory");
+    l.raw[0][0] = r01[0]; l.raw[0][1] = r01[1]; l.raw[1][0] = r01[2]; l.raw[1][1] = r01[3];
+    l.raw[2][0] = r23[0]; l.raw[2][1] = r23[1]; l.raw[3][0] = r23[2]; l.raw[3][1] = r23[3];
+  } else {
+    // group L + 64k starts at raw byte 7L + 448k: dwords d0 + 112k + {0,1,2}
+    const uint32_t byte = 7u * lane, sh = (byte & 3u) * 8u;
+    const uint32_t rb = lds_addr(buf) + 1024u + 4u * (byte >> 2);
+    uint32_t w[12];
+    asm volatile(
+        "ds_read2st64_b32 %0, %14 offset1:1\n\t"
+        "ds_read2st64_b32 %1, %14 offset0:2 offset1:3\n\t"
+        "ds_read_b32 %2, %15\n\t"
+        "ds_read_b32 %3, %15 offset:4\n\t"
+        "ds_read_b32 %4, %15 offset:8\n\t"
+        "ds_read_b32 %5, %15 offset:448\n\t"
+        "ds_read_b32 %6, %15 offset:452\n\t"
+        "ds_read_b32 %7, %15 offset:456\n\t"
+        "ds_read_b32 %8, %15 offset:896\n\t"
+        "ds_read_b32 %9, %15 offset:900\n\t"
+        "ds_read_b32 %10, %15 offset:904\n\t"
+        "ds_read_b32 %11, %15 offset:1344\n\t"
+        "ds_read_b32 %12, %15 offset:1348\n\t"
+        "ds_read_b32 %13, %15 offset:1352\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c01), "=&v"(c23), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]),
+          "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7]), "=&v"(w[8]), "=&v"(w[9]),
+          "=&v"(w[10]), "=&v"(w[11])
+        : "v"(cb), "v"(rb)
+        : "memory");
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k) {
+      l.raw[k][0] = __builtin_amdgcn_alignbit(w[3 * k + 1], w[3 * k], sh);
+      l.raw[k][1] = __builtin_amdgcn_alignbit(w[3 * k + 2], w[3 * k + 1], sh);
+    }
+  }
+  l.codes[0] = c01[0]; l.codes[1] = c01[1]; l.codes[2] = c23[0]; l.codes[3] = c23[1];
+}
+
+// Records e0 .. e0 + 63 (lane j: record e0 + j, clamped to `last` past the
+// stream): 2 instructions.
+template <int LAYOUT>
+__device__ inline void ring_load_esc(const uint32_t* esc_pos, const uint8_t* esc_sym, uint64_t n_esc,
+                                     uint64_t last, uint64_t e0, uint32_t* buf) {
+  constexpr uint32_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  const uint64_t idx = e0 + (uint64_t)lane_id();
+  const uint32_t ic = idx < n_esc ? (uint32_t)idx : (uint32_t)last;
+  lds_dma4(esc_pos + ic, buf + 768);
+  lds_dma4(esc_sym + ((ic * kSymBytes) & ~3u), buf + 832);
+}
+
+template <int LAYOUT>
+__device__ inline EscBatch ring_read_esc(const uint32_t* buf, uint64_t e0, uint64_t n_esc,
+                                         uint64_t last) {
+  constexpr uint32_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  const uint32_t ad = lds_addr(buf) + 4u * (uint32_t)lane_id();
+  uint32_t p, w;
+  asm volatile("ds_read_b32 %0, %2 offset:3072\n\tds_read_b32 %1, %2 offset:3328\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(p), "=&v"(w) : "v"(ad) : "memory");
+  const uint64_t idx = e0 + (uint64_t)lane_id();
+  const uint32_t ic = idx < n_esc ? (uint32_t)idx : (uint32_t)last;
+  EscBatch b;
+  b.pos = idx < n_esc ? p : 0xFFFFFFFFu;
+  b.sym = (w >> (8u * ((ic * kSymBytes) & 3u))) & (LAYOUT == WC_LAYOUT_K15 ? 0x1FFu : 0xFFu);
+  return b;
+}
+
 // ---- dense escape tiles: per-group symbol windows -----------------------
 //
 // When a tile holds more escapes than one wave-wide batch of records, each

@@ -198,15 +198,18 @@ def test_gemv_escape_dense(layout):
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_gemv_every_batch(layout):
     """Batches 1..16 on shapes with a ragged 16-row block and a partial last
-    128-column chunk; escapes in the tensor's last weights (the symbol window
-    of the last lanes meets the end of the stream) and one dense band."""
-    for rows, cols, dense in ((19, 160, False), (45, 1056, True)):
+    128-column chunk, and on rows of whole 2048-weight tiles (the LDS-ring
+    kernel); escapes in the tensor's last weights (the symbol window of the
+    last lanes meets the end of the stream) and one dense band."""
+    for rows, cols, dense in ((19, 160, False), (45, 1056, True), (13, 4096, True)):
         W = synth.random_bits(rows * cols, 1200 + rows, "normal").reshape(rows, cols)
         flat = W.reshape(-1)
         flat[::211] ^= 0x3000
         flat[-5:] ^= 0x4000
         if dense:
-            W[17:33] = synth.random_bits(16 * cols, 1300, "uniform").reshape(16, cols) & np.uint16(0xBFFF)
+            band = slice(17, 33) if rows > 33 else slice(5, 9)
+            nb = band.stop - band.start
+            W[band] = synth.random_bits(nb * cols, 1300, "uniform").reshape(nb, cols) & np.uint16(0xBFFF)
         h, c = gpu_encode(layout, W)
         assert h.n_esc > 0
         X = synth.vectors(1400 + rows, 16, cols)
