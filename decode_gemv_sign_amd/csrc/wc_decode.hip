@@ -25,10 +25,6 @@ constexpr uint64_t kDecodeTilesPerWave = WC_DECODE_TILES_PER_WAVE;
 #ifndef WC_DECODE_DMA
 #define WC_DECODE_DMA 1
 #endif
-#ifndef WC_DECODE_RING
-#define WC_DECODE_RING 2
-#endif
-constexpr int kDecodeRing = WC_DECODE_RING;  // LDS tile buffers per wave
 
 struct DecodeArgs {
   const uint8_t* codes;
@@ -45,12 +41,11 @@ template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   __shared__ uint32_t T2[256];
 #if WC_DECODE_DMA
-  // per wave: a ring of tile buffers filled by global->LDS loads
+  // per wave: a two-slot ring of tile buffers filled by global->LDS loads
   // 4 KB per slot: codes 1 KB + raw 2 KB, and the whole slot doubles as the
   // escape stage of the tile just read from it
   __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][kStageDwords];
   __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][kStageDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t ring2[kDecodeRing > 2 ? kBlockThreads / kWave : 1][kStageDwords];
 #else
   __shared__ __attribute__((aligned(16))) uint32_t stage[kBlockThreads / kWave][kStageDwords];
 #endif
@@ -103,13 +98,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
 
 #if WC_DECODE_DMA
   if (t0 < f1) {
-    // Full tiles stream through a ring of kDecodeRing LDS slots (wc_tile.h
-    // ring_*), kDecodeRing - 1 tiles ahead.  The loads need no registers, so
-    // the ring depth does not cost occupancy.  Their completion is awaited
-    // with explicit counts of the vector-memory instructions issued after
-    // them (per tile: 3 ring loads, 2 escape-record loads, 4 stores; extra
-    // loads on escape-heavy paths only make the wait longer).
-    constexpr int R = kDecodeRing;
+    // Full tiles stream through a two-slot LDS ring (wc_tile.h ring_*), one
+    // tile ahead.  The loads need no registers, so the prefetch does not
+    // cost occupancy.
     auto dma_tile = [&](uint64_t t, uint32_t* buf) {
       const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
       ring_load_tile<LAYOUT>(a.codes, a.raw, tc * (kTile / kGroup), buf);
@@ -123,50 +114,49 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     };
     uint32_t* const s0 = ring0[wib];
     uint32_t* const s1 = ring1[wib];
-    uint32_t* const s2 = ring2[kDecodeRing > 2 ? wib : 0];
     auto slot_buf = [&](auto slc) -> uint32_t* {
-      constexpr int sl = decltype(slc)::value % R;
-      return sl == 0 ? s0 : (sl == 1 ? s1 : s2);
+      return decltype(slc)::value % 2 == 0 ? s0 : s1;
     };
     find_cursor();
     dma_eb(e, s0);
     dma_tile(t0, s0);
-    if (R > 2) dma_tile(t0 + 1, s1);
     uint64_t t = t0;
-    // Per tile, in order: 3 ring loads (tile t + R - 1), then during the
-    // rebuild 2 record loads (tile t + 1, into its slot), then 4 stores.
-    auto step = [&](auto slc, uint32_t j) {
+    // Each step issues the next tile's ring loads, waits for the current
+    // tile's ring and record loads (ring_wait_ahead), then stores the
+    // previous tile: deferred by one step, the stores have a whole step to
+    // complete before a wait can find them outstanding.
+    uint32_t outA[16], outB[16];  // rebuilt tiles of even / odd steps
+    auto store_tile = [&](uint64_t tt, const uint32_t out[16]) {
+      u32x4* dst = (u32x4*)(a.out + tt * kTile) + lane;
+#pragma unroll
+      for (int k = 0; k < kLaneGroups; ++k)
+        __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
+                                    dst + kWave * k);
+    };
+    auto step = [&](auto slc, uint32_t* out, const uint32_t* prev) {
       constexpr int sl = decltype(slc)::value;
       wait_lgkm0();  // tile t-1's LDS reads and stage writes are done before it is refilled
-      dma_tile(t + R - 1, slot_buf(std::integral_constant<int, sl + R - 1>{}));
-      // wait for tile t's ring loads and its record loads.  The record
-      // loads are the younger ones (issued during tile t-1, after tile t's
-      // ring loads) and 7 instructions follow them: tile t-1's 4 stores and
-      // the 3 ring loads just issued.  The first tile's records come before
-      // its ring loads, which are followed by the other R - 1 tiles' loads.
-      if (j == 0) wait_vm<3 * (R - 1)>();
-      else wait_vm<7>();
+      dma_tile(t + 1, slot_buf(std::integral_constant<int, sl + 1>{}));
+      wait_vm<kRingAhead>();
+      if (t > t0) store_tile(t - 1, prev);
       Lane4 l;
       uint32_t* buf = slot_buf(slc);
       read_tile(buf, l);
       const EscBatch eb = read_eb(buf, e);
       uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
-      uint32_t out[16];
       rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf);
-      u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
-#pragma unroll
-      for (int k = 0; k < kLaneGroups; ++k)
-        __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
-                                    dst + kWave * k);
       ++t;
     };
-    while (t + R <= f1) {
-      step(std::integral_constant<int, 0>{}, (uint32_t)(t - t0));
-      step(std::integral_constant<int, 1>{}, (uint32_t)(t - t0));
-      if constexpr (R > 2) step(std::integral_constant<int, 2>{}, (uint32_t)(t - t0));
+    while (t + 2 <= f1) {
+      step(std::integral_constant<int, 0>{}, outA, outB);
+      step(std::integral_constant<int, 1>{}, outB, outA);
     }
-    if (t < f1) step(std::integral_constant<int, 0>{}, (uint32_t)(t - t0));
-    if (t < f1) step(std::integral_constant<int, 1>{}, (uint32_t)(t - t0));
+    if (t < f1) {
+      step(std::integral_constant<int, 0>{}, outA, outB);
+      store_tile(t - 1, outA);
+    } else {
+      store_tile(t - 1, outB);
+    }
     wait_vm<0>();  // the ring's last (unused) loads land before the stage is reused
     wait_lgkm0();
   }

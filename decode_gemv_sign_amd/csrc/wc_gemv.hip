@@ -261,11 +261,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
 // tiles and their first escape records stream through a two-slot LDS ring
 // filled by global->LDS loads (wc_tile.h ring_*), one tile ahead, instead
 // of the register ring.  At batch 1, x for the next tile rides in
-// registers; larger batches read x when the tile is used.  Completion of the
-// ring loads is awaited with explicit vmcnt counts over the per-tile
-// instruction sequence: 3 ring loads + (batch 1) 4 x loads, then during the
-// tile 2 record loads, then at a row's end its output stores (extra loads on
-// escape-heavy paths and the stores only lengthen a wait).
+// registers; larger batches read x when the tile is used.  Each step issues
+// the next tile's loads first and waits for them before its dot product.
 template <int LAYOUT, int B>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) {
   __shared__ uint32_t T2[256];
@@ -315,12 +312,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   auto step = [&](uint64_t q, uint32_t* buf, uint32_t* nbuf, uint32_t xv[16], uint32_t xn[16]) {
     wait_lgkm0();  // the previous tile's LDS reads and stage writes are done
     load_next(nbuf, xn);
-    // this tile's ring loads and (younger) record loads: after the records
-    // come the previous tile's output stores (if any), this step's 3 ring
-    // loads and (batch 1) 4 x loads; the first tile's records come before
-    // its ring loads and x loads
-    if (q == 0) wait_vm<kXpf ? 11 : 3>();
-    else wait_vm<kXpf ? 7 : 3>();
+    // The first tile's ring and record loads are complete once at most the 3
+    // ring loads just issued are outstanding (ring_wait_ahead); later tiles'
+    // loads were issued before the previous tile's full wait.
+    if (q == 0) wait_vm<kRingAhead>();
     Lane4 l;
     ring_read_tile<LAYOUT>(buf, l);
     const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, a.n_esc, a.esc_last);
@@ -339,6 +334,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
                          cnt_wave, pc.r * a.cols + pc.ct * kTile, kTile, eb);
     }
     e += cnt_wave;
+    // Full wait: x is read by ordinary loads, which the compiler awaits with
+    // vmcnt(0) anyway while global->LDS loads are pending; it also completes
+    // the next tile's ring and record loads.
+    wait_vm<0>();
     if (B == 1) {
       acc[0] = dot_lane(w, kXpf ? xv : xb1, acc[0]);
     } else {

@@ -367,6 +367,19 @@ __device__ inline void patch_tile(uint32_t* __restrict__ stage, uint32_t out[16]
 
 constexpr uint32_t kRingSlotDwords = 1024;
 
+// ring_wait_ahead: how a ring user awaits its slot.  vmcnt counts every
+// outstanding vector-memory operation, but only operations of one kind are
+// taken to complete in issue order: global->LDS loads among themselves.
+// Ordinary loads and stores may complete before an older global->LDS load
+// (the compiler's own wait placement assumes no order between the kinds:
+// with one pending it waits for vmcnt(0)).  So "at most N outstanding"
+// proves a global->LDS load complete only when N counts global->LDS loads
+// issued after it; ordinary loads and stores in between are never counted
+// (they only make the wait longer).  A ring user issues the next tile's 3
+// ring loads after the current tile's record loads and waits for at most
+// those 3.
+constexpr int kRingAhead = 3;
+
 // Tile whose first group is G (a multiple of 256, so every window below is
 // 16-byte aligned): 3 instructions.
 template <int LAYOUT>
