@@ -72,11 +72,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
 
   // Rebuild + escapes of tile t into out[16] (the lane's 4 groups).  The
   // tile's first escape records come in `eb` (loaded while the previous tile
-  // was processed); the next tile's are issued into `eb_next` as soon as
-  // this tile's escape count is known, so they arrive during its rebuild.
-  // `async`: eb was loaded by load_esc_async (flag ok_cur) and eb_next is
-  // loaded the same way (flag ok_next); the batch is awaited explicitly.
-  // `issue_next(e_next)` starts the next tile's first-records load as soon
+  // was processed); `issue_next(e_next)` starts the next tile's load as soon
   // as this tile's escape count is known (it arrives during the rebuild).
   auto rebuild = [&](uint64_t t, const Lane4& l, const EscBatch& eb, auto&& issue_next,
                      uint32_t out[16], uint32_t* stg) {
@@ -102,8 +98,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     // tile ahead.  The loads need no registers, so the prefetch does not
     // cost occupancy.
     auto dma_tile = [&](uint64_t t, uint32_t* buf) {
-      const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
-      ring_load_tile<LAYOUT>(a.codes, a.raw, tc * (kTile / kGroup), buf);
+      ring_load_tile<LAYOUT>(a.codes, a.raw, t * (kTile / kGroup), buf);
     };
     auto read_tile = [&](const uint32_t* buf, Lane4& l) { ring_read_tile<LAYOUT>(buf, l); };
     auto dma_eb = [&](uint64_t e0, uint32_t* buf) {
@@ -117,14 +112,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     auto slot_buf = [&](auto slc) -> uint32_t* {
       return decltype(slc)::value % 2 == 0 ? s0 : s1;
     };
+    dma_tile(t0, s0);  // in flight during the cursor search
     find_cursor();
     dma_eb(e, s0);
-    dma_tile(t0, s0);
     uint64_t t = t0;
     // Each step issues the next tile's ring loads, waits for the current
-    // tile's ring and record loads (ring_wait_ahead), then stores the
-    // previous tile: deferred by one step, the stores have a whole step to
-    // complete before a wait can find them outstanding.
+    // tile's ring and record loads (ring_wait_ahead; the last step, with no
+    // next tile, waits for all), then stores the previous tile: deferred by
+    // one step, the stores have a whole step to complete before a wait can
+    // find them outstanding.
     uint32_t outA[16], outB[16];  // rebuilt tiles of even / odd steps
     auto store_tile = [&](uint64_t tt, const uint32_t out[16]) {
       u32x4* dst = (u32x4*)(a.out + tt * kTile) + lane;
@@ -136,8 +132,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     auto step = [&](auto slc, uint32_t* out, const uint32_t* prev) {
       constexpr int sl = decltype(slc)::value;
       wait_lgkm0();  // tile t-1's LDS reads and stage writes are done before it is refilled
-      dma_tile(t + 1, slot_buf(std::integral_constant<int, sl + 1>{}));
-      wait_vm<kRingAhead>();
+      if (t + 1 < f1) {
+        dma_tile(t + 1, slot_buf(std::integral_constant<int, sl + 1>{}));
+        wait_vm<kRingAhead>();
+      } else {
+        wait_vm<0>();
+      }
       if (t > t0) store_tile(t - 1, prev);
       Lane4 l;
       uint32_t* buf = slot_buf(slc);
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     } else {
       store_tile(t - 1, outB);
     }
-    wait_vm<0>();  // the ring's last (unused) loads land before the stage is reused
+    wait_vm<0>();  // the last step's (unused) record loads land before the stage is reused
     wait_lgkm0();
   }
 #else

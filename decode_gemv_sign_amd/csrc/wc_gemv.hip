@@ -287,35 +287,36 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   uint32_t lg[kLaneGroups];
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) lg[k] = (uint32_t)lane + kWave * k;
-  // tile q of the wave: row r0 + q / tpr, tile q % tpr of the row; past the
-  // end the last tile is reloaded (its data is unused)
+  // tile q of the wave: row r0 + q / tpr, tile q % tpr of the row (loaded
+  // for q < nq only)
   TileCursor lc{r0, 0};
-  uint64_t lq = 0;
   auto load_next = [&](uint32_t* buf, uint32_t xv[16]) {
     ring_load_tile<LAYOUT>(a.codes, a.raw, lc.r * gpr + lc.ct * (kTile / kGroup), buf);
     if (kXpf) load_x_lane(a.x + lc.ct * kTile, lg, xv);
-    if (lq + 1 < nq) {
-      lc.next(tpr);
-      ++lq;
-    }
+    lc.next(tpr);
   };
 
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
+  load_next(s0, x0);  // in flight during the cursor search
+  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
   ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e, s0);
-  load_next(s0, x0);
   TileCursor pc{r0, 0};
 
   auto step = [&](uint64_t q, uint32_t* buf, uint32_t* nbuf, uint32_t xv[16], uint32_t xn[16]) {
     wait_lgkm0();  // the previous tile's LDS reads and stage writes are done
-    load_next(nbuf, xn);
     // The first tile's ring and record loads are complete once at most the 3
-    // ring loads just issued are outstanding (ring_wait_ahead); later tiles'
-    // loads were issued before the previous tile's full wait.
-    if (q == 0) wait_vm<kRingAhead>();
+    // ring loads of the next tile are outstanding (ring_wait_ahead), or none
+    // when there is no next tile; later tiles' loads were issued before the
+    // previous tile's full wait.
+    if (q + 1 < nq) {
+      load_next(nbuf, xn);
+      if (q == 0) wait_vm<kRingAhead>();
+    } else if (q == 0) {
+      wait_vm<0>();
+    }
     Lane4 l;
     ring_read_tile<LAYOUT>(buf, l);
     const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, a.n_esc, a.esc_last);
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     step(q + 1, s1, s0, x1, x0);
   }
   if (q < nq) step(q, s0, s1, x0, x1);
-  wait_vm<0>();  // the ring's last (unused) loads land before the wave ends
+  wait_vm<0>();  // the last tile's (unused) record loads land before the wave ends
 }
 
 // The same wave/tile schedule as k_decode_gemv with W read as plain BF16
