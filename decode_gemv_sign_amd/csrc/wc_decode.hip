@@ -22,9 +22,6 @@ namespace wc {
 #define WC_DECODE_TILES_PER_WAVE 4
 #endif
 constexpr uint64_t kDecodeTilesPerWave = WC_DECODE_TILES_PER_WAVE;
-#ifndef WC_DECODE_DMA
-#define WC_DECODE_DMA 1
-#endif
 
 struct DecodeArgs {
   const uint8_t* codes;
@@ -37,18 +34,19 @@ struct DecodeArgs {
   Dict dict;
 };
 
-template <int LAYOUT>
+// DEPTH: tiles in flight ahead of the one being rebuilt (1 or 2); the ring
+// has DEPTH + 1 slots.
+template <int LAYOUT, int DEPTH>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
+  static_assert(DEPTH == 1 || DEPTH == 2, "ring depth");
   __shared__ uint32_t T2[256];
-#if WC_DECODE_DMA
-  // per wave: a two-slot ring of tile buffers filled by global->LDS loads
-  // 4 KB per slot: codes 1 KB + raw 2 KB, and the whole slot doubles as the
-  // escape stage of the tile just read from it
-  __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][kStageDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][kStageDwords];
-#else
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kBlockThreads / kWave][kStageDwords];
-#endif
+  // per wave: a ring of tile buffers filled by global->LDS loads, 4 KB per
+  // slot (codes 1 KB + raw 2 KB + the first escape records); the whole slot
+  // doubles as the escape stage of the tile just read from it
+  constexpr int kWpb = kBlockThreads / kWave;
+  __shared__ __attribute__((aligned(16))) uint32_t ring0[kWpb][kStageDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring1[kWpb][kStageDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring2[DEPTH == 2 ? kWpb : 1][DEPTH == 2 ? kStageDwords : 4];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -60,11 +58,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   if (t0 >= t1) return;
 
   // Every tile but the tensor's last is full.  Full tiles run in a software
-  // pipeline: tile t+1's loads are in flight while tile t is rebuilt, patched
-  // and stored.  Two register sets alternate (the loop is unrolled by two)
-  // and every load is issued unconditionally, at a clamped valid address
-  // when its data will not be used, so the loads in flight are the same on
-  // every path and no wait covers the prefetch.
+  // pipeline: the next tiles' loads are in flight while tile t is rebuilt,
+  // patched and stored.
   const uint64_t full_tiles = a.n / kTile;
   const uint64_t f1 = t1 < full_tiles ? t1 : full_tiles;  // end of this wave's full tiles
   uint64_t e = 0;  // escape cursor, found once the first tile's loads are in flight
@@ -92,11 +87,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     e += cnt_wave;
   };
 
-#if WC_DECODE_DMA
   if (t0 < f1) {
-    // Full tiles stream through a two-slot LDS ring (wc_tile.h ring_*), one
-    // tile ahead.  The loads need no registers, so the prefetch does not
-    // cost occupancy.
+    // Full tiles stream through the LDS ring (wc_tile.h ring_*), DEPTH tiles
+    // ahead.  The loads need no registers, so the prefetch does not cost
+    // occupancy.
     auto dma_tile = [&](uint64_t t, uint32_t* buf) {
       ring_load_tile<LAYOUT>(a.codes, a.raw, t * (kTile / kGroup), buf);
     };
@@ -109,97 +103,107 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     };
     uint32_t* const s0 = ring0[wib];
     uint32_t* const s1 = ring1[wib];
-    auto slot_buf = [&](auto slc) -> uint32_t* {
-      return decltype(slc)::value % 2 == 0 ? s0 : s1;
-    };
-    dma_tile(t0, s0);  // in flight during the cursor search
-    find_cursor();
-    dma_eb(e, s0);
-    uint64_t t = t0;
-    // Each step issues the next tile's ring loads, waits for the current
-    // tile's ring and record loads (ring_wait_ahead; the last step, with no
-    // next tile, waits for all), then stores the previous tile: deferred by
-    // one step, the stores have a whole step to complete before a wait can
-    // find them outstanding.
-    uint32_t outA[16], outB[16];  // rebuilt tiles of even / odd steps
-    auto store_tile = [&](uint64_t tt, const uint32_t out[16]) {
-      u32x4* dst = (u32x4*)(a.out + tt * kTile) + lane;
+    if constexpr (DEPTH == 2) {
+      // Three slots, two tiles ahead.  A step waits for its tile's ring and
+      // record loads, reads the tile, counts its escapes, then issues the next
+      // tile's records and the ring loads of the tile after it (into the slot
+      // the previous step used), so the records are always followed by exactly
+      // one tile's ring loads, or by none at the run's end (ring_wait_ahead).
+      uint32_t* const s2 = ring2[wib];
+      auto slot3 = [&](auto slc) -> uint32_t* {
+        constexpr int k = decltype(slc)::value % 3;
+        return k == 0 ? s0 : (k == 1 ? s1 : s2);
+      };
+      dma_tile(t0, s0);  // in flight during the cursor search
+      find_cursor();
+      dma_eb(e, s0);
+      if (t0 + 1 < f1) dma_tile(t0 + 1, s1);
+      uint64_t t = t0;
+      auto step = [&](auto slc) {
+        constexpr int sl = decltype(slc)::value;
+        wait_lgkm0();  // tile t-1's LDS reads and stage writes are done before its slot is refilled
+        if (t + 1 < f1) wait_vm<kRingAhead>();
+        else wait_vm<0>();
+        Lane4 l;
+        uint32_t* buf = slot3(slc);
+        read_tile(buf, l);
+        const EscBatch eb = read_eb(buf, e);
+        uint32_t* const n1 = slot3(std::integral_constant<int, sl + 1>{});
+        uint32_t* const n2 = slot3(std::integral_constant<int, sl + 2>{});
+        uint32_t out[16];
+        rebuild(t, l, eb, [&](uint64_t en) {
+          if (t + 1 < f1) dma_eb(en, n1);
+          if (t + 2 < f1) dma_tile(t + 2, n2);
+        }, out, buf);
+        u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
 #pragma unroll
-      for (int k = 0; k < kLaneGroups; ++k)
-        __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
-                                    dst + kWave * k);
-    };
-    auto step = [&](auto slc, uint32_t* out, const uint32_t* prev) {
-      constexpr int sl = decltype(slc)::value;
-      wait_lgkm0();  // tile t-1's LDS reads and stage writes are done before it is refilled
-      if (t + 1 < f1) {
-        dma_tile(t + 1, slot_buf(std::integral_constant<int, sl + 1>{}));
-        wait_vm<kRingAhead>();
-      } else {
-        wait_vm<0>();
+        for (int k = 0; k < kLaneGroups; ++k)
+          __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
+                                      dst + kWave * k);
+        ++t;
+      };
+      while (t + 3 <= f1) {
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
       }
-      if (t > t0) store_tile(t - 1, prev);
-      Lane4 l;
-      uint32_t* buf = slot_buf(slc);
-      read_tile(buf, l);
-      const EscBatch eb = read_eb(buf, e);
-      uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
-      rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf);
-      ++t;
-    };
-    while (t + 2 <= f1) {
-      step(std::integral_constant<int, 0>{}, outA, outB);
-      step(std::integral_constant<int, 1>{}, outB, outA);
-    }
-    if (t < f1) {
-      step(std::integral_constant<int, 0>{}, outA, outB);
-      store_tile(t - 1, outA);
+      if (t < f1) step(std::integral_constant<int, 0>{});
+      if (t < f1) step(std::integral_constant<int, 1>{});
+      wait_lgkm0();
     } else {
-      store_tile(t - 1, outB);
-    }
-    wait_vm<0>();  // the last step's (unused) record loads land before the stage is reused
-    wait_lgkm0();
-  }
-#else
-  if (t0 < f1) {
-    auto load_full = [&](uint64_t t, Lane4& l) {
-      const uint64_t tc = t < f1 ? t : f1 - 1;  // past the run: reload its last tile
-      const GroupBase gb = group_base(LAYOUT, a.codes, a.raw, tc * (kTile / kGroup), a.raw_last);
+      // Two slots, one tile ahead.
+      auto slot_buf = [&](auto slc) -> uint32_t* {
+        return decltype(slc)::value % 2 == 0 ? s0 : s1;
+      };
+      dma_tile(t0, s0);  // in flight during the cursor search
+      find_cursor();
+      dma_eb(e, s0);
+      uint64_t t = t0;
+      // Each step issues the next tile's ring loads, waits for the current
+      // tile's ring and record loads (ring_wait_ahead; the last step, with no
+      // next tile, waits for all), then stores the previous tile: deferred by
+      // one step, the stores have a whole step to complete before a wait can
+      // find them outstanding.
+      uint32_t outA[16], outB[16];  // rebuilt tiles of even / odd steps
+      auto store_tile = [&](uint64_t tt, const uint32_t out[16]) {
+        u32x4* dst = (u32x4*)(a.out + tt * kTile) + lane;
 #pragma unroll
-      for (int k = 0; k < kLaneGroups; ++k)
-        load_group<LAYOUT>(gb, (uint32_t)(lane + kWave * k), l.codes[k], l.raw[k]);
-    };
-    struct Slot {
-      Lane4 l;
-      EscBatch eb;
-    };
-    auto process = [&](uint64_t t, const Slot& cur, Slot& nxt) {
-      uint32_t out[16];
-      rebuild(t, cur.l, cur.eb, [&](uint64_t en) {
-        nxt.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, en);
-      }, out, stage[wib]);
-      u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
-#pragma unroll
-      for (int k = 0; k < kLaneGroups; ++k)
-        __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
-                                    dst + kWave * k);
-    };
-    // Two slots alternate (static register sets); an odd last tile runs
-    // after the loop, so no path leaves the loop body half-way.
-    Slot sa, sb;
-    load_full(t0, sa.l);
-    find_cursor();
-    sa.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
-    uint64_t t = t0;
-    for (; t + 1 < f1; t += 2) {
-      load_full(t + 1, sb.l);
-      process(t, sa, sb);
-      load_full(t + 2, sa.l);
-      process(t + 1, sb, sa);
+        for (int k = 0; k < kLaneGroups; ++k)
+          __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
+                                      dst + kWave * k);
+      };
+      auto step = [&](auto slc, uint32_t* out, const uint32_t* prev) {
+        constexpr int sl = decltype(slc)::value;
+        wait_lgkm0();  // tile t-1's LDS reads and stage writes are done before it is refilled
+        if (t + 1 < f1) {
+          dma_tile(t + 1, slot_buf(std::integral_constant<int, sl + 1>{}));
+          wait_vm<kRingAhead>();
+        } else {
+          wait_vm<0>();
+        }
+        if (t > t0) store_tile(t - 1, prev);
+        Lane4 l;
+        uint32_t* buf = slot_buf(slc);
+        read_tile(buf, l);
+        const EscBatch eb = read_eb(buf, e);
+        uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
+        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf);
+        ++t;
+      };
+      while (t + 2 <= f1) {
+        step(std::integral_constant<int, 0>{}, outA, outB);
+        step(std::integral_constant<int, 1>{}, outB, outA);
+      }
+      if (t < f1) {
+        step(std::integral_constant<int, 0>{}, outA, outB);
+        store_tile(t - 1, outA);
+      } else {
+        store_tile(t - 1, outB);
+      }
+      wait_vm<0>();  // the last step's (unused) record loads land before the stage is reused
+      wait_lgkm0();
     }
-    if (t < f1) process(t, sa, sb);
   }
-#endif
   if (t0 >= f1) find_cursor();  // a wave with only the partial last tile
   if (t1 > full_tiles) {
     // The tensor's partial last tile: groups past n are skipped, the group
@@ -222,11 +226,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     }
     uint32_t out[16];
     const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
-#if WC_DECODE_DMA
     rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib]);
-#else
-    rebuild(full_tiles, l, eb, [](uint64_t) {}, out, stage[wib]);
-#endif
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
       const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;
@@ -267,10 +267,19 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   const uint64_t wpb = kBlockThreads / kWave;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb));
   a.dict = dict_of(&h);
-  if (h.layout == WC_LAYOUT_K15)
-    hipLaunchKernelGGL(k_decode<WC_LAYOUT_K15>, grid, dim3(kBlockThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_decode<WC_LAYOUT_BYTESPLIT>, grid, dim3(kBlockThreads), 0, s, a);
+  // Two tiles ahead, except for escape-heavy tensors (more than one weight
+  // in 8 escapes): their dense tiles read symbol windows with ordinary
+  // loads, whose waits drain the ring, and the fourth wave per SIMD that a
+  // two-slot ring leaves room for pays more there.
+  const bool deep = h.n_esc <= h.n / 8;
+  const dim3 blk(kBlockThreads);
+  if (h.layout == WC_LAYOUT_K15) {
+    if (deep) hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, 2>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, 1>), grid, blk, 0, s, a);
+  } else {
+    if (deep) hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, 2>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, 1>), grid, blk, 0, s, a);
+  }
   return hipGetLastError();
 }
 
