@@ -44,9 +44,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   // slot (codes 1 KB + raw 2 KB + the first escape records); the whole slot
   // doubles as the escape stage of the tile just read from it
   constexpr int kWpb = kBlockThreads / kWave;
-  __shared__ __attribute__((aligned(16))) uint32_t ring0[kWpb][kStageDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t ring1[kWpb][kStageDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t ring2[DEPTH == 2 ? kWpb : 1][DEPTH == 2 ? kStageDwords : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t ring0[kWpb][kRingSlotDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring1[kWpb][kRingSlotDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring2[DEPTH == 2 ? kWpb : 1][DEPTH == 2 ? kRingSlotDwords : 4];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -65,19 +65,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   uint64_t e = 0;  // escape cursor, found once the first tile's loads are in flight
   auto find_cursor = [&]() { e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile) : 0; };
 
-  // Rebuild + escapes of tile t into out[16] (the lane's 4 groups).  The
-  // tile's first escape records come in `eb` (loaded while the previous tile
-  // was processed); `issue_next(e_next)` starts the next tile's load as soon
-  // as this tile's escape count is known (it arrives during the rebuild).
+  // Rebuild + escapes of tile t into out[16] (the lane's 4 groups); `stg` is
+  // the tile's ring slot, free once the tile is in registers.  The tile's
+  // first escape records come in `eb` (loaded while the previous tile was
+  // processed).  As soon as this tile's escape count is known,
+  // `issue_next(e_next, symrun)` issues the next tile's record loads, then
+  // calls symrun() (a dense tile's symbol run into `stg`), then any further
+  // ring loads, and says whether 3 ring loads followed the run.
   auto rebuild = [&](uint64_t t, const Lane4& l, const EscBatch& eb, auto&& issue_next,
                      uint32_t out[16], uint32_t* stg) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
-    issue_next(e + cnt_wave);
+    const bool dense = cnt_wave > kDenseMin;
+    uint32_t off0 = 0;
+    const bool ahead = issue_next(e + cnt_wave, [&]() {
+      if (dense) off0 = ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg);
+    });
     rebuild_lane<LAYOUT>(T2, a.dict, l, out);
-    if (cnt_wave > kDenseMin) {
-      patch_tile_windows<LAYOUT>(l, out, a.esc_sym, a.sym_last, e);
+    if (dense) {
+      if (ahead) wait_vm<kRingAhead>();  // the symbol run is complete (ring_wait_ahead)
+      else wait_vm<0>();
+      patch_tile_symrun<LAYOUT>(l, out, stg, off0);
     } else if (cnt_wave) {
       const uint64_t tile_start = t * kTile;
       const uint32_t tile_len = a.n - tile_start >= kTile ? kTile : (uint32_t)(a.n - tile_start);
@@ -131,9 +140,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         uint32_t* const n1 = slot3(std::integral_constant<int, sl + 1>{});
         uint32_t* const n2 = slot3(std::integral_constant<int, sl + 2>{});
         uint32_t out[16];
-        rebuild(t, l, eb, [&](uint64_t en) {
+        rebuild(t, l, eb, [&](uint64_t en, auto&& symrun) {
           if (t + 1 < f1) dma_eb(en, n1);
-          if (t + 2 < f1) dma_tile(t + 2, n2);
+          symrun();
+          if (t + 2 >= f1) return false;
+          dma_tile(t + 2, n2);
+          return true;
         }, out, buf);
         u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
 #pragma unroll
@@ -187,7 +199,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         read_tile(buf, l);
         const EscBatch eb = read_eb(buf, e);
         uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
-        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf);
+        rebuild(t, l, eb, [&](uint64_t en, auto&& symrun) {
+          dma_eb(en, nbuf);
+          symrun();
+          return false;
+        }, out, buf);
         ++t;
       };
       while (t + 2 <= f1) {
@@ -226,7 +242,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     }
     uint32_t out[16];
     const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
-    rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib]);
+    // no global->LDS load is in flight here: ring0 is free
+    rebuild(full_tiles, l, eb, [](uint64_t, auto&& symrun) {
+      symrun();
+      return false;
+    }, out, ring0[wib]);
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
       const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;

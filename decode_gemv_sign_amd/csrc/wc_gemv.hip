@@ -326,10 +326,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave, nbuf);
+    // a dense tile's symbol run goes into its own slot (free: the tile is in
+    // registers)
+    const bool dense = cnt_wave > kDenseMin;
+    const uint32_t off0 = dense ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, a.dict, l, w);
-    if (cnt_wave > kDenseMin) {
-      patch_tile_windows<LAYOUT>(l, w, a.esc_sym, a.sym_last, e);
+    if (dense) {
+      wait_vm<0>();
+      patch_tile_symrun<LAYOUT>(l, w, buf, off0);
     } else if (cnt_wave) {
       patch_tile<LAYOUT>(buf, w, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
                          cnt_wave, pc.r * a.cols + pc.ct * kTile, kTile, eb);

@@ -359,13 +359,16 @@ __device__ inline void patch_tile(uint32_t* __restrict__ stage, uint32_t out[16]
 // A ring slot (4 KB per wave) holds one tile as loaded by global->LDS loads:
 // codes at bytes [0, 1024), raw part at [1024, 3072) (K15 uses 1792 bytes),
 // and the tile's first 64 escape records at [3072, 3584): positions at
-// dwords 768.., and at dwords 832.. the dword holding each symbol.  The
+// dwords 768.., and at dwords 832.. the dword holding each symbol (a dense
+// tile's symbol run replaces all of it once the tile is in registers).  The
 // loads count in vmcnt and the compiler does not track their LDS writes, so
 // users await them with explicit counts before reading the slot, and read it
 // with hand-written LDS instructions.  Once read, the slot can serve as the
 // tile's escape stage.
 
-constexpr uint32_t kRingSlotDwords = 1024;
+// 4 KB of tile and records, plus room for a dense tile's symbol run (up to
+// 4096 bytes from a 16-byte-aligned start, read back in 20-byte windows).
+constexpr uint32_t kRingSlotDwords = 1040;
 
 // ring_wait_ahead: how a ring user awaits its slot.  vmcnt counts every
 // outstanding vector-memory operation, but only operations of one kind are
@@ -593,6 +596,81 @@ __device__ inline void expand_window(uint32_t m, const uint32_t (&w)[WinDwords<L
   }
 }
 
+// Per group of the lane: m = its code-15 weights (bit i: weight i), c = their
+// count, first = its first record relative to the tile's first (groups
+// L + 64k in tile order: all of k = 0, then k = 1, ...; counts are packed two
+// per dword for the wave's prefix sum).
+__device__ inline void group_records(const Lane4& l, uint32_t m[kLaneGroups],
+                                     uint32_t c[kLaneGroups], uint32_t first[kLaneGroups]) {
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) {
+    m[k] = group_esc_bits(l.codes[k]);
+    c[k] = (uint32_t)__popc(m[k]);
+  }
+  const uint32_t p01 = c[0] | (c[1] << 16), p23 = c[2] | (c[3] << 16);
+  const uint32_t i01 = wave_incl_scan_dpp(p01), i23 = wave_incl_scan_dpp(p23);
+  const uint32_t t01 = (uint32_t)__builtin_amdgcn_readlane((int)i01, kWave - 1);
+  const uint32_t t23 = (uint32_t)__builtin_amdgcn_readlane((int)i23, kWave - 1);
+  const uint32_t x01 = i01 - p01, x23 = i23 - p23;
+  first[0] = x01 & 0xFFFFu;
+  first[1] = (t01 & 0xFFFFu) + (x01 >> 16);
+  first[2] = (t01 & 0xFFFFu) + (t01 >> 16) + (x23 & 0xFFFFu);
+  first[3] = (t01 & 0xFFFFu) + (t01 >> 16) + (t23 & 0xFFFFu) + (x23 >> 16);
+}
+
+// A dense tile's symbol run (records e .. e + cnt - 1, cnt <= 2048) into a
+// ring slot with global->LDS loads: the run's 16-byte chunks from the one
+// holding record e's symbol, 64 chunks per instruction (at most 5; chunks
+// past the stream's padded end re-read its last one).  Returns the byte
+// offset of record e's symbol in the slot.  The caller awaits the loads
+// (ring_wait_ahead) before patch_tile_symrun reads the slot.
+template <int LAYOUT>
+__device__ inline uint32_t ring_load_symrun(const uint8_t* esc_sym, uint64_t sym_last, uint64_t e,
+                                            uint32_t cnt, uint32_t* buf) {
+  constexpr uint64_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  const uint64_t b0 = e * kSymBytes;
+  const uint64_t base = b0 & ~(uint64_t)15;
+  const uint32_t nch = (uint32_t)((b0 + cnt * kSymBytes - base + 15) >> 4);
+  const uint64_t last_chunk = (4 * (sym_last + 1) - 16) >> 4;  // the padded extent is 16-byte whole
+  const uint32_t lane = (uint32_t)lane_id();
+  for (uint32_t c0 = 0; c0 < nch; c0 += kWave) {
+    if (c0 + lane < nch) {
+      uint64_t ch = (base >> 4) + c0 + lane;
+      ch = ch < last_chunk ? ch : last_chunk;
+      lds_dma16(esc_sym + 16 * ch, buf + 4 * c0);
+    }
+  }
+  return (uint32_t)(b0 - base);
+}
+
+// Patch a dense tile from its symbol run in LDS (ring_load_symrun, run byte
+// offset off0): each group reads the window that starts at its first record
+// and writes the symbols into its code-15 weights.
+template <int LAYOUT>
+__device__ inline void patch_tile_symrun(const Lane4& l, uint32_t out[16], const uint32_t* buf,
+                                         uint32_t off0) {
+  constexpr int W = WinDwords<LAYOUT>::value;
+  constexpr uint32_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  uint32_t m[kLaneGroups], c[kLaneGroups], first[kLaneGroups];
+  group_records(l, m, c, first);
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) {
+    const uint32_t o = off0 + first[k] * kSymBytes;  // < 16 + 4096: the window stays in the slot
+    const uint32_t ad = lds_addr(buf) + (o & ~3u);
+    uint32_t w[W];
+    if constexpr (W == 3) {
+      asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %3 offset:4\n\tds_read_b32 %2, %3 offset:8\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]) : "v"(ad) : "memory");
+    } else {
+      asm volatile("ds_read_b32 %0, %5\n\tds_read_b32 %1, %5 offset:4\n\tds_read_b32 %2, %5 offset:8\n\t"
+                   "ds_read_b32 %3, %5 offset:12\n\tds_read_b32 %4, %5 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]) : "v"(ad) : "memory");
+    }
+    if (c[k]) expand_window<LAYOUT>(m[k], w, o & 3u, out + 4 * k);
+  }
+}
+
 // Patch a tile from per-group windows.  `e` = index of the tile's first
 // record; `sym_last` = last dword of the symbol stream's 16-byte padded
 // extent (windows are moved back so they end there; their start may then
@@ -603,24 +681,8 @@ __device__ inline void patch_tile_windows(const Lane4& l, uint32_t out[16],
                                           uint64_t e) {
   constexpr int W = WinDwords<LAYOUT>::value;
   constexpr uint64_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
-  uint32_t m[kLaneGroups], c[kLaneGroups];
-#pragma unroll
-  for (int k = 0; k < kLaneGroups; ++k) {
-    m[k] = group_esc_bits(l.codes[k]);
-    c[k] = (uint32_t)__popc(m[k]);
-  }
-  // first record of each group relative to the tile's (groups L + 64k in
-  // tile order: all of k = 0, then k = 1, ...); counts packed two per dword
-  const uint32_t p01 = c[0] | (c[1] << 16), p23 = c[2] | (c[3] << 16);
-  const uint32_t i01 = wave_incl_scan_dpp(p01), i23 = wave_incl_scan_dpp(p23);
-  const uint32_t t01 = (uint32_t)__builtin_amdgcn_readlane((int)i01, kWave - 1);
-  const uint32_t t23 = (uint32_t)__builtin_amdgcn_readlane((int)i23, kWave - 1);
-  const uint32_t x01 = i01 - p01, x23 = i23 - p23;
-  uint32_t first[kLaneGroups];
-  first[0] = x01 & 0xFFFFu;
-  first[1] = (t01 & 0xFFFFu) + (x01 >> 16);
-  first[2] = (t01 & 0xFFFFu) + (t01 >> 16) + (x23 & 0xFFFFu);
-  first[3] = (t01 & 0xFFFFu) + (t01 >> 16) + (t23 & 0xFFFFu) + (x23 >> 16);
+  uint32_t m[kLaneGroups], c[kLaneGroups], first[kLaneGroups];
+  group_records(l, m, c, first);
   // windows are loaded and applied kWinPass groups at a time (fewer live
   // registers for smaller passes)
 #pragma unroll
