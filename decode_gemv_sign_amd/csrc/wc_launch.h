@@ -18,6 +18,20 @@ struct DictResult {
   uint16_t dict[16];
 };
 
+// Compute units of the current device (cached per device).
+inline uint32_t cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return (uint32_t)cached[dev];
+}
+
 hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t* work,
                              hipStream_t s);
 hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,

@@ -126,6 +126,21 @@ def test_ragged_sizes(layout, kind):
         check_roundtrip(layout, synth.random_bits(n, 500 + i, kind), f"{kind} n={n}")
 
 
+# Tensors of 6146, 9301 and 12290 tiles (2048 weights each, the last one
+# partial): the decode takes runs of 2 to 4 tiles per wave at the chip's wave
+# counts, so its pipelined loops run every length with a ragged last run;
+# 'normal' tensors take the three-slot ring and 'uniform' ones (almost every
+# weight escapes) the two-slot ring.
+LONG = [6145 * 2048 + 1001, 9300 * 2048 + 17, 12289 * 2048 + 2047]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("kind", ["normal", "uniform"])
+def test_run_lengths(layout, kind):
+    for i, n in enumerate(LONG):
+        check_roundtrip(layout, synth.random_bits(n, 700 + i, kind), f"{kind} n={n}")
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_empty_tensor(layout):
     w = torch.empty(0, dtype=torch.int16, device=DEV)
