@@ -116,13 +116,42 @@ __device__ inline uint32_t wave_total(uint32_t v) {
 }
 
 // First index i in [0, count) with pos[i] >= t (count if none), found by the
-// whole wave: each round probes 64 evenly spaced entries and keeps the one
-// interval that can hold the answer.  Every round shrinks the interval, so it
-// ends even on an unsorted (corrupt) array.  Result is wave-uniform.
+// whole wave: each round probes 64 entries and keeps the one interval that
+// can hold the answer.  The first round probes around where t would fall if
+// the count entries were spread evenly over positions [0, total) (skipped
+// when total is 0): 64 probes
+// at a stride of about sqrt(count) / 21 (some three standard deviations of a
+// uniform spread on either side), on multiples of the stride so that waves
+// with nearby targets share the probed lines.  If they bracket the answer
+// within one stride the search goes on there; otherwise (a clustered stream)
+// it starts over on the whole array, whose first rounds probe entries that
+// every wave shares.  Every round shrinks the interval, so it ends even on an
+// unsorted (corrupt) array.  Result is wave-uniform.
 __device__ inline uint64_t wave_lower_bound(const uint32_t* __restrict__ pos, uint64_t count,
-                                            uint64_t t) {
+                                            uint64_t t, uint64_t total) {
   const int lane = lane_id();
   uint64_t lo = 0, hi = count;
+  if (count > 4 * (uint64_t)kWave && total > 0) {
+    const double f = (double)t / (double)total;
+    const int64_t g = (int64_t)((double)count * (f < 1.0 ? f : 1.0));
+    const int64_t s = (int64_t)(__builtin_sqrt((double)count) * (1.0 / 21.0)) + 1;
+    const int64_t i0 = (g / s - (int64_t)(kWave / 2)) * s;  // lane 0's probe
+    const int64_t idx = i0 + (int64_t)lane * s;
+    // outside the array: below before its start, not below past its end
+    const bool below = idx < 0 || (idx < (int64_t)count && (uint64_t)pos[idx] < t);
+    const int64_t k = (int64_t)__popcll(__ballot(below));
+    auto clampi = [&](int64_t v) -> uint64_t {
+      return v < 0 ? 0u : ((uint64_t)v > count ? count : (uint64_t)v);
+    };
+    // lane k - 1 is below (the answer is past its probe), lane k is not (the
+    // answer is at most its probe)
+    const uint64_t blo = k > 0 ? clampi(i0 + (k - 1) * s + 1) : 0u;
+    const uint64_t bhi = k < kWave ? clampi(i0 + k * s) : count;
+    if (bhi - blo <= (uint64_t)s) {
+      lo = blo;
+      hi = bhi;
+    }
+  }
   while (hi - lo > (uint64_t)kWave) {
     const uint64_t step = (hi - lo + kWave - 1) / kWave;
     const uint64_t idx = lo + (uint64_t)lane * step;

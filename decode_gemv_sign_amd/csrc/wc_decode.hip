@@ -31,7 +31,8 @@ struct DecodeArgs {
   const uint8_t* esc_sym;
   uint16_t* out;
   uint64_t n, n_esc, esc_last, raw_last, n_tiles, tiles_per_wave;
-  uint64_t sym_last;  // last dword of the symbol stream's padded extent
+  uint64_t sym_last;     // last dword of the symbol stream's padded extent
+  uint64_t guess_total;  // n: the cursor search starts with an interpolated probe; 0: it does not
   Dict dict;
 };
 
@@ -64,7 +65,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   const uint64_t full_tiles = a.n / kTile;
   const uint64_t f1 = t1 < full_tiles ? t1 : full_tiles;  // end of this wave's full tiles
   uint64_t e = 0;  // escape cursor, found once the first tile's loads are in flight
-  auto find_cursor = [&]() { e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile) : 0; };
+  auto find_cursor = [&]() {
+    e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile, a.guess_total) : 0;
+  };
 
   // Rebuild + escapes of tile t into out[16] (the lane's 4 groups); `stg` is
   // the tile's ring slot, free once the tile is in registers.  The tile's
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
 hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t* out,
                          hipStream_t s) {
   if (h.n == 0) return hipSuccess;
-  DecodeArgs a;
+  DecodeArgs a{};
   a.codes = container + h.off_codes;
   a.raw = container + h.off_raw;
   a.esc_pos = (const uint32_t*)(container + h.off_esc_pos);
@@ -291,7 +294,13 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   // waves the chip holds at once (3 or 4 per SIMD, LDS-bound) takes runs
   // that fill exactly one round instead.
   const uint64_t slots = (uint64_t)cu_count() * 4u * (deep ? 3u : 4u);
-  a.tiles_per_wave = a.n_tiles <= 3 * slots ? (a.n_tiles + slots - 1) / slots : kDecodeTilesPerWave;
+  const bool one_round = a.n_tiles <= 3 * slots;
+  a.tiles_per_wave = one_round ? (a.n_tiles + slots - 1) / slots : kDecodeTilesPerWave;
+  // In one round every wave's cursor search sits on the kernel's critical
+  // path: start it with an interpolated probe (two loads for evenly spread
+  // escapes instead of three).  Over several rounds the shared probes of the
+  // plain search hit L2, and a clustered stream costs the guess a round.
+  a.guess_total = one_round ? h.n : 0;
   const uint64_t waves = (a.n_tiles + a.tiles_per_wave - 1) / a.tiles_per_wave;
   const uint64_t wpb = kBlockThreads / kWave;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb));

@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   if (esc) {
     for (int rr = s; rr < kMRows; rr += S) {
       const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
-      const uint64_t e = wave_lower_bound(a.esc_pos, a.n_esc, t);
+      const uint64_t e = wave_lower_bound(a.esc_pos, a.n_esc, t, 0);
       if (lane == 0) erow0[rr] = e;
     }
   }

@@ -41,7 +41,8 @@ struct GemvArgs {
   const uint16_t* x;
   float* y;
   uint64_t rows, cols, n_esc, esc_last, raw_last, rows_per_wave;
-  uint64_t sym_last;  // last dword of the symbol stream's padded extent
+  uint64_t sym_last;     // last dword of the symbol stream's padded extent
+  uint64_t guess_total;  // rows * cols: cursor searches start with an interpolated probe; 0: not
   uint32_t batch;
   Dict dict;
 };
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   };
 
   auto init = [&](Slot& s0) {
-    e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
+    e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols, a.guess_total) : 0;
     s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
   };
   run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, init, load_tile, process);
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
   load_next(s0, x0);  // in flight during the cursor search
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols) : 0;
+  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols, a.guess_total) : 0;
   ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e, s0);
   TileCursor pc{r0, 0};
 
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_generic(GemvArgs 
   const uint64_t row_start = r * a.cols;
   const uint64_t n = a.rows * a.cols;
   const uint64_t raw_len = raw_bytes(LAYOUT, n);
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, row_start) : 0;
+  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, row_start, a.guess_total) : 0;
   float acc[WC_MAX_BATCH];
 #pragma unroll
   for (int b = 0; b < (int)WC_MAX_BATCH; ++b) acc[b] = 0.0f;
@@ -564,6 +565,10 @@ template <int LAYOUT>
 static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
   GemvArgs a = a0;
   a.rows_per_wave = rows_per_wave(a.cols);
+  // One round of waves (4 per SIMD): every cursor search is on the critical
+  // path, so it starts with an interpolated probe (as in the decode).
+  const uint64_t waves = (a.rows + a.rows_per_wave - 1) / a.rows_per_wave;
+  a.guess_total = waves <= (uint64_t)cu_count() * 16u ? a.rows * a.cols : 0;
   // Batch sizes 1, 2, 4, 8 and 16 have their own kernels; other sizes run as
   // a sum of those over consecutive slices of x and y.
   uint32_t done = 0;
@@ -607,7 +612,7 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
   }
   if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
     return launch_decode_gemm_mfma(h, container, rows, cols, x, batch, y, s);
-  GemvArgs a;
+  GemvArgs a{};
   a.codes = container + h.off_codes;
   a.raw = container + h.off_raw;
   a.esc_pos = (const uint32_t*)(container + h.off_esc_pos);
