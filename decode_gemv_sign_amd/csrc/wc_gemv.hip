@@ -550,9 +550,14 @@ static dim3 row_grid(uint64_t rows) {
 #ifndef WC_GEMV_MIN_TILES
 #define WC_GEMV_MIN_TILES 4
 #endif
-static uint64_t rows_per_wave(uint64_t cols) {
+static uint64_t rows_per_wave(uint64_t rows, uint64_t cols) {
   const uint64_t tpr = (cols + kTile - 1) / kTile;
-  return tpr >= WC_GEMV_MIN_TILES ? 1 : (WC_GEMV_MIN_TILES + tpr - 1) / tpr;
+  const uint64_t rpw = tpr >= WC_GEMV_MIN_TILES ? 1 : (WC_GEMV_MIN_TILES + tpr - 1) / tpr;
+  // Less than one round of waves (4 per SIMD): spread the rows over one
+  // round instead, as few per wave as fill it.
+  const uint64_t slots = (uint64_t)cu_count() * 16u;
+  if ((rows + rpw - 1) / rpw < slots) return rows > slots ? (rows + slots - 1) / slots : 1;
+  return rpw;
 }
 
 static dim3 wave_grid(uint64_t rows, uint64_t rpw) {
@@ -564,7 +569,7 @@ static dim3 wave_grid(uint64_t rows, uint64_t rpw) {
 template <int LAYOUT>
 static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
   GemvArgs a = a0;
-  a.rows_per_wave = rows_per_wave(a.cols);
+  a.rows_per_wave = rows_per_wave(a.rows, a.cols);
   // One round of waves (4 per SIMD): every cursor search is on the critical
   // path, so it starts with an interpolated probe (as in the decode).
   const uint64_t waves = (a.rows + a.rows_per_wave - 1) / a.rows_per_wave;
@@ -670,7 +675,7 @@ hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, con
     hipLaunchKernelGGL(k_gemv_bf16_generic, row_grid(rows), dim3(kBlockThreads), 0, s, a);
     return hipGetLastError();
   }
-  a.rows_per_wave = rows_per_wave(cols);
+  a.rows_per_wave = rows_per_wave(rows, cols);
   uint32_t done = 0;
   while (done < batch) {
     const uint32_t left = batch - done;
