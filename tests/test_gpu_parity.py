@@ -211,6 +211,26 @@ def test_gemv_escape_dense(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
+def test_clustered_escapes_small(layout):
+    """A band of escape-dense rows in a tensor small enough to run as one
+    round of waves: cursor searches that start with an interpolated probe
+    land far from the band's records and take the full-range search."""
+    rows, cols = 1024, 4096
+    w = synth.random_bits(rows * cols, 903, "normal").reshape(rows, cols)
+    band = synth.random_bits(96 * cols, 904, "uniform").reshape(96, cols) & np.uint16(0xBFFF)
+    w[700:796] = band
+    x = synth.vectors(905, 4, cols)
+    h, c = check_roundtrip(layout, w, "clustered escapes")
+    # most escapes are in the band
+    d, nd, _ = oracle.dictionary(layout, oracle.histogram(layout, w), w.size)
+    sym = w >> (7 if layout == wc.K15 else 8)
+    esc = ~np.isin(sym, d[:nd])
+    assert esc[700:796].sum() > 0.8 * esc.sum() and h.n_esc == esc.sum()
+    check_gemv(layout, w, x, h, c, "clustered escapes")
+    check_gemv(layout, w, x[:1], h, c, "clustered escapes, batch 1")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 def test_gemv_every_batch(layout):
     """Batches 1..16 on shapes with a ragged 16-row block and a partial last
     128-column chunk, and on rows of whole 2048-weight tiles (the LDS-ring
