@@ -145,7 +145,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the codec shards per tensor with no exchange; see DESIGN.md)", file=sys.stderr)
+              f"(the codec shards per tensor with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

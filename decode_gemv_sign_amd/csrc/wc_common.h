@@ -45,16 +45,10 @@ __host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_
 }
 
 // Dictionary as kernel argument: symbol per code, slot 15 (escape) = 0, so a
-// rebuilt escape holds only its raw bits until it is patched.  `hi` holds the
-// byte each code puts in a weight's high byte (the symbol for byte-split, the
-// symbol's top 8 bits for K15), `lo` (K15) the byte each code puts in the low
-// byte (0x80 when the symbol's lowest bit, exponent bit 0, is set), both
-// packed 4 codes per dword, code c in byte c % 4 of dword c / 4.
+// rebuilt escape holds only its raw bits until it is patched.
 struct Dict {
   uint16_t sym[16];
   uint32_t n_dict;
-  uint32_t hi[4];
-  uint32_t lo[4];
 };
 
 // ---- wave primitives -----------------------------------------------------
@@ -226,14 +220,6 @@ inline Dict dict_of(const wc_header* h) {
   Dict d;
   for (int k = 0; k < 16; ++k) d.sym[k] = (k < h->n_dict && k < 15) ? h->dict[k] : 0;
   d.n_dict = h->n_dict;
-  for (int q = 0; q < 4; ++q) d.hi[q] = d.lo[q] = 0;
-  for (int k = 0; k < 16; ++k) {
-    const uint32_t s = d.sym[k];
-    const uint32_t hb = h->layout == WC_LAYOUT_K15 ? s >> 1 : s;
-    const uint32_t lb = h->layout == WC_LAYOUT_K15 ? (s & 1u) << 7 : 0u;
-    d.hi[k / 4] |= (hb & 0xFFu) << (8 * (k % 4));
-    d.lo[k / 4] |= lb << (8 * (k % 4));
-  }
   return d;
 }
 

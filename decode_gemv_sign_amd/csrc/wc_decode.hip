@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     const bool ahead = issue_next(e + cnt_wave, [&]() {
       if (dense) off0 = ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg);
     });
-    rebuild_lane<LAYOUT>(T2, a.dict, l, out);
+    rebuild_lane<LAYOUT>(T2, l, out);
     if (dense) {
       if (ahead) wait_vm<kRingAhead>();  // the symbol run is complete (ring_wait_ahead)
       else wait_vm<0>();

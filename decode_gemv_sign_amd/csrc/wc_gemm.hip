@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
               lr.raw[m][1] = cur.wr[2 * m + 1];
             }
           }
-          rebuild_lane<LAYOUT>(T2, a.dict, lr, wv);
+          rebuild_lane<LAYOUT>(T2, lr, wv);
           uint32_t* st = stage[s];
           uint32_t* wl = win[s] + lane * kWinDwords;
           if (cnt != 0) {
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
             lr.raw[m][1] = cur.wr[2 * m + 1];
           }
         }
-        rebuild_lane<LAYOUT>(T2, a.dict, lr, wv);
+        rebuild_lane<LAYOUT>(T2, lr, wv);
       }
     }
     // Operands of blocks past the row end are zeroed with masks rather than

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     // the next tile's first records, in flight while this tile is rebuilt
     sn.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave);
     uint32_t w[16];
-    rebuild_lane<LAYOUT>(T2, a.dict, s.l, w);
+    rebuild_lane<LAYOUT>(T2, s.l, w);
     if (cnt_wave > kDenseMin) {
       patch_tile_windows<LAYOUT>(s.l, w, a.esc_sym, a.sym_last, e);
     } else if (cnt_wave) {
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     const bool dense = cnt_wave > kDenseMin;
     const uint32_t off0 = dense ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
     uint32_t w[16];
-    rebuild_lane<LAYOUT>(T2, a.dict, l, w);
+    rebuild_lane<LAYOUT>(T2, l, w);
     if (dense) {
       wait_vm<0>();
       patch_tile_symrun<LAYOUT>(l, w, buf, off0);

@@ -102,54 +102,6 @@ __device__ inline void load_group(const GroupBase& b, uint32_t lg, uint32_t& c, 
   }
 }
 
-#ifndef WC_REBUILD_VALU
-#define WC_REBUILD_VALU 0
-#endif
-
-// Four codes (one per byte, 0..15) -> the four bytes `tab` holds for them.
-// v_perm_b32 picks bytes 0-7 of a register pair by a 3-bit selector, so
-// codes 0-7 and 8-15 are looked up separately and merged per byte on code
-// bit 3 (selector 12 gives 0x00 and 13 gives 0xFF, which builds the mask).
-__device__ inline uint32_t lookup4(const uint32_t tab[4], uint32_t sel, uint32_t mask) {
-  const uint32_t a = __builtin_amdgcn_perm(tab[1], tab[0], sel);
-  const uint32_t b = __builtin_amdgcn_perm(tab[3], tab[2], sel);
-  return (b & mask) | (a & ~mask);
-}
-
-__device__ inline void sel_mask(uint32_t c4, uint32_t& sel, uint32_t& mask) {
-  sel = c4 & 0x07070707u;
-  mask = __builtin_amdgcn_perm(0u, 0u, ((c4 >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
-}
-
-// Rebuild one group from registers only: the dictionary bytes come from the
-// kernel arguments (SGPRs), no LDS table.
-template <int LAYOUT>
-__device__ inline void rebuild_group_valu(const Dict& d, uint32_t c, const uint32_t r[2],
-                                          uint32_t out[4]) {
-  const uint32_t ev = c & 0x0F0F0F0Fu;         // codes of weights 0, 2, 4, 6
-  const uint32_t od = (c >> 4) & 0x0F0F0F0Fu;  // codes of weights 1, 3, 5, 7
-  const uint32_t c03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // codes 0..3 in bytes
-  const uint32_t c47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // codes 4..7
-  uint32_t s0, m0, s1, m1;
-  sel_mask(c03, s0, m0);
-  sel_mask(c47, s1, m1);
-  const uint32_t h03 = lookup4(d.hi, s0, m0), h47 = lookup4(d.hi, s1, m1);
-  if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
-    // [low(2j), high(2j), low(2j+1), high(2j+1)]
-    out[0] = __builtin_amdgcn_perm(h03, r[0], 0x05010400u);
-    out[1] = __builtin_amdgcn_perm(h03, r[0], 0x07030602u);
-    out[2] = __builtin_amdgcn_perm(h47, r[1], 0x05010400u);
-    out[3] = __builtin_amdgcn_perm(h47, r[1], 0x07030602u);
-  } else {
-    const uint32_t l03 = lookup4(d.lo, s0, m0), l47 = lookup4(d.lo, s1, m1);
-    const uint32_t f[4] = {r[0], r[0] >> 14, __builtin_amdgcn_alignbit(r[1], r[0], 28), r[1] >> 10};
-    out[0] = __builtin_amdgcn_perm(h03, l03, 0x05010400u) | (f[0] & 0x7Fu) | ((f[0] << 9) & 0x007F0000u);
-    out[1] = __builtin_amdgcn_perm(h03, l03, 0x07030602u) | (f[1] & 0x7Fu) | ((f[1] << 9) & 0x007F0000u);
-    out[2] = __builtin_amdgcn_perm(h47, l47, 0x05010400u) | (f[2] & 0x7Fu) | ((f[2] << 9) & 0x007F0000u);
-    out[3] = __builtin_amdgcn_perm(h47, l47, 0x07030602u) | (f[3] & 0x7Fu) | ((f[3] << 9) & 0x007F0000u);
-  }
-}
-
 // Rebuild one group into out[4] (escapes carry a zero symbol).
 template <int LAYOUT>
 __device__ inline void rebuild_group(const uint32_t* __restrict__ T2, uint32_t c, const uint32_t r[2],
@@ -173,16 +125,10 @@ __device__ inline void rebuild_group(const uint32_t* __restrict__ T2, uint32_t c
 }
 
 template <int LAYOUT>
-__device__ inline void rebuild_lane(const uint32_t* __restrict__ T2, const Dict& d, const Lane4& l,
+__device__ inline void rebuild_lane(const uint32_t* __restrict__ T2, const Lane4& l,
                                     uint32_t out[16]) {
 #pragma unroll
-  for (int k = 0; k < kLaneGroups; ++k) {
-#if WC_REBUILD_VALU
-    rebuild_group_valu<LAYOUT>(d, l.codes[k], l.raw[k], out + 4 * k);
-#else
-    rebuild_group<LAYOUT>(T2, l.codes[k], l.raw[k], out + 4 * k);
-#endif
-  }
+  for (int k = 0; k < kLaneGroups; ++k) rebuild_group<LAYOUT>(T2, l.codes[k], l.raw[k], out + 4 * k);
 }
 
 // Code-15 (escape) marks of the lane's groups: bit 4i + 3 of esc[k] is set
