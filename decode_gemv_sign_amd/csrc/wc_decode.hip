@@ -8,9 +8,10 @@
 // HBM-bound: per weight it reads bpw/8 bytes of container and writes 2 bytes.
 // Each wave owns a contiguous run of 2048-weight tiles, so the escape cursor
 // is found once per wave (one 64-ary search of the position stream) and then
-// advanced by each tile's code-15 count.  Tiles without escapes (a wave-wide
-// ballot) store straight from registers with 16-byte non-temporal stores;
-// tiles with escapes are patched in LDS first (wc_tile.h).
+// advanced by each tile's code-15 count.  Tiles stream through a per-wave
+// LDS ring filled by global->LDS loads and are rebuilt in registers; tiles
+// with escapes are patched (wc_tile.h), and every tile is stored with
+// 16-byte non-temporal stores.
 #include <type_traits>
 
 #include "wc_launch.h"
@@ -48,7 +49,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   constexpr int kWpb = kBlockThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint32_t ring0[kWpb][kRingSlotDwords];
   __shared__ __attribute__((aligned(16))) uint32_t ring1[kWpb][kRingSlotDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t ring2[DEPTH == 2 ? kWpb : 1][DEPTH == 2 ? kRingSlotDwords : 4];
+  constexpr int kSlot2 = DEPTH == 2 ? kRingSlotDwords : 4;  // the third slot (DEPTH 2 only)
+  __shared__ __attribute__((aligned(16))) uint32_t ring2[DEPTH == 2 ? kWpb : 1][kSlot2];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 

@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   // rebuilt weights of lanes with escapes (16 dwords per lane); the final sums
   __shared__ __attribute__((aligned(16))) uint32_t stage[S][kWave * (PLAIN ? 4 : 16)];
   __shared__ uint32_t win[PLAIN ? 1 : S][PLAIN ? 1 : kWave * kWinDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t xcnt[2][kMRows][S];  // escapes per row in each wave's chunk
+  // escapes per row in each wave's chunk
+  __shared__ __attribute__((aligned(16))) uint32_t xcnt[2][kMRows][S];
   __shared__ uint64_t erow0[kMRows];
   if constexpr (!PLAIN) build_pair_table<LAYOUT>(T2, a.dict);
 

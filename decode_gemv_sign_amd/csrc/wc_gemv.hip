@@ -15,7 +15,10 @@
 // multiplies them with the matching x values by v_dot2_f32_bf16 (exact BF16
 // products, fp32 accumulate), and at the row's end the 64 lane partials are
 // summed by butterfly shuffles.  HBM-bound at batch 1 and 4: per weight bpw/8
-// bytes of container are read (x stays in L2).
+// bytes of container are read (x stays in L2).  Rows made of whole tiles at
+// batch <= 4 stream through an LDS ring (k_decode_gemv_ring); other shapes
+// use a register ring (k_decode_gemv); batches of 8 and more go to the
+// matrix-core kernel (wc_gemm.hip) when the shape fits it.
 //
 // Rows whose length is not a multiple of 8 (a group would straddle two rows)
 // take the generic kernels at the end of this file: one weight per lane per
@@ -100,8 +103,9 @@ struct TileCursor {
 
 // Software pipeline over nq tiles with a ring of D register slots: tile q+D-1
 // is loaded just before tile q is processed.  init(slot 0) runs once the
-// first tiles' loads are issued (it may wait on memory of its own).  The ring is unrolled, so every
-// slot index is static (no register copies, which would wait on the loads),
+// first tiles' loads are issued (it may wait on memory of its own).  The
+// ring is unrolled, so every slot index is static (no register copies,
+// which would wait on the loads),
 // and loads past the end re-read the last tile (their data is unused), so the
 // loads in flight are the same on every path.  process(cursor, slot, next)
 // may also fill fields of the next tile's slot that the load does not touch

@@ -246,7 +246,8 @@ __device__ inline void stage_load(const uint32_t* __restrict__ stage, uint32_t o
   for (int k = 0; k < kLaneGroups; ++k) {
     if ((gmask >> k) & 1u) {
       u32x4 v;
-      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(base + 1024u * k) : "memory");
+      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(v) : "v"(base + 1024u * k) : "memory");
       out[4 * k] = v[0]; out[4 * k + 1] = v[1]; out[4 * k + 2] = v[2]; out[4 * k + 3] = v[3];
     }
   }
