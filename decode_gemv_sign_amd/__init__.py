@@ -50,7 +50,7 @@ class Header(ctypes.Structure):
         ("dict", ctypes.c_uint16 * 16), ("off_codes", ctypes.c_uint64),
         ("off_raw", ctypes.c_uint64), ("off_esc_pos", ctypes.c_uint64),
         ("off_esc_sym", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
-        ("reserved", ctypes.c_uint8 * 32),
+        ("off_esc_idx", ctypes.c_uint64), ("reserved", ctypes.c_uint8 * 24),
     ]
 
     def to_bytes(self) -> bytes:

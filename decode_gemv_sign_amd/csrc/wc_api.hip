@@ -53,6 +53,7 @@ extern "C" int wc_build_dict(int layout, const uint16_t* d_w, uint64_t n, void* 
   h.off_raw = g.off_raw;
   h.off_esc_pos = g.off_esc_pos;
   h.off_esc_sym = g.off_esc_sym;
+  h.off_esc_idx = g.off_esc_idx;
   h.total_bytes = g.total;
   *h_out = h;
   return WC_OK;
@@ -110,7 +111,7 @@ extern "C" int wc_bits_per_weight(const wc_header* h, double* bpw, double* paylo
   if (v != WC_OK) return v;
   if (h->n == 0) return WC_E_ARG;
   const uint64_t payload = (h->n + 1u) / 2u + wc::raw_bytes(h->layout, h->n) + 4u * h->n_esc +
-                           wc::sym_bytes(h->layout) * h->n_esc;
+                           wc::sym_bytes(h->layout) * h->n_esc + 4u * wc::index_entries(h->n, h->n_esc);
   *bpw = 8.0 * (double)h->total_bytes / (double)h->n;
   *payload_bpw = 8.0 * (double)payload / (double)h->n;
   return WC_OK;

@@ -30,8 +30,14 @@ __host__ __device__ inline uint64_t raw_bytes(int layout, uint64_t n) {
 }
 __host__ __device__ inline uint64_t sym_bytes(int layout) { return layout == WC_LAYOUT_K15 ? 2u : 1u; }
 
+// Escape-index entries: one per WC_INDEX_TILE-weight tile start plus the
+// closing one, none without escapes.
+__host__ __device__ inline uint64_t index_entries(uint64_t n, uint64_t n_esc) {
+  return n_esc ? (n + WC_INDEX_TILE - 1u) / WC_INDEX_TILE + 1u : 0u;
+}
+
 struct Geometry {
-  uint64_t off_codes, off_raw, off_esc_pos, off_esc_sym, total;
+  uint64_t off_codes, off_raw, off_esc_pos, off_esc_sym, off_esc_idx, total;
 };
 
 __host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_esc) {
@@ -40,7 +46,8 @@ __host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_
   g.off_raw = pad16(g.off_codes + (n + 1u) / 2u);
   g.off_esc_pos = pad16(g.off_raw + raw_bytes(layout, n));
   g.off_esc_sym = pad16(g.off_esc_pos + 4u * n_esc);
-  g.total = pad16(g.off_esc_sym + sym_bytes(layout) * n_esc);
+  g.off_esc_idx = pad16(g.off_esc_sym + sym_bytes(layout) * n_esc);
+  g.total = pad16(g.off_esc_idx + 4u * index_entries(n, n_esc));
   return g;
 }
 
@@ -109,43 +116,13 @@ __device__ inline uint32_t wave_total(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
-// First index i in [0, count) with pos[i] >= t (count if none), found by the
+// First index i in [lo, hi) with pos[i] >= t (hi if none), found by the
 // whole wave: each round probes 64 entries and keeps the one interval that
-// can hold the answer.  The first round probes around where t would fall if
-// the count entries were spread evenly over positions [0, total) (skipped
-// when total is 0): 64 probes
-// at a stride of about sqrt(count) / 21 (some three standard deviations of a
-// uniform spread on either side), on multiples of the stride so that waves
-// with nearby targets share the probed lines.  If they bracket the answer
-// within one stride the search goes on there; otherwise (a clustered stream)
-// it starts over on the whole array, whose first rounds probe entries that
-// every wave shares.  Every round shrinks the interval, so it ends even on an
-// unsorted (corrupt) array.  Result is wave-uniform.
-__device__ inline uint64_t wave_lower_bound(const uint32_t* __restrict__ pos, uint64_t count,
-                                            uint64_t t, uint64_t total) {
+// can hold the answer.  Every round shrinks the interval, so it ends even on
+// an unsorted (corrupt) array.  Result is wave-uniform.
+__device__ inline uint64_t wave_lower_bound(const uint32_t* __restrict__ pos, uint64_t lo,
+                                            uint64_t hi, uint64_t t) {
   const int lane = lane_id();
-  uint64_t lo = 0, hi = count;
-  if (count > 4 * (uint64_t)kWave && total > 0) {
-    const double f = (double)t / (double)total;
-    const int64_t g = (int64_t)((double)count * (f < 1.0 ? f : 1.0));
-    const int64_t s = (int64_t)(__builtin_sqrt((double)count) * (1.0 / 21.0)) + 1;
-    const int64_t i0 = (g / s - (int64_t)(kWave / 2)) * s;  // lane 0's probe
-    const int64_t idx = i0 + (int64_t)lane * s;
-    // outside the array: below before its start, not below past its end
-    const bool below = idx < 0 || (idx < (int64_t)count && (uint64_t)pos[idx] < t);
-    const int64_t k = (int64_t)__popcll(__ballot(below));
-    auto clampi = [&](int64_t v) -> uint64_t {
-      return v < 0 ? 0u : ((uint64_t)v > count ? count : (uint64_t)v);
-    };
-    // lane k - 1 is below (the answer is past its probe), lane k is not (the
-    // answer is at most its probe)
-    const uint64_t blo = k > 0 ? clampi(i0 + (k - 1) * s + 1) : 0u;
-    const uint64_t bhi = k < kWave ? clampi(i0 + k * s) : count;
-    if (bhi - blo <= (uint64_t)s) {
-      lo = blo;
-      hi = bhi;
-    }
-  }
   while (hi - lo > (uint64_t)kWave) {
     const uint64_t step = (hi - lo + kWave - 1) / kWave;
     const uint64_t idx = lo + (uint64_t)lane * step;
@@ -160,6 +137,25 @@ __device__ inline uint64_t wave_lower_bound(const uint32_t* __restrict__ pos, ui
   const uint64_t idx = lo + (uint64_t)lane;
   const bool below = idx < hi && (uint64_t)pos[idx] < t;
   return lo + (uint64_t)__popcll(__ballot(below));
+}
+
+// The first escape record at or after weight t (count if none) of a tensor
+// of n weights with `count` records.  The escape index holds the answer for
+// every multiple of WC_INDEX_TILE, so a tile start costs one load; any other
+// t is searched for among the records of its index tile only.  Entries are
+// clamped to [0, count] and to each other, so a corrupt index still gives a
+// cursor in range.  Wave-uniform.
+__device__ inline uint64_t escape_cursor(const uint32_t* __restrict__ idx,
+                                         const uint32_t* __restrict__ pos, uint64_t count,
+                                         uint64_t n, uint64_t t) {
+  if (count == 0 || t >= n) return count;
+  const uint64_t j = t / WC_INDEX_TILE;
+  uint64_t lo = idx[j];
+  lo = lo < count ? lo : count;
+  if (t % WC_INDEX_TILE == 0) return lo;
+  uint64_t hi = idx[j + 1];
+  hi = hi < lo ? lo : (hi > count ? count : hi);
+  return wave_lower_bound(pos, lo, hi, t);
 }
 
 // ---- global -> LDS loads and explicit waits --------------------------------
@@ -209,9 +205,9 @@ inline int validate_header(const wc_header* h) {
   }
   const Geometry g = geometry(h->layout, h->n, h->n_esc);
   if (h->off_codes != g.off_codes || h->off_raw != g.off_raw || h->off_esc_pos != g.off_esc_pos ||
-      h->off_esc_sym != g.off_esc_sym || h->total_bytes != g.total)
+      h->off_esc_sym != g.off_esc_sym || h->off_esc_idx != g.off_esc_idx || h->total_bytes != g.total)
     return WC_E_CORRUPT;
-  for (int k = 0; k < 32; ++k)
+  for (int k = 0; k < 24; ++k)
     if (h->reserved[k] != 0) return WC_E_CORRUPT;
   return WC_OK;
 }

@@ -7,7 +7,7 @@
 //
 // HBM-bound: per weight it reads bpw/8 bytes of container and writes 2 bytes.
 // Each wave owns a contiguous run of 2048-weight tiles, so the escape cursor
-// is found once per wave (one 64-ary search of the position stream) and then
+// is read once per wave (the escape index entry of its first tile) and then
 // advanced by each tile's code-15 count.  Tiles stream through a per-wave
 // LDS ring filled by global->LDS loads and are rebuilt in registers; tiles
 // with escapes are patched (wc_tile.h), and every tile is stored with
@@ -30,10 +30,10 @@ struct DecodeArgs {
   const uint8_t* raw;
   const uint32_t* esc_pos;
   const uint8_t* esc_sym;
+  const uint32_t* esc_idx;
   uint16_t* out;
   uint64_t n, n_esc, esc_last, raw_last, n_tiles, tiles_per_wave;
-  uint64_t sym_last;     // last dword of the symbol stream's padded extent
-  uint64_t guess_total;  // n: the cursor search starts with an interpolated probe; 0: it does not
+  uint64_t sym_last;  // last dword of the symbol stream's padded extent
   Dict dict;
 };
 
@@ -66,10 +66,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   // patched and stored.
   const uint64_t full_tiles = a.n / kTile;
   const uint64_t f1 = t1 < full_tiles ? t1 : full_tiles;  // end of this wave's full tiles
-  uint64_t e = 0;  // escape cursor, found once the first tile's loads are in flight
-  auto find_cursor = [&]() {
-    e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, t0 * kTile, a.guess_total) : 0;
-  };
+  uint64_t e = 0;  // escape cursor, read once the first tile's loads are in flight
+  auto find_cursor = [&]() { e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.n, t0 * kTile); };
 
   // Rebuild + escapes of tile t into out[16] (the lane's 4 groups); `stg` is
   // the tile's ring slot, free once the tile is in registers.  The tile's
@@ -129,7 +127,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         constexpr int k = decltype(slc)::value % 3;
         return k == 0 ? s0 : (k == 1 ? s1 : s2);
       };
-      dma_tile(t0, s0);  // in flight during the cursor search
+      dma_tile(t0, s0);  // in flight while the escape cursor is read
       find_cursor();
       dma_eb(e, s0);
       if (t0 + 1 < f1) dma_tile(t0 + 1, s1);
@@ -173,7 +171,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
       auto slot_buf = [&](auto slc) -> uint32_t* {
         return decltype(slc)::value % 2 == 0 ? s0 : s1;
       };
-      dma_tile(t0, s0);  // in flight during the cursor search
+      dma_tile(t0, s0);  // in flight while the escape cursor is read
       find_cursor();
       dma_eb(e, s0);
       uint64_t t = t0;
@@ -274,17 +272,19 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   a.raw = container + h.off_raw;
   a.esc_pos = (const uint32_t*)(container + h.off_esc_pos);
   a.esc_sym = container + h.off_esc_sym;
+  a.esc_idx = (const uint32_t*)(container + h.off_esc_idx);
   a.out = out;
   a.n = h.n;
   a.n_esc = h.n_esc;
   // with no escapes, the (never used) escape loads read the container header
   a.esc_last = h.n_esc ? h.n_esc - 1 : 0;
+  a.sym_last = h.n_esc ? (h.off_esc_idx - h.off_esc_sym) / 4 - 1 : 0;
   if (h.n_esc == 0) {
     a.esc_pos = (const uint32_t*)container;
     a.esc_sym = container;
+    a.esc_idx = (const uint32_t*)container;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
-  a.sym_last = (h.total_bytes - h.off_esc_sym) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;
   // Two tiles ahead, except for escape-heavy tensors (more than one weight
   // in 8 escapes): their dense tiles wait for their symbol run, and the
@@ -298,11 +298,6 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   const uint64_t slots = (uint64_t)cu_count() * 4u * (deep ? 3u : 4u);
   const bool one_round = a.n_tiles <= 3 * slots;
   a.tiles_per_wave = one_round ? (a.n_tiles + slots - 1) / slots : kDecodeTilesPerWave;
-  // In one round every wave's cursor search sits on the kernel's critical
-  // path: start it with an interpolated probe (two loads for evenly spread
-  // escapes instead of three).  Over several rounds the shared probes of the
-  // plain search hit L2, and a clustered stream costs the guess a round.
-  a.guess_total = one_round ? h.n : 0;
   const uint64_t waves = (a.n_tiles + a.tiles_per_wave - 1) / a.tiles_per_wave;
   const uint64_t wpb = kBlockThreads / kWave;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb));

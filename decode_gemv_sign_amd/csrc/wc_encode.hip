@@ -14,7 +14,8 @@
 //               symbol asc) -> 48-byte result copied to the host.
 //   encode:     k_pack (codes, raw stream, per-block escape counts, header and
 //               zero gaps) -> k_scan (exclusive scan of the block counts) ->
-//               k_emit (escape positions and symbols in weight order).
+//               k_emit (escape positions and symbols in weight order, and the
+//               escape index: the records before each 2048-weight tile).
 // Every output byte is a pure function of the input, so the container is
 // byte-identical from run to run.
 #include "wc_launch.h"
@@ -293,7 +294,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
       const uint64_t pe = h.off_esc_pos + 4u * h.n_esc;
       for (uint64_t o = pe; o < h.off_esc_sym; ++o) a.container[o] = 0;
       const uint64_t se = h.off_esc_sym + sym_bytes(LAYOUT) * h.n_esc;
-      for (uint64_t o = se; o < h.total_bytes; ++o) a.container[o] = 0;
+      for (uint64_t o = se; o < h.off_esc_idx; ++o) a.container[o] = 0;
+      const uint64_t ie = h.off_esc_idx + 4u * index_entries(h.n, h.n_esc);
+      for (uint64_t o = ie; o < h.total_bytes; ++o) a.container[o] = 0;
     }
   }
 }
@@ -332,11 +335,22 @@ struct EmitArgs {
   wc_header h;
 };
 
+// Block b covers weights [8192 b, 8192 b + 8192): wave q of it covers exactly
+// the 2048-weight tile 4 b + q, so the wave's first record number is that
+// tile's escape-index entry.
 template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
+  static_assert(kTile == (int)WC_INDEX_TILE && kPackBlock == 4 * kTile, "one index tile per wave");
   __shared__ uint32_t wtot[kBlockThreads / kWave];
-  if (a.blk_cnt[blockIdx.x] == 0) return;  // whole block: no escapes
   const int tid = threadIdx.x;
+  uint32_t* const index = (uint32_t*)(a.container + a.h.off_esc_idx);
+  const uint64_t n_tiles = (a.n + kTile - 1) / kTile;
+  const uint64_t my_tile = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)(tid / kWave);
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) index[n_tiles] = (uint32_t)a.h.n_esc;  // closing entry
+  if (a.blk_cnt[blockIdx.x] == 0) {  // whole block: no escapes
+    if ((tid & (kWave - 1)) == 0 && my_tile < n_tiles) index[my_tile] = a.blk_off[blockIdx.x];
+    return;
+  }
   const uint64_t chunk = (uint64_t)blockIdx.x * kBlockThreads + (uint64_t)tid;
   const uint64_t base = chunk * kChunk;
   uint32_t mask = 0;  // bit i: weight base+i escapes
@@ -356,6 +370,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
   uint32_t wbase = 0;
   for (int q = 0; q < tid / kWave; ++q) wbase += wtot[q];
   uint64_t o = (uint64_t)a.blk_off[blockIdx.x] + wbase + ex;
+  if (lane_id() == 0 && my_tile < n_tiles) index[my_tile] = (uint32_t)o;  // ex == 0 in lane 0
   uint32_t* pos = (uint32_t*)(a.container + a.h.off_esc_pos);
   uint8_t* sym = a.container + a.h.off_esc_sym;
   while (mask) {

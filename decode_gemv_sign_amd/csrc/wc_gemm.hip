@@ -29,8 +29,9 @@
 // waves swap these counts through LDS; every lane then knows the first record
 // of its own weights (row cursor + counts of the chunks and lanes to its
 // left), loads the symbols of its run as one window and writes them into the
-// placeholders of its rebuilt weights.  The row cursors start from one
-// search of the position stream per row.
+// placeholders of its rebuilt weights.  The row cursors start from the
+// escape index: one load for a row that starts on a 2048-weight boundary,
+// else a search of the records of the row start's index tile.
 #include "wc_launch.h"
 #include "wc_tile.h"
 
@@ -51,6 +52,7 @@ struct GemmArgs {
   const uint8_t* raw;
   const uint32_t* esc_pos;
   const uint8_t* esc_sym;
+  const uint32_t* esc_idx;
   const uint16_t* w;  // plain BF16 weights (comparator)
   const uint16_t* x;
   float* y;
@@ -350,12 +352,12 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   // compiler wait for the prefetch at the loop head).
   f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
   Slot s0, s1;
-  load(0, s0);  // in flight during the cursor searches
+  load(0, s0);  // in flight while the row cursors are read
   // Row cursors: first record at or after each row's start.
   if (esc) {
     for (int rr = s; rr < kMRows; rr += S) {
       const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
-      const uint64_t e = wave_lower_bound(a.esc_pos, a.n_esc, t, 0);
+      const uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, t);
       if (lane == 0) erow0[rr] = e;
     }
   }
@@ -429,9 +431,10 @@ hipError_t launch_decode_gemm_mfma(const wc_header& h, const uint8_t* container,
   a.raw = container + h.off_raw;
   a.esc_pos = (const uint32_t*)(container + h.off_esc_pos);
   a.esc_sym = container + h.off_esc_sym;
+  a.esc_idx = (const uint32_t*)(container + h.off_esc_idx);
   a.n_esc = h.n_esc;
-  // last dword of the symbol stream's 16-byte padded extent (the container's end)
-  a.sym_last = (h.total_bytes - h.off_esc_sym) / 4 - 1;
+  // last dword of the symbol stream's 16-byte padded extent (unused without escapes)
+  a.sym_last = h.n_esc ? (h.off_esc_idx - h.off_esc_sym) / 4 - 1 : 0;
   a.dict = dict_of(&h);
   if (h.layout == WC_LAYOUT_K15)
     launch_mfma<WC_LAYOUT_K15, false>(a, s);

@@ -40,12 +40,12 @@ struct GemvArgs {
   const uint8_t* raw;
   const uint32_t* esc_pos;
   const uint8_t* esc_sym;
+  const uint32_t* esc_idx;
   const uint16_t* w;  // plain BF16 weights (comparator)
   const uint16_t* x;
   float* y;
   uint64_t rows, cols, n_esc, esc_last, raw_last, rows_per_wave;
-  uint64_t sym_last;     // last dword of the symbol stream's padded extent
-  uint64_t guess_total;  // rows * cols: cursor searches start with an interpolated probe; 0: not
+  uint64_t sym_last;  // last dword of the symbol stream's padded extent
   uint32_t batch;
   Dict dict;
 };
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   };
 
   auto init = [&](Slot& s0) {
-    e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols, a.guess_total) : 0;
+    e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, r0 * a.cols);
     s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
   };
   run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, init, load_tile, process);
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
-  load_next(s0, x0);  // in flight during the cursor search
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, r0 * a.cols, a.guess_total) : 0;
+  load_next(s0, x0);  // in flight while the escape cursor is read
+  uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, r0 * a.cols);
   ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e, s0);
   TileCursor pc{r0, 0};
 
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_generic(GemvArgs 
   const uint64_t row_start = r * a.cols;
   const uint64_t n = a.rows * a.cols;
   const uint64_t raw_len = raw_bytes(LAYOUT, n);
-  uint64_t e = a.n_esc ? wave_lower_bound(a.esc_pos, a.n_esc, row_start, a.guess_total) : 0;
+  uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, n, row_start);
   float acc[WC_MAX_BATCH];
 #pragma unroll
   for (int b = 0; b < (int)WC_MAX_BATCH; ++b) acc[b] = 0.0f;
@@ -549,8 +549,9 @@ static dim3 row_grid(uint64_t rows) {
   return dim3((unsigned)((rows + wpb - 1) / wpb));
 }
 
-// Rows per wave: enough tiles per wave (about 4) to amortise the escape
-// cursor search, while leaving many waves for the scheduler to balance.
+// Rows per wave: enough tiles per wave (about 4) to amortise each wave's
+// start (escape cursor, first loads), while leaving many waves for the
+// scheduler to balance.
 #ifndef WC_GEMV_MIN_TILES
 #define WC_GEMV_MIN_TILES 4
 #endif
@@ -574,10 +575,6 @@ template <int LAYOUT>
 static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
   GemvArgs a = a0;
   a.rows_per_wave = rows_per_wave(a.rows, a.cols);
-  // One round of waves (4 per SIMD): every cursor search is on the critical
-  // path, so it starts with an interpolated probe (as in the decode).
-  const uint64_t waves = (a.rows + a.rows_per_wave - 1) / a.rows_per_wave;
-  a.guess_total = waves <= (uint64_t)cu_count() * 16u ? a.rows * a.cols : 0;
   // Batch sizes 1, 2, 4, 8 and 16 have their own kernels; other sizes run as
   // a sum of those over consecutive slices of x and y.
   uint32_t done = 0;
@@ -626,6 +623,7 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
   a.raw = container + h.off_raw;
   a.esc_pos = (const uint32_t*)(container + h.off_esc_pos);
   a.esc_sym = container + h.off_esc_sym;
+  a.esc_idx = (const uint32_t*)(container + h.off_esc_idx);
   a.w = nullptr;
   a.x = x;
   a.y = y;
@@ -634,12 +632,13 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
   a.n_esc = h.n_esc;
   // with no escapes, the (never used) escape loads read the container header
   a.esc_last = h.n_esc ? h.n_esc - 1 : 0;
+  a.sym_last = h.n_esc ? (h.off_esc_idx - h.off_esc_sym) / 4 - 1 : 0;
   if (h.n_esc == 0) {
     a.esc_pos = (const uint32_t*)container;
     a.esc_sym = container;
+    a.esc_idx = (const uint32_t*)container;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
-  a.sym_last = (h.total_bytes - h.off_esc_sym) / 4 - 1;
   a.batch = batch;
   a.dict = dict_of(&h);
   if (cols % kGroup == 0) {

@@ -29,6 +29,11 @@
  *                    mantissa i at stream bits [7i, 7i+7), ceil(7n/8) bytes
  *   off_esc_pos      n_esc u32 positions (flat weight index), ascending
  *   off_esc_sym      n_esc symbols: u8 (byte-split) or u16 (K15)
+ *   off_esc_idx      escape index, only when n_esc > 0: for j = 0..T with
+ *                    T = ceil(n / WC_INDEX_TILE), u32 entry j = the number of
+ *                    escapes at positions below j * WC_INDEX_TILE (entry T =
+ *                    n_esc), so a kernel finds the first escape record of any
+ *                    tile with one load instead of a search of the positions
  *   total_bytes      end of the container
  * Symbols: byte-split s = b >> 8 (sign + exponent[7:1]); K15 s = b >> 7
  * (sign + exponent).  A weight is rebuilt as (s << 8) | low byte, or
@@ -70,8 +75,9 @@ extern "C" {
 #define WC_E_UNSUPPORTED (-5) /* batch outside 1..WC_MAX_BATCH */
 
 #define WC_MAGIC 0x36314357u /* bytes "WC16" */
-#define WC_VERSION 1u
+#define WC_VERSION 2u
 #define WC_HEADER_BYTES 128u
+#define WC_INDEX_TILE 2048u /* weights per escape-index entry */
 #define WC_MAX_BATCH 16u
 
 /* Scratch bytes wc_build_dict and wc_encode need for n weights. */
@@ -90,8 +96,9 @@ typedef struct wc_header {
   uint64_t off_raw;     /* = pad16(128 + ceil(n/2)) */
   uint64_t off_esc_pos; /* = pad16(off_raw + raw bytes) */
   uint64_t off_esc_sym; /* = pad16(off_esc_pos + 4 n_esc) */
-  uint64_t total_bytes; /* = pad16(off_esc_sym + symbol bytes) */
-  uint8_t reserved[32]; /* zero */
+  uint64_t total_bytes; /* = pad16(off_esc_idx + 4 (T + 1)), or off_esc_idx when n_esc == 0 */
+  uint64_t off_esc_idx; /* = pad16(off_esc_sym + symbol bytes) */
+  uint8_t reserved[24]; /* zero */
 } wc_header;
 
 /*
@@ -109,7 +116,8 @@ int wc_build_dict(int layout, const uint16_t *d_w, uint64_t n, void *d_work,
 /*
  * Encode [P3 "Cómo funciona la compresión"]: writes the whole container for
  * d_w[0..h->n) — header, codes, raw stream, escape positions and symbols —
- * into d_container[0..h->total_bytes).  *h must be the header wc_build_dict
+ * into d_container[0..h->total_bytes) (with the escape index when there are
+ * escapes).  *h must be the header wc_build_dict
  * returned for the same weights (checked for consistency; a header whose
  * escape count does not match the data yields a container that fails to
  * decode).  container_bytes >= h->total_bytes; d_work as for wc_build_dict.
@@ -122,9 +130,10 @@ int wc_encode(const wc_header *h, const uint16_t *d_w, uint8_t *d_container,
  * Exact decode [P3 "Cómo funciona la compresión"; P2 "¿Qué significa “sin
  * pérdida”…"]: rebuilds the n BF16 bit patterns into d_out[0..n).  *h is the
  * host copy of the container's header (validated: WC_E_CORRUPT).  Escape
- * records whose position lies outside the tile being decoded, or past
- * n_esc, are ignored, so a corrupt stream body cannot make the kernel read
- * or write outside the container and d_out.
+ * index entries are clamped to [0, n_esc], and escape records whose position
+ * lies outside the tile being decoded, or past n_esc, are ignored, so a
+ * corrupt stream body cannot make the kernel read or write outside the
+ * container and d_out.
  */
 int wc_decode(const wc_header *h, const uint8_t *d_container,
               size_t container_bytes, uint16_t *d_out, void *stream);
@@ -154,7 +163,8 @@ int wc_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols,
 /*
  * Accounting [P3 "Cómo funciona la compresión": bits per weight with all
  * overhead included]: *bpw = 8 * total_bytes / n (header, dictionary,
- * streams, padding); *payload_bpw = 8 * (codes + raw + escape bytes) / n.
+ * streams, padding); *payload_bpw = 8 * (codes + raw + escape bytes) / n,
+ * the escape bytes being positions, symbols and the escape index.
  * Host only.  n == 0 -> WC_E_ARG.
  */
 int wc_bits_per_weight(const wc_header *h, double *bpw, double *payload_bpw);

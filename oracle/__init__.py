@@ -151,14 +151,14 @@ def header_info(container: np.ndarray) -> dict:
     n = ctypes.c_uint64(0)
     ne = ctypes.c_uint64(0)
     d = np.zeros(16, dtype=np.uint16)
-    off = np.zeros(5, dtype=np.uint64)
+    off = np.zeros(6, dtype=np.uint64)
     _check(_load().orc_header_info(_ptr(c), c.size, ctypes.byref(lay), ctypes.byref(nd),
                                    ctypes.byref(n), ctypes.byref(ne), _ptr(d), _ptr(off)),
            "header")
     return {"layout": lay.value, "n_dict": nd.value, "n": n.value, "n_esc": ne.value,
             "dict": d, "off_codes": int(off[0]), "off_raw": int(off[1]),
             "off_esc_pos": int(off[2]), "off_esc_sym": int(off[3]),
-            "total_bytes": int(off[4])}
+            "total_bytes": int(off[4]), "off_esc_idx": int(off[5])}
 
 
 def decode(container: np.ndarray) -> np.ndarray:

@@ -29,8 +29,10 @@
  *  - codes: two per byte, the even-index weight in the low nibble;
  *  - K15 mantissas: one LSB-first bitstream, mantissa i at bits [7i, 7i+7);
  *  - escape stream: ascending u32 positions, then the symbols (u8 for
- *    byte-split, u16 for K15);
- *  - container: 128-byte little-endian header, then the four streams, each
+ *    byte-split, u16 for K15), then (only when there are escapes) an index:
+ *    for every multiple of 2048 weights j*2048 up to the tensor's last tile
+ *    end, the number of escapes at positions below it (u32);
+ *  - container: 128-byte little-endian header, then the five streams, each
  *    starting at a 16-byte aligned offset, gaps and tail zero.
  */
 #include "wc_oracle.h"
@@ -38,8 +40,9 @@
 #include <string.h>
 
 #define ORC_MAGIC 0x36314357u /* bytes "WC16" */
-#define ORC_VERSION 1u
+#define ORC_VERSION 2u
 #define ORC_HEADER_BYTES 128u
+#define ORC_INDEX_TILE 2048u /* weights per escape-index entry */
 
 /* ---- little-endian field access (byte by byte) ------------------------- */
 
@@ -79,19 +82,26 @@ static uint64_t raw_stream_bytes(int layout, uint64_t n) {
 
 static uint64_t sym_bytes(int layout) { return layout == ORC_LAYOUT_K15 ? 2u : 1u; }
 
+/* escape-index entries: one per 2048-weight tile start plus the end, and
+ * none at all without escapes */
+static uint64_t index_entries(uint64_t n, uint64_t e) {
+  return e ? (n + ORC_INDEX_TILE - 1u) / ORC_INDEX_TILE + 1u : 0u;
+}
+
 static int layout_ok(int layout) {
   return layout == ORC_LAYOUT_BYTESPLIT || layout == ORC_LAYOUT_K15;
 }
 
-/* stream offsets for n weights and e escapes:
+/* stream offsets for n weights and e escapes, in the header's field order:
  * off[0] codes, off[1] raw, off[2] escape positions, off[3] escape symbols,
- * off[4] total container bytes */
-static void layout_offsets(int layout, uint64_t n, uint64_t e, uint64_t off[5]) {
+ * off[4] total container bytes, off[5] escape index (the last stream) */
+static void layout_offsets(int layout, uint64_t n, uint64_t e, uint64_t off[6]) {
   off[0] = ORC_HEADER_BYTES;
   off[1] = pad16(off[0] + (n + 1u) / 2u);
   off[2] = pad16(off[1] + raw_stream_bytes(layout, n));
   off[3] = pad16(off[2] + 4u * e);
-  off[4] = pad16(off[3] + sym_bytes(layout) * e);
+  off[5] = pad16(off[3] + sym_bytes(layout) * e);
+  off[4] = pad16(off[5] + 4u * index_entries(n, e));
 }
 
 /* ---- step 1: symbol counts ------------------------------------------- */
@@ -136,7 +146,7 @@ int orc_container_size(int layout, uint64_t n, uint64_t n_esc, uint64_t *total) 
   if (!layout_ok(layout) || !total) return ORC_E_ARG;
   if (n >= (1ull << 32)) return ORC_E_SIZE;
   if (n_esc > n) return ORC_E_ARG;
-  uint64_t off[5];
+  uint64_t off[6];
   layout_offsets(layout, n, n_esc, off);
   *total = off[4];
   return ORC_OK;
@@ -156,7 +166,7 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
   uint64_t n_esc;
   orc_dictionary(layout, counts, n, dict, &n_dict, &n_esc);
 
-  uint64_t off[5];
+  uint64_t off[6];
   layout_offsets(layout, n, n_esc, off);
   if (cap < off[4]) return ORC_E_SIZE;
   memset(out, 0, off[4]); /* gaps and tails are zero */
@@ -170,8 +180,11 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
   uint8_t *raw = out + off[1];
   uint8_t *esc_pos = out + off[2];
   uint8_t *esc_sym = out + off[3];
+  uint8_t *esc_idx = out + off[5];
   uint64_t e = 0;
   for (uint64_t i = 0; i < n; ++i) {
+    /* index entry of each tile: the escapes seen before its first weight */
+    if (n_esc && i % ORC_INDEX_TILE == 0) put_le(esc_idx + 4u * (i / ORC_INDEX_TILE), e, 4);
     uint32_t s = symbol_of(layout, w[i]);
     uint32_t r = raw_of(layout, w[i]);
     uint32_t c = code_of[s];
@@ -194,6 +207,9 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
     }
   }
 
+  /* the closing entry: every escape lies below the last tile's end */
+  if (n_esc) put_le(esc_idx + 4u * (index_entries(n, n_esc) - 1u), e, 4);
+
   uint8_t *h = out;
   put_le(h + 0, ORC_MAGIC, 4);
   put_le(h + 4, ORC_VERSION, 2);
@@ -202,7 +218,7 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
   put_le(h + 8, n, 8);
   put_le(h + 16, n_esc, 8);
   for (int k = 0; k < 16; ++k) put_le(h + 24 + 2 * k, dict[k], 2);
-  for (int k = 0; k < 5; ++k) put_le(h + 56 + 8 * k, off[k], 8);
+  for (int k = 0; k < 6; ++k) put_le(h + 56 + 8 * k, off[k], 8);
   *size = off[4];
   return ORC_OK;
 }
@@ -211,7 +227,7 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
 
 int orc_header_info(const uint8_t *c, uint64_t size, int *layout, int *n_dict,
                     uint64_t *n, uint64_t *n_esc, uint16_t dict[16],
-                    uint64_t offsets[5]) {
+                    uint64_t offsets[6]) {
   if (!c || !layout || !n_dict || !n || !n_esc || !dict || !offsets) return ORC_E_ARG;
   if (size < ORC_HEADER_BYTES) return ORC_E_CORRUPT;
   if (get_le(c + 0, 4) != ORC_MAGIC || get_le(c + 4, 2) != ORC_VERSION) return ORC_E_CORRUPT;
@@ -227,13 +243,13 @@ int orc_header_info(const uint8_t *c, uint64_t size, int *layout, int *n_dict,
     for (int j = 0; j < k && k < nd; ++j)
       if (dict[j] == dict[k]) return ORC_E_CORRUPT;
   }
-  uint64_t want[5];
+  uint64_t want[6];
   layout_offsets(lay, nn, ne, want);
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < 6; ++k) {
     offsets[k] = get_le(c + 56 + 8 * k, 8);
     if (offsets[k] != want[k]) return ORC_E_CORRUPT;
   }
-  for (int k = 96; k < 128; ++k)
+  for (int k = 104; k < 128; ++k)
     if (c[k] != 0) return ORC_E_CORRUPT;
   if (offsets[4] > size) return ORC_E_CORRUPT;
   *layout = lay;
@@ -250,7 +266,7 @@ int orc_header_info(const uint8_t *c, uint64_t size, int *layout, int *n_dict,
 
 int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap) {
   int layout, n_dict;
-  uint64_t n, n_esc, off[5];
+  uint64_t n, n_esc, off[6];
   uint16_t dict[16];
   int st = orc_header_info(c, size, &layout, &n_dict, &n, &n_esc, dict, off);
   if (st != ORC_OK) return st;
@@ -259,8 +275,12 @@ int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap) {
   const uint8_t *raw = c + off[1];
   const uint8_t *esc_pos = c + off[2];
   const uint8_t *esc_sym = c + off[3];
+  const uint8_t *esc_idx = c + off[5];
   uint64_t e = 0;
   for (uint64_t i = 0; i < n; ++i) {
+    /* every index entry must count the escapes before its tile */
+    if (n_esc && i % ORC_INDEX_TILE == 0 && get_le(esc_idx + 4u * (i / ORC_INDEX_TILE), 4) != e)
+      return ORC_E_CORRUPT;
     uint32_t code = (codes[i / 2] >> ((i % 2) * 4)) & 15u;
     uint32_t s;
     if (code == 15) {
@@ -285,6 +305,7 @@ int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap) {
     out[i] = (uint16_t)((s << symbol_shift(layout)) | r);
   }
   if (e != n_esc) return ORC_E_CORRUPT;
+  if (n_esc && get_le(esc_idx + 4u * (index_entries(n, n_esc) - 1u), 4) != e) return ORC_E_CORRUPT;
   return ORC_OK;
 }
 
@@ -339,18 +360,19 @@ int orc_gemv_f64(const uint16_t *W, uint64_t rows, uint64_t cols,
 /* ---- accounting [P3 "Cómo funciona…": bits per weight with all overhead
  * included] -------------------------------------------------------------
  * bpw counts every container byte (header, dictionary, streams, padding);
- * payload_bpw counts the four streams' own bytes only. */
+ * payload_bpw counts the streams' own bytes only (the escape index is part
+ * of the escape overhead). */
 
 int orc_bits_per_weight(const uint8_t *c, uint64_t size, double *bpw,
                         double *payload_bpw) {
   int layout, n_dict;
-  uint64_t n, n_esc, off[5];
+  uint64_t n, n_esc, off[6];
   uint16_t dict[16];
   int st = orc_header_info(c, size, &layout, &n_dict, &n, &n_esc, dict, off);
   if (st != ORC_OK) return st;
   if (!bpw || !payload_bpw || n == 0) return ORC_E_ARG;
   uint64_t payload = (n + 1u) / 2u + raw_stream_bytes(layout, n) + 4u * n_esc +
-                     sym_bytes(layout) * n_esc;
+                     sym_bytes(layout) * n_esc + 4u * index_entries(n, n_esc);
   *bpw = 8.0 * (double)off[4] / (double)n;
   *payload_bpw = 8.0 * (double)payload / (double)n;
   return ORC_OK;

@@ -64,10 +64,12 @@ int orc_container_size(int layout, uint64_t n, uint64_t n_esc, uint64_t *total);
 int orc_encode(int layout, const uint16_t *w, uint64_t n,
                uint8_t *out, uint64_t cap, uint64_t *size);
 
-/* Header fields of a container (parsed by the oracle's own reader). */
+/* Header fields of a container (parsed by the oracle's own reader).
+ * offsets: codes, raw, escape positions, escape symbols, total bytes,
+ * escape index. */
 int orc_header_info(const uint8_t *c, uint64_t size, int *layout, int *n_dict,
                     uint64_t *n, uint64_t *n_esc, uint16_t dict[16],
-                    uint64_t offsets[5]);
+                    uint64_t offsets[6]);
 
 /* Decode a container into out[0..n). */
 int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap);

@@ -66,8 +66,8 @@ def test_bits_per_weight_matches_oracle(wc, layout):
 def test_host_checks_reject_bad_headers(wc):
     w = synth.random_bits(3000, 5, "uniform")
     h, _ = _header_from_oracle(0, w)
-    for field, val in [("magic", 0), ("version", 2), ("layout", 7), ("n_dict", 16),
-                       ("off_raw", 0), ("total_bytes", 1)]:
+    for field, val in [("magic", 0), ("version", 1), ("layout", 7), ("n_dict", 16),
+                       ("off_raw", 0), ("total_bytes", 1), ("off_esc_idx", 0)]:
         bad = wc.Header.from_bytes(h.to_bytes())
         setattr(bad, field, val)
         with pytest.raises(wc.WCError) as e:
@@ -117,10 +117,11 @@ def test_header_struct_layout(wc):
     offs = {f[0]: getattr(wc.Header, f[0]).offset for f in wc.Header._fields_}
     assert offs == {"magic": 0, "version": 4, "layout": 6, "n_dict": 7, "n": 8, "n_esc": 16,
                     "dict": 24, "off_codes": 56, "off_raw": 64, "off_esc_pos": 72,
-                    "off_esc_sym": 80, "total_bytes": 88, "reserved": 96}
+                    "off_esc_sym": 80, "total_bytes": 88, "off_esc_idx": 96, "reserved": 104}
     # and a container header written by the oracle parses field by field
     w = np.array([0x3F80, 0xBF80, 0x3F80, 0x4000, 0x3F81], dtype=np.uint16)
     h, _ = _header_from_oracle(0, w)
-    assert (h.magic, h.version, h.layout, h.n_dict, h.n, h.n_esc) == (0x36314357, 1, 0, 3, 5, 0)
+    assert (h.magic, h.version, h.layout, h.n_dict, h.n, h.n_esc) == (0x36314357, 2, 0, 3, 5, 0)
     assert list(h.dict)[:3] == [0x3F, 0x40, 0xBF]
-    assert (h.off_codes, h.off_raw, h.off_esc_pos, h.total_bytes) == (128, 144, 160, 160)
+    assert (h.off_codes, h.off_raw, h.off_esc_pos, h.total_bytes, h.off_esc_idx) == \
+        (128, 144, 160, 160, 160)

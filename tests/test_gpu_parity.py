@@ -213,8 +213,8 @@ def test_gemv_escape_dense(layout):
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_clustered_escapes_small(layout):
     """A band of escape-dense rows in a tensor small enough to run as one
-    round of waves: cursor searches that start with an interpolated probe
-    land far from the band's records and take the full-range search."""
+    round of waves: every wave of the band starts from an escape-index entry
+    that lies deep in the record stream."""
     rows, cols = 1024, 4096
     w = synth.random_bits(rows * cols, 903, "normal").reshape(rows, cols)
     band = synth.random_bits(96 * cols, 904, "uniform").reshape(96, cols) & np.uint16(0xBFFF)

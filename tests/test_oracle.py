@@ -53,6 +53,12 @@ def expected_container(case):
 
 
 def weights_of(case):
+    if "weights_sparse" in case:
+        sp = case["weights_sparse"]
+        w = np.full(sp["n"], int(sp["fill"], 16), dtype=np.uint16)
+        for i, h in sp["at"].items():
+            w[int(i)] = int(h, 16)
+        return w
     return np.array([int(h, 16) for h in case["weights"]], dtype=np.uint16)
 
 
@@ -226,14 +232,23 @@ def test_escape_stream_invariants(layout):
         assert not any(int(s) in dset for s in sym)
         exp_pos = np.nonzero(~np.isin(w.astype(np.uint32) >> sh, list(dset)))[0]
         assert np.array_equal(pos.astype(np.int64), exp_pos)
+        # index entry j = escapes below weight 2048 j, for every tile start and
+        # the last tile's end (counted here by a search of the positions)
+        tiles = -(-w.size // 2048)
+        idx = c[info["off_esc_idx"]:info["off_esc_idx"] + 4 * (tiles + 1)].view("<u4")
+        bounds = 2048 * np.arange(tiles + 1, dtype=np.int64)
+        assert np.array_equal(idx.astype(np.int64), np.searchsorted(exp_pos, bounds, "left"))
+        assert info["total_bytes"] == -(-(info["off_esc_idx"] + 4 * (tiles + 1)) // 16) * 16
 
 
 # ------------------------------------------------------------- accounting
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_accounting_decomposition(layout):
-    """Payload bits/weight = 4 (code) + 8 or 7 (raw) + escape bits; all overhead
-    (header, padding) on top of that."""
+    """Payload bits/weight = 4 (code) + 8 or 7 (raw) + escape bits (a 32-bit
+    position and the symbol per escape, plus one 32-bit index entry per
+    2048-weight tile and one closing entry when there are escapes); all
+    overhead (header, padding) on top of that."""
     raw_bits = 7 if layout == oracle.K15 else 8
     esc_bits = 32 + (16 if layout == oracle.K15 else 8)
     for n, kind in [(4096, "normal"), (8192, "uniform"), (65536, "few"), (2 ** 20, "normal")]:
@@ -241,9 +256,10 @@ def test_accounting_decomposition(layout):
         c = oracle.encode(layout, w)
         e = oracle.header_info(c)["n_esc"]
         bpw, pay = oracle.bits_per_weight(c)
-        assert pay == pytest.approx(4 + raw_bits + esc_bits * e / n, rel=1e-12)
+        index_bits = 32 * (-(-n // 2048) + 1) if e else 0
+        assert pay == pytest.approx(4 + raw_bits + (esc_bits * e + index_bits) / n, rel=1e-12)
         overhead_bytes = (bpw - pay) * n / 8
-        assert 128 <= overhead_bytes < 128 + 4 * 16
+        assert 128 <= overhead_bytes < 128 + 5 * 16
 
 
 def test_pages_printed_totals():
@@ -329,6 +345,10 @@ def test_corruption_detected(layout):
     assert _err(oracle.decode, c[:-16]) == -3
     # escape position moved: the record no longer sits at its weight
     info = oracle.header_info(c)
+    for k in (1, 0):  # an index entry off by one (a tile start, then the first)
+        bad = c.copy()
+        bad[info["off_esc_idx"] + 4 * k] ^= 1
+        assert _err(oracle.decode, bad) == -3, k
     bad = c.copy()
     bad[info["off_esc_pos"]] ^= 1
     assert _err(oracle.decode, bad) == -3
@@ -384,6 +404,12 @@ MUTATIONS = {
     "gemv_dropped_term": [(r"float acc = 0\.0f;\n      for \(uint64_t c = 0;",
                            "float acc = 0.0f;\n      for (uint64_t c = 1;")],
     "symbol_shift": [(r"return layout == ORC_LAYOUT_K15 \? 7 : 8;", "return layout == ORC_LAYOUT_K15 ? 8 : 8;")],
+    # index entries counted up to and including the tile's first weight, in
+    # the encoder and in the decoder's check alike
+    "index_inclusive": [(r"if \(n_esc && i % ORC_INDEX_TILE == 0\) put_le\(esc_idx \+ 4u \* \(i / ORC_INDEX_TILE\), e, 4\);\n    uint32_t s = symbol_of\(layout, w\[i\]\);",
+                         "uint32_t s = symbol_of(layout, w[i]);\n    if (n_esc && i % ORC_INDEX_TILE == 0) put_le(esc_idx + 4u * (i / ORC_INDEX_TILE), e + (code_of[s] == 15), 4);"),
+                        (r"get_le\(esc_idx \+ 4u \* \(i / ORC_INDEX_TILE\), 4\) != e\)",
+                         "get_le(esc_idx + 4u * (i / ORC_INDEX_TILE), 4) != e + (((codes[i / 2] >> ((i % 2) * 4)) & 15u) == 15u))")],
 }
 
 
