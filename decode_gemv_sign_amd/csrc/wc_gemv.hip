@@ -304,21 +304,48 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+  // Escape cursors from the escape index: rows are whole tiles, so the
+  // wave's tile q is tile r0 * tpr + q of the tensor and its first record is
+  // that tile's index entry.  Lane i holds the entry of tile qb + i (64 at a
+  // time, clamped to n_esc), so the records of the next tile can be loaded
+  // before this tile's escapes are counted.
+  const uint64_t last_entry = a.rows * tpr;  // the closing entry
+  uint64_t qb = 0;
+  uint32_t iv = 0;
+  auto load_iv = [&]() {
+    if (a.n_esc) {
+      uint64_t j = r0 * tpr + qb + (uint64_t)lane;
+      j = j < last_entry ? j : last_entry;
+      const uint32_t v = a.esc_idx[j];
+      iv = v < a.n_esc ? v : (uint32_t)a.n_esc;
+    }
+  };
+  // first record of tile q; called with q non-decreasing
+  auto cursor = [&](uint64_t q) -> uint64_t {
+    if (q - qb >= (uint64_t)kWave) {
+      qb = q;
+      load_iv();
+    }
+    return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)iv, (int)(q - qb));
+  };
+
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
-  load_next(s0, x0);  // in flight while the escape cursor is read
-  uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, r0 * a.cols);
-  ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e, s0);
+  load_next(s0, x0);  // in flight while the escape index is read
+  load_iv();
+  ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, cursor(0), s0);
   TileCursor pc{r0, 0};
 
   auto step = [&](uint64_t q, uint32_t* buf, uint32_t* nbuf, uint32_t xv[16], uint32_t xn[16]) {
     wait_lgkm0();  // the previous tile's LDS reads and stage writes are done
-    // The first tile's ring and record loads are complete once at most the 3
-    // ring loads of the next tile are outstanding (ring_wait_ahead), or none
-    // when there is no next tile; later tiles' loads were issued before the
-    // previous tile's full wait.
+    const uint64_t e = cursor(q);
+    // The next tile's ring loads and its first records go out together.  The
+    // first tile's ring and record loads are complete once at most those 3 +
+    // 2 loads are outstanding, or none when there is no next tile; later
+    // tiles' loads were issued before the previous tile's full wait.
     if (q + 1 < nq) {
       load_next(nbuf, xn);
-      if (q == 0) wait_vm<kRingAhead>();
+      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, cursor(q + 1), nbuf);
+      if (q == 0) wait_vm<kRingAheadEsc>();
     } else if (q == 0) {
       wait_vm<0>();
     }
@@ -330,7 +357,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
-    ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave, nbuf);
     // a dense tile's symbol run goes into its own slot (free: the tile is in
     // registers)
     const bool dense = cnt_wave > kDenseMin;
@@ -344,7 +370,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
       patch_tile<LAYOUT>(buf, w, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
                          cnt_wave, pc.r * a.cols + pc.ct * kTile, kTile, eb);
     }
-    e += cnt_wave;
     // Full wait: x is read by ordinary loads, which the compiler awaits with
     // vmcnt(0) anyway while global->LDS loads are pending; it also completes
     // the next tile's ring and record loads.

@@ -239,17 +239,23 @@ __device__ inline void stage_store(uint32_t* __restrict__ stage, const uint32_t 
   }
 }
 
+// All four of the lane's group slots are read at once, behind one wait (one
+// LDS round trip instead of one per group); only the staged groups (bit k of
+// gmask) are taken.
 __device__ inline void stage_load(const uint32_t* __restrict__ stage, uint32_t out[16],
                                   uint32_t gmask) {
+  static_assert(kLaneGroups == 4, "four groups per lane");
   const uint32_t base = lds_addr(stage) + 16u * (uint32_t)lane_id();
+  u32x4 v[kLaneGroups];
+  asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+               "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(base) : "memory");
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) {
-    if ((gmask >> k) & 1u) {
-      u32x4 v;
-      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                   : "=&v"(v) : "v"(base + 1024u * k) : "memory");
-      out[4 * k] = v[0]; out[4 * k + 1] = v[1]; out[4 * k + 2] = v[2]; out[4 * k + 3] = v[3];
-    }
+    const bool take = (gmask >> k) & 1u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[4 * k + i] = take ? v[k][i] : out[4 * k + i];
   }
 }
 
@@ -325,10 +331,13 @@ constexpr uint32_t kRingSlotDwords = 1040;
 // with one pending it waits for vmcnt(0)).  So "at most N outstanding"
 // proves a global->LDS load complete only when N counts global->LDS loads
 // issued after it; ordinary loads and stores in between are never counted
-// (they only make the wait longer).  A ring user issues the next tile's 3
+// (they only make the wait longer).  The decode issues the next tile's 3
 // ring loads after the current tile's record loads and waits for at most
-// those 3.
+// those 3; the fused GEMV issues a tile's 3 ring loads and its 2 record
+// loads (ring_load_esc) together, after the current tile's, and waits for at
+// most those 5.
 constexpr int kRingAhead = 3;
+constexpr int kRingAheadEsc = kRingAhead + 2;
 
 // Tile whose first group is G (a multiple of 256, so every window below is
 // 16-byte aligned): 3 instructions.
