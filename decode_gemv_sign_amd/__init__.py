@@ -22,13 +22,15 @@ import os
 import torch  # loaded first, so libwc binds to the HIP runtime torch already uses
 
 __all__ = [
-    "BYTESPLIT", "K15", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into",
+    "BYTESPLIT", "K15", "RAW", "AUTO", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into",
     "encode", "decode", "decode_gemv", "gemv_bf16", "bits_per_weight", "read_header",
     "LIB_PATH",
 ]
 
 BYTESPLIT = 0
 K15 = 1
+RAW = 2   # fallback layout: the BF16 bit patterns as stored
+AUTO = 3  # build_dict / encode only: the smallest of the three
 MAX_BATCH = 16
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwc.so")
 

@@ -15,7 +15,10 @@ namespace {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? WC_OK : WC_E_HIP; }
 
-bool layout_ok(int layout) { return layout == WC_LAYOUT_BYTESPLIT || layout == WC_LAYOUT_K15; }
+bool layout_ok(int layout) {
+  return layout == WC_LAYOUT_BYTESPLIT || layout == WC_LAYOUT_K15 || layout == WC_LAYOUT_RAW ||
+         layout == WC_LAYOUT_AUTO;
+}
 
 }  // namespace
 
@@ -28,27 +31,50 @@ extern "C" int wc_build_dict(int layout, const uint16_t* d_w, uint64_t n, void* 
   if (work_bytes < WC_WORKSPACE_BYTES(n)) return WC_E_SIZE;
   hipStream_t s = (hipStream_t)stream;
 
-  wc::DictResult r;
-  memset(&r, 0, sizeof r);
-  if (n) {
+  // r[0]: the dictionary of `layout` (byte-split's under AUTO), r[1]: K15's
+  // under AUTO; the raw layout has none
+  wc::DictResult r[2];
+  memset(r, 0, sizeof r);
+  if (n && layout != WC_LAYOUT_RAW) {
     hipError_t e = wc::launch_build_dict(layout, d_w, n, (uint8_t*)d_work, s);
     if (e != hipSuccess) return WC_E_HIP;
-    e = hipMemcpyAsync(&r, (uint8_t*)d_work + wc::kWorkResult, sizeof r, hipMemcpyDeviceToHost, s);
+    static_assert(wc::kWorkResult2 == wc::kWorkResult + sizeof(wc::DictResult), "results adjacent");
+    const size_t nres = layout == WC_LAYOUT_AUTO ? 2 : 1;
+    e = hipMemcpyAsync(r, (uint8_t*)d_work + wc::kWorkResult, nres * sizeof(wc::DictResult),
+                       hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return WC_E_HIP;
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return WC_E_HIP;
-    if (r.n_dict > 15 || r.n_esc > n) return WC_E_HIP;  // not a valid result: the device work failed
+    for (int k = 0; k < (layout == WC_LAYOUT_AUTO ? 2 : 1); ++k)
+      if (r[k].n_dict > 15 || r[k].n_esc > n) return WC_E_HIP;  // not a valid result: the device work failed
   }
+  if (layout == WC_LAYOUT_AUTO) {
+    // the smallest container, ties to the lower layout number
+    const uint64_t t0 = wc::geometry(WC_LAYOUT_BYTESPLIT, n, r[0].n_esc).total;
+    const uint64_t t1 = wc::geometry(WC_LAYOUT_K15, n, r[1].n_esc).total;
+    const uint64_t t2 = wc::geometry(WC_LAYOUT_RAW, n, 0).total;
+    layout = WC_LAYOUT_BYTESPLIT;
+    uint64_t best = t0;
+    if (t1 < best) {
+      layout = WC_LAYOUT_K15;
+      best = t1;
+      r[0] = r[1];
+    }
+    if (t2 < best) layout = WC_LAYOUT_RAW;
+  }
+  const wc::DictResult& rr = r[0];
   wc_header h;
   memset(&h, 0, sizeof h);
   h.magic = WC_MAGIC;
   h.version = WC_VERSION;
   h.layout = (uint8_t)layout;
-  h.n_dict = (uint8_t)r.n_dict;
   h.n = n;
-  h.n_esc = r.n_esc;
-  for (int k = 0; k < 16; ++k) h.dict[k] = k < (int)r.n_dict ? r.dict[k] : 0;
-  const wc::Geometry g = wc::geometry(layout, n, r.n_esc);
+  if (layout != WC_LAYOUT_RAW) {
+    h.n_dict = (uint8_t)rr.n_dict;
+    h.n_esc = rr.n_esc;
+    for (int k = 0; k < 16; ++k) h.dict[k] = k < (int)rr.n_dict ? rr.dict[k] : 0;
+  }
+  const wc::Geometry g = wc::geometry(layout, n, h.n_esc);
   h.off_codes = g.off_codes;
   h.off_raw = g.off_raw;
   h.off_esc_pos = g.off_esc_pos;
@@ -110,7 +136,7 @@ extern "C" int wc_bits_per_weight(const wc_header* h, double* bpw, double* paylo
   const int v = wc::validate_header(h);
   if (v != WC_OK) return v;
   if (h->n == 0) return WC_E_ARG;
-  const uint64_t payload = (h->n + 1u) / 2u + wc::raw_bytes(h->layout, h->n) + 4u * h->n_esc +
+  const uint64_t payload = wc::code_bytes(h->layout, h->n) + wc::raw_bytes(h->layout, h->n) + 4u * h->n_esc +
                            wc::sym_bytes(h->layout) * h->n_esc + 4u * wc::index_entries(h->n, h->n_esc);
   *bpw = 8.0 * (double)h->total_bytes / (double)h->n;
   *payload_bpw = 8.0 * (double)payload / (double)h->n;

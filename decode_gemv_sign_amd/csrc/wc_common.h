@@ -26,7 +26,10 @@ constexpr int kPackBlock = kBlockThreads * kChunk;  // weights per encode block 
 __host__ __device__ inline uint64_t pad16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
 __host__ __device__ inline int sym_shift(int layout) { return layout == WC_LAYOUT_K15 ? 7 : 8; }
 __host__ __device__ inline uint64_t raw_bytes(int layout, uint64_t n) {
-  return layout == WC_LAYOUT_K15 ? (7u * n + 7u) / 8u : n;
+  return layout == WC_LAYOUT_K15 ? (7u * n + 7u) / 8u : (layout == WC_LAYOUT_RAW ? 2u * n : n);
+}
+__host__ __device__ inline uint64_t code_bytes(int layout, uint64_t n) {
+  return layout == WC_LAYOUT_RAW ? 0u : (n + 1u) / 2u;
 }
 __host__ __device__ inline uint64_t sym_bytes(int layout) { return layout == WC_LAYOUT_K15 ? 2u : 1u; }
 
@@ -43,7 +46,7 @@ struct Geometry {
 __host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_esc) {
   Geometry g;
   g.off_codes = WC_HEADER_BYTES;
-  g.off_raw = pad16(g.off_codes + (n + 1u) / 2u);
+  g.off_raw = pad16(g.off_codes + code_bytes(layout, n));
   g.off_esc_pos = pad16(g.off_raw + raw_bytes(layout, n));
   g.off_esc_sym = pad16(g.off_esc_pos + 4u * n_esc);
   g.off_esc_idx = pad16(g.off_esc_sym + sym_bytes(layout) * n_esc);
@@ -190,8 +193,10 @@ __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // WC_OK when *h is exactly the header the format defines for its fields.
 inline int validate_header(const wc_header* h) {
   if (h->magic != WC_MAGIC || h->version != WC_VERSION) return WC_E_CORRUPT;
-  if (h->layout != WC_LAYOUT_BYTESPLIT && h->layout != WC_LAYOUT_K15) return WC_E_CORRUPT;
+  if (h->layout != WC_LAYOUT_BYTESPLIT && h->layout != WC_LAYOUT_K15 && h->layout != WC_LAYOUT_RAW)
+    return WC_E_CORRUPT;
   if (h->n_dict > 15) return WC_E_CORRUPT;
+  if (h->layout == WC_LAYOUT_RAW && (h->n_dict != 0 || h->n_esc != 0)) return WC_E_CORRUPT;
   if (h->n >= (1ull << 32) || h->n_esc > h->n) return WC_E_CORRUPT;
   const uint32_t nsym = h->layout == WC_LAYOUT_K15 ? 512u : 256u;
   for (int k = 0; k < 16; ++k) {

@@ -264,9 +264,72 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   }
 }
 
+// ---- raw layout: the weights stored as they are ---------------------------
+// One 16-byte vector (8 weights) per thread and step, grid-stride.  Encode
+// writes the container's header and pads its last vector with zeros (the
+// stream's padding); decode writes only the n weights.
+
+__global__ __launch_bounds__(kBlockThreads) void k_encode_raw(const uint16_t* __restrict__ w,
+                                                              uint8_t* __restrict__ container,
+                                                              uint64_t n, wc_header h) {
+  if (blockIdx.x == 0 && threadIdx.x < WC_HEADER_BYTES / 4)
+    ((uint32_t*)container)[threadIdx.x] = ((const uint32_t*)&h)[threadIdx.x];
+  u32x4* dst = (u32x4*)(container + h.off_raw);
+  const uint64_t nvec = (n + 7) / 8;
+  for (uint64_t v = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x; v < nvec;
+       v += (uint64_t)gridDim.x * kBlockThreads) {
+    if (8 * v + 8 <= n) {
+      dst[v] = __builtin_nontemporal_load((const u32x4*)w + v);
+    } else {
+      uint32_t d[4] = {0u, 0u, 0u, 0u};
+      for (uint64_t i = 8 * v; i < n; ++i) d[(i & 7) >> 1] |= (uint32_t)w[i] << (16u * (uint32_t)(i & 1));
+      dst[v] = u32x4{d[0], d[1], d[2], d[3]};
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_decode_raw(const uint8_t* __restrict__ raw,
+                                                              uint16_t* __restrict__ out,
+                                                              uint64_t n) {
+  const u32x4* src = (const u32x4*)raw;
+  const uint64_t nvec = (n + 7) / 8;
+  for (uint64_t v = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x; v < nvec;
+       v += (uint64_t)gridDim.x * kBlockThreads) {
+    const u32x4 d = __builtin_nontemporal_load(src + v);
+    if (8 * v + 8 <= n) {
+      __builtin_nontemporal_store(d, (u32x4*)out + v);
+    } else {
+      for (uint64_t i = 8 * v; i < n; ++i) out[i] = (uint16_t)(d[(i & 7) >> 1] >> (16u * (uint32_t)(i & 1)));
+    }
+  }
+}
+
+static dim3 raw_grid(uint64_t n) {
+  const uint64_t nvec = (n + 7) / 8;
+  uint64_t blocks = (nvec + kBlockThreads - 1) / kBlockThreads;
+  const uint64_t cap = (uint64_t)cu_count() * 16u;  // a few rounds' worth; the loop strides the rest
+  blocks = blocks < cap ? blocks : cap;
+  return dim3((unsigned)(blocks ? blocks : 1));
+}
+
+hipError_t launch_encode_raw(const wc_header& h, const uint16_t* w, uint8_t* container,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_encode_raw, raw_grid(h.n), dim3(kBlockThreads), 0, s, w, container, h.n, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_raw(const wc_header& h, const uint8_t* container, uint16_t* out,
+                             hipStream_t s) {
+  if (h.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_decode_raw, raw_grid(h.n), dim3(kBlockThreads), 0, s, container + h.off_raw,
+                     out, h.n);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t* out,
                          hipStream_t s) {
   if (h.n == 0) return hipSuccess;
+  if (h.layout == WC_LAYOUT_RAW) return launch_decode_raw(h, container, out, s);
   DecodeArgs a{};
   a.codes = container + h.off_codes;
   a.raw = container + h.off_raw;

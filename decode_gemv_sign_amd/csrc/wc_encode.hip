@@ -161,8 +161,15 @@ hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t*
   if (blocks > 1024) blocks = 1024;
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(k_hist, dim3((unsigned)blocks), dim3(kBlockThreads), 0, s, w, n, hist);
-  hipLaunchKernelGGL(k_top15, dim3(1), dim3(512), 0, s, hist, layout, n,
-                     (DictResult*)(work + kWorkResult));
+  if (layout == WC_LAYOUT_AUTO) {
+    hipLaunchKernelGGL(k_top15, dim3(1), dim3(512), 0, s, hist, (int)WC_LAYOUT_BYTESPLIT, n,
+                       (DictResult*)(work + kWorkResult));
+    hipLaunchKernelGGL(k_top15, dim3(1), dim3(512), 0, s, hist, (int)WC_LAYOUT_K15, n,
+                       (DictResult*)(work + kWorkResult2));
+  } else {
+    hipLaunchKernelGGL(k_top15, dim3(1), dim3(512), 0, s, hist, layout, n,
+                       (DictResult*)(work + kWorkResult));
+  }
   return hipGetLastError();
 }
 
@@ -391,6 +398,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
 
 hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
                          hipStream_t s) {
+  if (h.layout == WC_LAYOUT_RAW) return launch_encode_raw(h, w, container, s);
   const uint64_t nblk = (h.n + kPackBlock - 1) / kPackBlock;
   uint32_t* blk_cnt = (uint32_t*)(work + kWorkBlocks);
   uint32_t* blk_off = blk_cnt + nblk;

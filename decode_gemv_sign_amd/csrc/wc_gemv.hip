@@ -641,6 +641,9 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
                        count);
     return hipGetLastError();
   }
+  // raw layout: the stored weights are plain BF16
+  if (h.layout == WC_LAYOUT_RAW)
+    return launch_gemv_bf16((const uint16_t*)(container + h.off_raw), rows, cols, x, batch, y, s);
   if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
     return launch_decode_gemm_mfma(h, container, rows, cols, x, batch, y, s);
   GemvArgs a{};

@@ -8,7 +8,8 @@ namespace wc {
 
 // Byte offsets inside the caller's workspace (WC_WORKSPACE_BYTES(n) bytes).
 constexpr size_t kWorkHist = 0;         // u32[512] symbol counts
-constexpr size_t kWorkResult = 2048;    // DictResult
+constexpr size_t kWorkResult = 2048;    // DictResult (of the layout asked for; byte-split's under AUTO)
+constexpr size_t kWorkResult2 = 2096;   // DictResult of K15 under AUTO
 constexpr size_t kWorkBlocks = 4096;    // u32[nblk] escape counts, then u32[nblk] offsets
 
 struct DictResult {
@@ -32,7 +33,14 @@ inline uint32_t cu_count() {
   return (uint32_t)cached[dev];
 }
 
+// layout WC_LAYOUT_AUTO ranks both symbol kinds (results at kWorkResult and
+// kWorkResult2).
 hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t* work,
+                             hipStream_t s);
+// Raw layout (wc_decode.hip): the weights copied into / out of the container.
+hipError_t launch_encode_raw(const wc_header& h, const uint16_t* w, uint8_t* container,
+                             hipStream_t s);
+hipError_t launch_decode_raw(const wc_header& h, const uint8_t* container, uint16_t* out,
                              hipStream_t s);
 hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
                          hipStream_t s);

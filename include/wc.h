@@ -21,6 +21,7 @@
  * Container (all integers little-endian; every stream starts at a 16-byte
  * aligned offset; gaps and tails are zero):
  *   [0,128)          wc_header below
+ * Byte-split and K15 (layouts 0 and 1):
  *   off_codes (128)  4-bit codes, ceil(n/2) bytes; weight i in byte i/2, the
  *                    low nibble when i is even; code k < n_dict selects
  *                    dict[k]; code 15 marks an escape
@@ -35,6 +36,10 @@
  *                    n_esc), so a kernel finds the first escape record of any
  *                    tile with one load instead of a search of the positions
  *   total_bytes      end of the container
+ * Raw (layout 2, a per-tensor fallback for tensors that do not code below
+ * 16 bits/weight): n_dict = n_esc = 0, dictionary zero, an empty code
+ * stream, and the raw stream at off_raw = 128 holds the n BF16 bit patterns
+ * as u16; the escape streams are empty (all later offsets = total_bytes).
  * Symbols: byte-split s = b >> 8 (sign + exponent[7:1]); K15 s = b >> 7
  * (sign + exponent).  A weight is rebuilt as (s << 8) | low byte, or
  * (s << 7) | mantissa.  The dictionary holds the min(15, #distinct) most
@@ -49,7 +54,8 @@
  *  - d_w, d_container, d_out, d_x must be 16-byte aligned; d_y 4-byte.
  *  - `stream` is a hipStream_t (NULL = the null stream).  All device work is
  *    enqueued on it in order and returns without waiting, except
- *    wc_build_dict, which waits for `stream` once (it reads back 64 bytes).
+ *    wc_build_dict, which waits for `stream` once (it reads back 48 bytes, or
+ *    96 under WC_LAYOUT_AUTO).
  *  - Return value: WC_OK or a negative WC_E_* code; nothing is enqueued when
  *    an argument check fails.  A device fault shows up at the caller's next
  *    synchronisation.  No call aborts or throws.
@@ -66,6 +72,8 @@ extern "C" {
 
 #define WC_LAYOUT_BYTESPLIT 0
 #define WC_LAYOUT_K15 1
+#define WC_LAYOUT_RAW 2  /* fallback: the BF16 bit patterns as they are */
+#define WC_LAYOUT_AUTO 3 /* wc_build_dict only: the smallest of the three */
 
 #define WC_OK 0
 #define WC_E_ARG (-1)         /* null pointer, misalignment, bad size/shape */
@@ -107,6 +115,13 @@ typedef struct wc_header {
  * patterns), takes the top 15 as the dictionary, and fills *h_out with the
  * complete header of the container wc_encode will write (escape count,
  * stream offsets and total size included), so the caller can allocate it.
+ * layout WC_LAYOUT_AUTO counts both symbol kinds in the same pass and
+ * returns the header of whichever of byte-split, K15 and raw gives the
+ * smallest container (ties to the lower layout number); WC_LAYOUT_RAW needs
+ * no device work and does not wait.  The pages ask for a BF16 fallback
+ * where the coding does not pay (page "Compresión de pesos LLM sin pérdida
+ * vs 8-bit GGUF…", section "Preguntas para un vendor o equipo de
+ * investigación").
  * d_work: WC_WORKSPACE_BYTES(n) bytes of device scratch (contents ignored
  * and overwritten).  Waits for `stream`.  n == 0 is allowed (empty tensor).
  */

@@ -24,6 +24,7 @@ import numpy as np
 
 BYTESPLIT = 0
 K15 = 1
+RAW = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wc_oracle.c")
@@ -64,9 +65,11 @@ def _bind(path: str):
     lib.orc_gemv_f32.argtypes = [P, U64, U64, P, ctypes.c_uint32, P]
     lib.orc_gemv_f64.argtypes = [P, U64, U64, P, ctypes.c_uint32, P, P]
     lib.orc_bits_per_weight.argtypes = [P, U64, P, P]
+    lib.orc_choose_layout.argtypes = [P, U64, P]
     for f in (lib.orc_histogram, lib.orc_dictionary, lib.orc_container_size,
               lib.orc_encode, lib.orc_header_info, lib.orc_decode,
-              lib.orc_gemv_f32, lib.orc_gemv_f64, lib.orc_bits_per_weight):
+              lib.orc_gemv_f32, lib.orc_gemv_f64, lib.orc_bits_per_weight,
+              lib.orc_choose_layout):
         f.restype = I
     return lib
 
@@ -131,10 +134,20 @@ def container_size(layout: int, n: int, n_esc: int) -> int:
     return t.value
 
 
+def choose_layout(w) -> int:
+    """The layout (BYTESPLIT, K15 or RAW) with the smallest container."""
+    a = _u16(w)
+    lay = ctypes.c_int(-1)
+    _check(_load().orc_choose_layout(_ptr(a), a.size, ctypes.byref(lay)), "choose_layout")
+    return lay.value
+
+
 def encode(layout: int, w) -> np.ndarray:
     a = _u16(w)
-    counts = histogram(layout, a)
-    _, _, n_esc = dictionary(layout, counts, a.size)
+    n_esc = 0
+    if layout != RAW:
+        counts = histogram(layout, a)
+        _, _, n_esc = dictionary(layout, counts, a.size)
     cap = container_size(layout, a.size, n_esc)
     out = np.zeros(cap, dtype=np.uint8)
     size = ctypes.c_uint64(0)

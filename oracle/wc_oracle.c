@@ -33,7 +33,11 @@
  *    for every multiple of 2048 weights j*2048 up to the tensor's last tile
  *    end, the number of escapes at positions below it (u32);
  *  - container: 128-byte little-endian header, then the five streams, each
- *    starting at a 16-byte aligned offset, gaps and tail zero.
+ *    starting at a 16-byte aligned offset, gaps and tail zero;
+ *  - raw layout (a BF16 fallback per tensor): no dictionary, codes or
+ *    escapes, the weights as u16 in the raw stream; a tensor takes the
+ *    layout (byte-split, K15 or raw) with the smallest container, ties to
+ *    the lower layout number.
  */
 #include "wc_oracle.h"
 
@@ -76,8 +80,15 @@ static uint32_t raw_of(int layout, uint16_t b) {
 }
 
 static uint64_t raw_stream_bytes(int layout, uint64_t n) {
-  /* byte-split keeps one low byte per weight; K15 keeps 7 bits per weight */
+  /* byte-split keeps one low byte per weight; K15 keeps 7 bits per weight;
+   * raw keeps the whole 16-bit weight */
+  if (layout == ORC_LAYOUT_RAW) return 2u * n;
   return layout == ORC_LAYOUT_K15 ? (7u * n + 7u) / 8u : n;
+}
+
+/* two 4-bit codes per byte; the raw layout has no codes */
+static uint64_t code_stream_bytes(int layout, uint64_t n) {
+  return layout == ORC_LAYOUT_RAW ? 0u : (n + 1u) / 2u;
 }
 
 static uint64_t sym_bytes(int layout) { return layout == ORC_LAYOUT_K15 ? 2u : 1u; }
@@ -89,15 +100,18 @@ static uint64_t index_entries(uint64_t n, uint64_t e) {
 }
 
 static int layout_ok(int layout) {
-  return layout == ORC_LAYOUT_BYTESPLIT || layout == ORC_LAYOUT_K15;
+  return layout == ORC_LAYOUT_BYTESPLIT || layout == ORC_LAYOUT_K15 || layout == ORC_LAYOUT_RAW;
 }
+
+/* layouts with a dictionary and escapes */
+static int coded(int layout) { return layout != ORC_LAYOUT_RAW; }
 
 /* stream offsets for n weights and e escapes, in the header's field order:
  * off[0] codes, off[1] raw, off[2] escape positions, off[3] escape symbols,
  * off[4] total container bytes, off[5] escape index (the last stream) */
 static void layout_offsets(int layout, uint64_t n, uint64_t e, uint64_t off[6]) {
   off[0] = ORC_HEADER_BYTES;
-  off[1] = pad16(off[0] + (n + 1u) / 2u);
+  off[1] = pad16(off[0] + code_stream_bytes(layout, n));
   off[2] = pad16(off[1] + raw_stream_bytes(layout, n));
   off[3] = pad16(off[2] + 4u * e);
   off[5] = pad16(off[3] + sym_bytes(layout) * e);
@@ -107,7 +121,7 @@ static void layout_offsets(int layout, uint64_t n, uint64_t e, uint64_t off[6]) 
 /* ---- step 1: symbol counts ------------------------------------------- */
 
 int orc_histogram(int layout, const uint16_t *w, uint64_t n, uint64_t *counts) {
-  if (!layout_ok(layout) || !counts || (n && !w)) return ORC_E_ARG;
+  if (!layout_ok(layout) || !coded(layout) || !counts || (n && !w)) return ORC_E_ARG;
   for (int s = 0; s < n_symbols(layout); ++s) counts[s] = 0;
   for (uint64_t i = 0; i < n; ++i) counts[symbol_of(layout, w[i])] += 1;
   return ORC_OK;
@@ -120,7 +134,7 @@ int orc_histogram(int layout, const uint16_t *w, uint64_t n, uint64_t *counts) {
 
 int orc_dictionary(int layout, const uint64_t *counts, uint64_t n,
                    uint16_t dict[16], int *n_dict, uint64_t *n_esc) {
-  if (!layout_ok(layout) || !counts || !dict || !n_dict || !n_esc) return ORC_E_ARG;
+  if (!layout_ok(layout) || !coded(layout) || !counts || !dict || !n_dict || !n_esc) return ORC_E_ARG;
   int picked[512];
   memset(picked, 0, sizeof picked);
   for (int k = 0; k < 16; ++k) dict[k] = 0;
@@ -145,10 +159,41 @@ int orc_dictionary(int layout, const uint64_t *counts, uint64_t n,
 int orc_container_size(int layout, uint64_t n, uint64_t n_esc, uint64_t *total) {
   if (!layout_ok(layout) || !total) return ORC_E_ARG;
   if (n >= (1ull << 32)) return ORC_E_SIZE;
-  if (n_esc > n) return ORC_E_ARG;
+  if (n_esc > n || (!coded(layout) && n_esc)) return ORC_E_ARG;
   uint64_t off[6];
   layout_offsets(layout, n, n_esc, off);
   *total = off[4];
+  return ORC_OK;
+}
+
+/* ---- layout choice [the pages ask for a BF16 fallback: page "Compresión
+ * de pesos LLM sin pérdida vs 8-bit GGUF…", section "Preguntas para un
+ * vendor o equipo de investigación"] --------------------------------------
+ * Each layout's container size follows from its escape count; the smallest
+ * wins, ties to the lower layout number. */
+
+int orc_choose_layout(const uint16_t *w, uint64_t n, int *layout) {
+  if (!layout || (n && !w)) return ORC_E_ARG;
+  if (n >= (1ull << 32)) return ORC_E_SIZE;
+  int best = -1;
+  uint64_t best_total = 0;
+  for (int lay = ORC_LAYOUT_BYTESPLIT; lay <= ORC_LAYOUT_RAW; ++lay) {
+    uint64_t e = 0;
+    if (coded(lay)) {
+      uint64_t counts[512];
+      uint16_t dict[16];
+      int n_dict;
+      orc_histogram(lay, w, n, counts);
+      orc_dictionary(lay, counts, n, dict, &n_dict, &e);
+    }
+    uint64_t total;
+    orc_container_size(lay, n, e, &total);
+    if (best < 0 || total < best_total) {
+      best = lay;
+      best_total = total;
+    }
+  }
+  *layout = best;
   return ORC_OK;
 }
 
@@ -158,6 +203,22 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
                uint8_t *out, uint64_t cap, uint64_t *size) {
   if (!layout_ok(layout) || !out || !size || (n && !w)) return ORC_E_ARG;
   if (n >= (1ull << 32)) return ORC_E_SIZE; /* positions are u32 */
+
+  if (!coded(layout)) {
+    /* raw: header, then every weight as a little-endian u16 */
+    uint64_t off[6];
+    layout_offsets(layout, n, 0, off);
+    if (cap < off[4]) return ORC_E_SIZE;
+    memset(out, 0, off[4]);
+    for (uint64_t i = 0; i < n; ++i) put_le(out + off[1] + 2u * i, w[i], 2);
+    put_le(out + 0, ORC_MAGIC, 4);
+    put_le(out + 4, ORC_VERSION, 2);
+    put_le(out + 6, (uint64_t)layout, 1);
+    put_le(out + 8, n, 8);
+    for (int k = 0; k < 6; ++k) put_le(out + 56 + 8 * k, off[k], 8);
+    *size = off[4];
+    return ORC_OK;
+  }
 
   uint64_t counts[512];
   orc_histogram(layout, w, n, counts);
@@ -236,6 +297,7 @@ int orc_header_info(const uint8_t *c, uint64_t size, int *layout, int *n_dict,
   if (!layout_ok(lay) || nd > 15) return ORC_E_CORRUPT;
   uint64_t nn = get_le(c + 8, 8), ne = get_le(c + 16, 8);
   if (nn >= (1ull << 32) || ne > nn) return ORC_E_CORRUPT;
+  if (!coded(lay) && (nd != 0 || ne != 0)) return ORC_E_CORRUPT;
   for (int k = 0; k < 16; ++k) {
     dict[k] = (uint16_t)get_le(c + 24 + 2 * k, 2);
     if (k >= nd && dict[k] != 0) return ORC_E_CORRUPT;
@@ -271,6 +333,10 @@ int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap) {
   int st = orc_header_info(c, size, &layout, &n_dict, &n, &n_esc, dict, off);
   if (st != ORC_OK) return st;
   if (n > n_cap || (n && !out)) return ORC_E_ARG;
+  if (!coded(layout)) {
+    for (uint64_t i = 0; i < n; ++i) out[i] = (uint16_t)get_le(c + off[1] + 2u * i, 2);
+    return ORC_OK;
+  }
   const uint8_t *codes = c + off[0];
   const uint8_t *raw = c + off[1];
   const uint8_t *esc_pos = c + off[2];
@@ -371,7 +437,7 @@ int orc_bits_per_weight(const uint8_t *c, uint64_t size, double *bpw,
   int st = orc_header_info(c, size, &layout, &n_dict, &n, &n_esc, dict, off);
   if (st != ORC_OK) return st;
   if (!bpw || !payload_bpw || n == 0) return ORC_E_ARG;
-  uint64_t payload = (n + 1u) / 2u + raw_stream_bytes(layout, n) + 4u * n_esc +
+  uint64_t payload = code_stream_bytes(layout, n) + raw_stream_bytes(layout, n) + 4u * n_esc +
                      sym_bytes(layout) * n_esc + 4u * index_entries(n, n_esc);
   *bpw = 8.0 * (double)off[4] / (double)n;
   *payload_bpw = 8.0 * (double)payload / (double)n;

@@ -42,6 +42,7 @@ extern "C" {
 
 #define ORC_LAYOUT_BYTESPLIT 0
 #define ORC_LAYOUT_K15 1
+#define ORC_LAYOUT_RAW 2 /* the BF16 bit patterns stored as they are */
 
 #define ORC_OK 0
 #define ORC_E_ARG (-1)
@@ -59,6 +60,10 @@ int orc_dictionary(int layout, const uint64_t *counts, uint64_t n,
 
 /* Exact container size for n weights with n_esc escapes. */
 int orc_container_size(int layout, uint64_t n, uint64_t n_esc, uint64_t *total);
+
+/* The layout whose container is smallest for w[0..n): byte-split, K15 or
+ * raw, ties to the lower layout number. */
+int orc_choose_layout(const uint16_t *w, uint64_t n, int *layout);
 
 /* Full encode into out[0..cap); *size receives the container size. */
 int orc_encode(int layout, const uint16_t *w, uint64_t n,

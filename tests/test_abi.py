@@ -83,6 +83,20 @@ def test_host_checks_reject_bad_headers(wc):
         wc.bits_per_weight(bad)
 
 
+def test_raw_layout_header(wc):
+    w = synth.random_bits(1000, 6, "uniform")
+    h, c = _header_from_oracle(2, w)
+    assert (h.layout, h.n_dict, h.n_esc, h.off_raw, h.total_bytes) == (2, 0, 0, 128, 2128)
+    bpw, pay = wc.bits_per_weight(h)
+    assert pay == 16.0 and bpw == pytest.approx(8 * 2128 / 1000, rel=1e-15)
+    for field, val in [("n_esc", 1), ("n_dict", 1), ("off_raw", 144)]:
+        bad = wc.Header.from_bytes(h.to_bytes())
+        setattr(bad, field, val)
+        with pytest.raises(wc.WCError) as e:
+            wc.bits_per_weight(bad)
+        assert e.value.code == -3, field
+
+
 def test_argument_checks_before_device_work(wc):
     lib = ctypes.CDLL(wc.LIB_PATH)
     lib.wc_build_dict.restype = ctypes.c_int
@@ -92,7 +106,7 @@ def test_argument_checks_before_device_work(wc):
                              ctypes.byref(h)) == -1
     assert lib.wc_build_dict(0, None, ctypes.c_uint64(0), None, ctypes.c_size_t(0), None,
                              None) == -1
-    assert lib.wc_build_dict(3, None, ctypes.c_uint64(0), None, ctypes.c_size_t(0), None,
+    assert lib.wc_build_dict(4, None, ctypes.c_uint64(0), None, ctypes.c_size_t(0), None,
                              ctypes.byref(h)) == -1
     assert lib.wc_build_dict(0, None, ctypes.c_uint64(1 << 32), None, ctypes.c_size_t(0), None,
                              ctypes.byref(h)) == -2

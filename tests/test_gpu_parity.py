@@ -253,6 +253,41 @@ def test_gemv_every_batch(layout):
             check_gemv(layout, W, X[:batch], h, c, f"{rows}x{cols} b={batch}", ref=ref)
 
 
+# ------------------------------------------- raw layout and layout choice
+
+@pytest.mark.parametrize("kind", ["normal", "uniform"])
+def test_raw_layout_roundtrip(kind):
+    for i, n in enumerate([1, 7, 8, 9, 2047, 2049, 65537, (1 << 20) + 3]):
+        h, _ = check_roundtrip(wc.RAW, synth.random_bits(n, 1500 + i, kind), f"raw {kind} n={n}")
+        assert (h.layout, h.n_dict, h.n_esc) == (wc.RAW, 0, 0)
+
+
+def test_raw_layout_gemv():
+    for i, (rows, cols, batch) in enumerate([(33, 4096, 1), (17, 100, 3), (64, 2048, 16), (9, 6144, 8)]):
+        W = synth.random_bits(rows * cols, 1600 + i, "uniform").reshape(rows, cols) & np.uint16(0xBFFF)
+        x = synth.vectors(1700 + i, batch, cols)
+        check_gemv(wc.RAW, W, x, what=f"raw {rows}x{cols} b={batch}")
+
+
+def test_auto_layout_matches_oracle_choice():
+    """wc_build_dict with WC_LAYOUT_AUTO picks the layout the oracle picks
+    (smallest container, ties to the lower number), and encodes it byte for
+    byte as the oracle does."""
+    from tests.test_oracle import _choice_cases
+    cases = [(name, w) for name, w, _ in _choice_cases()]
+    cases.append(("mlp W1", synth.mlp()["W1"].reshape(-1)))
+    cases.append(("banded", synth.banded()["W"].reshape(-1)))
+    for name, w in cases:
+        want = oracle.choose_layout(w)
+        h, c = gpu_encode(wc.AUTO, w)
+        assert h.layout == want, (name, h.layout, want)
+        assert np.array_equal(c.cpu().numpy(), oracle.encode(want, w)), name
+        if w.size:
+            out = wc.decode(h, c)
+            torch.cuda.synchronize()
+            assert np.array_equal(host16(out), w), name
+
+
 def test_gemv_cols_zero_and_rows_zero():
     w = torch.empty(0, dtype=torch.int16, device=DEV)
     h, c = wc.encode(w, wc.BYTESPLIT)

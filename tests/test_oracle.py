@@ -241,6 +241,59 @@ def test_escape_stream_invariants(layout):
         assert info["total_bytes"] == -(-(info["off_esc_idx"] + 4 * (tiles + 1)) // 16) * 16
 
 
+# ------------------------------------------------ raw layout and choice
+
+def test_raw_roundtrip_and_accounting():
+    for i, n in enumerate([0, 1, 7, 8, 9, 2047, 2048, 20001]):
+        w = synth.random_bits(n, 900 + i, "uniform")
+        c = oracle.encode(oracle.RAW, w)
+        info = oracle.header_info(c)
+        assert (info["layout"], info["n_dict"], info["n_esc"]) == (oracle.RAW, 0, 0)
+        assert c.size == 128 + -(-2 * n // 16) * 16
+        assert np.array_equal(c[128:128 + 2 * n].view("<u2"), w)
+        assert np.array_equal(oracle.decode(c), w)
+        if n:
+            bpw, pay = oracle.bits_per_weight(c)
+            assert pay == 16.0 and bpw == 8 * c.size / n
+    w = synth.all_patterns(5)
+    assert np.array_equal(oracle.decode(oracle.encode(oracle.RAW, w)), w)
+
+
+def _choice_cases():
+    """(name, weights, expected layout) worked out by hand from the container
+    sizes: header 128, codes ceil(n/2), raw n / ceil(7n/8) / 2n, 4 + 1 or 2
+    bytes per escape, index 4 (tiles + 1) bytes with escapes, each padded to 16."""
+    # one symbol: byte-split 128 + 2048 + 4096 = 6272, K15 128 + 2048 + 3584 =
+    # 5760, raw 128 + 8192 = 8320
+    const = np.full(4096, 0x3F80, dtype=np.uint16)
+    # 30 exponents (100 weights each), 15 high bytes: byte-split has no
+    # escapes (128 + 1504 + 3008 = 4640); K15 escapes 1500 of 3000 weights
+    # (over 12000 bytes); raw 128 + 6000 = 6128
+    e = np.repeat(np.arange(100, 130, dtype=np.uint16), 100)
+    thirty = (e << 7) | np.uint16(0x15)
+    # uniform bit patterns: nearly every weight escapes in both coded layouts
+    uni = synth.random_bits(4096, 77, "uniform")
+    # empty: every container is the 128-byte header; the tie goes to byte-split
+    empty = np.zeros(0, dtype=np.uint16)
+    return [("constant", const, oracle.K15), ("thirty_exponents", thirty, oracle.BYTESPLIT),
+            ("uniform", uni, oracle.RAW), ("empty", empty, oracle.BYTESPLIT)]
+
+
+@pytest.mark.parametrize("case", _choice_cases(), ids=lambda c: c[0] if isinstance(c, tuple) else "")
+def test_layout_choice_hand_cases(case):
+    _, w, want = case
+    assert oracle.choose_layout(w) == want
+
+
+def test_layout_choice_is_the_smallest_container():
+    tensors = [synth.random_bits(n, 950 + n, kind) for n in (1, 100, 5000, 40000)
+               for kind in ("normal", "uniform", "few")]
+    tensors.append(synth.random_bits(6000, 3, "normal", sigma=300.0))  # wide exponent spread
+    for w in tensors:
+        sizes = [oracle.encode(lay, w).size for lay in (oracle.BYTESPLIT, oracle.K15, oracle.RAW)]
+        assert oracle.choose_layout(w) == int(np.argmin(sizes)), sizes  # argmin: first of equals
+
+
 # ------------------------------------------------------------- accounting
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -406,6 +459,11 @@ MUTATIONS = {
     "symbol_shift": [(r"return layout == ORC_LAYOUT_K15 \? 7 : 8;", "return layout == ORC_LAYOUT_K15 ? 8 : 8;")],
     # index entries counted up to and including the tile's first weight, in
     # the encoder and in the decoder's check alike
+    "raw_byte_order": [(r"put_le\(out \+ off\[1\] \+ 2u \* i, w\[i\], 2\);",
+                        "put_le(out + off[1] + 2u * i, (uint16_t)((w[i] >> 8) | (w[i] << 8)), 2);"),
+                       (r"out\[i\] = \(uint16_t\)get_le\(c \+ off\[1\] \+ 2u \* i, 2\);",
+                        "{ uint16_t v = (uint16_t)get_le(c + off[1] + 2u * i, 2); out[i] = (uint16_t)((v >> 8) | (v << 8)); }")],
+    "choice_tie": [(r"if \(best < 0 \|\| total < best_total\)", "if (best < 0 || total <= best_total)")],
     "index_inclusive": [(r"if \(n_esc && i % ORC_INDEX_TILE == 0\) put_le\(esc_idx \+ 4u \* \(i / ORC_INDEX_TILE\), e, 4\);\n    uint32_t s = symbol_of\(layout, w\[i\]\);",
                          "uint32_t s = symbol_of(layout, w[i]);\n    if (n_esc && i % ORC_INDEX_TILE == 0) put_le(esc_idx + 4u * (i / ORC_INDEX_TILE), e + (code_of[s] == 15), 4);"),
                         (r"get_le\(esc_idx \+ 4u \* \(i / ORC_INDEX_TILE\), 4\) != e\)",
@@ -434,6 +492,9 @@ def _pins_pass():
         for layout in LAYOUTS:
             w = synth.all_patterns(3)
             if not np.array_equal(oracle.decode(oracle.encode(layout, w)), w):
+                return False
+        for _, w, want in _choice_cases():
+            if oracle.choose_layout(w) != want:
                 return False
     except oracle.OracleError:
         return False
