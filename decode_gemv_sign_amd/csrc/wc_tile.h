@@ -421,7 +421,7 @@ __device__ inline void ring_load_esc(const uint32_t* esc_pos, const uint8_t* esc
   const uint64_t idx = e0 + (uint64_t)lane_id();
   const uint32_t ic = idx < n_esc ? (uint32_t)idx : (uint32_t)last;
   lds_dma4(esc_pos + ic, buf + 768);
-  lds_dma4(esc_sym + ((ic * kSymBytes) & ~3u), buf + 832);
+  lds_dma4(esc_sym + (((uint64_t)ic * kSymBytes) & ~(uint64_t)3), buf + 832);
 }
 
 template <int LAYOUT>

@@ -253,6 +253,77 @@ def test_gemv_every_batch(layout):
             check_gemv(layout, W, X[:batch], h, c, f"{rows}x{cols} b={batch}", ref=ref)
 
 
+# --------------------------------------------------- maximum sizes
+
+def _gpu_normal_bits(n: int, seed: int, sigma: float = 0.02) -> torch.Tensor:
+    """n BF16 bit patterns of N(0, sigma), drawn on the device from a seeded
+    generator (a 2^32-weight tensor is 8 GiB: drawing it on the host would
+    take minutes), in 2^28-weight chunks; torch rounds fp32 to BF16 to
+    nearest even."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    out = torch.empty(n, dtype=torch.int16, device=DEV)
+    step = 1 << 28
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        z = torch.randn(b - a, generator=g, device=DEV, dtype=torch.float32) * sigma
+        out[a:b] = z.to(torch.bfloat16).view(torch.int16)
+    return out
+
+
+def _device_counts(w: torch.Tensor, shift: int) -> np.ndarray:
+    """Symbol counts of w (b >> shift), counted on the device in chunks."""
+    nsym = 1 << (16 - shift)
+    counts = torch.zeros(nsym, dtype=torch.int64, device=DEV)
+    step = 1 << 28
+    for a in range(0, w.numel(), step):
+        sym = (w[a:a + step].to(torch.int32) & 0xFFFF) >> shift
+        counts += torch.bincount(sym, minlength=nsym)
+    return counts.cpu().numpy().astype(np.uint64)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_maximum_size_roundtrip(layout):
+    """n = 2^32 - 1, the largest tensor the format holds (u32 positions): the
+    last tile is partial and the last code byte holds one nibble; escape
+    positions run up to the top of the u32 range.  Checks: exact round trip,
+    and the dictionary and escape count equal the oracle's ranking of the
+    symbol counts (counted on the device, ranked by the oracle)."""
+    n = (1 << 32) - 1
+    print(f"max-size round trip: layout={layout} n={n}", flush=True)
+    w = _gpu_normal_bits(n, 2024 + layout)
+    h, c = wc.encode(w, layout)
+    counts = _device_counts(w, 7 if layout == wc.K15 else 8)
+    d, nd, ne = oracle.dictionary(layout, counts, n)
+    assert (h.n, h.n_dict, h.n_esc) == (n, nd, ne)
+    assert list(h.dict)[:nd] == list(d[:nd])
+    assert h.total_bytes == oracle.container_size(layout, n, ne)
+    del counts
+    out = wc.decode(h, c)
+    torch.cuda.synchronize()
+    assert torch.equal(out, w), "maximum-size tensor not rebuilt exactly"
+    # the last escape records sit near the top of the position range
+    last_pos = int(c[h.off_esc_pos + 4 * (h.n_esc - 1):h.off_esc_pos + 4 * h.n_esc].cpu().numpy().view("<u4")[0])
+    assert last_pos > n - (1 << 20)
+
+
+def test_maximum_size_gemv():
+    """65535 x 65536 (n just below 2^32), byte-split, batch 1 (LDS-ring
+    kernel) and 16 (matrix cores): sampled rows against the oracle."""
+    rows, cols = 65535, 65536
+    print(f"max-size GEMV: {rows}x{cols}", flush=True)
+    w = _gpu_normal_bits(rows * cols, 2030)
+    h, c = wc.encode(w, wc.BYTESPLIT)
+    X = synth.vectors(2031, 16, cols)
+    sample = [0, 1, 2047, 32768, rows - 2, rows - 1]
+    Ws = w.view(rows, cols)[sample].cpu().numpy().view(np.uint16)
+    for batch in (1, 16):
+        y = wc.decode_gemv(h, c, rows, cols, dev16(X[:batch]))
+        torch.cuda.synchronize()
+        y64, a = oracle.gemv_f64(Ws, X[:batch])
+        assert_gemv_close(y.cpu().numpy()[:, sample], y64, a, f"max-size GEMV b={batch}")
+
+
 # ------------------------------------------- raw layout and layout choice
 
 @pytest.mark.parametrize("kind", ["normal", "uniform"])
