@@ -43,6 +43,8 @@ WORKLOADS = {
     "square": "4096x4096 N(0,0.02), 1% zeros, 0.1% outliers N(0,2); batch 1",
     "mlp": "14336x4096 + 4096x14336, row std 10^U(-4,-1); batch 1",
     "banded": "6144x24576 N(0,0.02) + 5% escapes in 64-row bands; batch 1/4/16",
+    "layerset": "96 tensors, 20.25 GiB: 48 x (6144x24576), 24 x (24576x6144) N(0,0.015), "
+                "24 x [6144] N(1,0.05); streamed encode + decode, per-tensor dictionaries",
 }
 
 
@@ -141,12 +143,130 @@ def cpu_baseline(mats, xs, layouts, min_seconds: float, gpu_results):
             "ms_per_step": round(1e3 * el / steps, 3)}, parity
 
 
+def run_layerset(args):
+    """The 96-tensor layer set, every container resident: one step encodes all
+    96 tensors (dictionary pass, which waits for the GPU, then encode, per
+    tensor) and then decodes them one after another, per layout.  The tensors
+    are drawn on the device from a seeded generator with the set's shapes and
+    distributions (20 GiB drawn on the host would take minutes); the GPU tests
+    check six of the set's tensors as drawn by `synth`.  Every decode is
+    checked bit for bit against its source; the oracle encodes a norm vector
+    and a 6144 x 24576 matrix of the set, byte-compared with the GPU's."""
+    import numpy as np
+    import torch
+
+    import decode_gemv_sign_amd as wc
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    layouts = [wc.BYTESPLIT, wc.K15]
+    tensors = []
+    for t in range(96):
+        name, shape, mean, sigma = synth.layerset_spec(t)
+        n = int(np.prod(shape))
+        g = torch.Generator(device=dev)
+        g.manual_seed(4000 + t)
+        z = torch.randn(n, generator=g, device=dev, dtype=torch.float32) * sigma + mean
+        tensors.append(z.to(torch.bfloat16).view(torch.int16))
+        del z
+    n_total = sum(w.numel() for w in tensors)
+    work = torch.empty(wc.workspace_bytes(max(w.numel() for w in tensors)), dtype=torch.uint8,
+                       device=dev)
+    conts = {li: [] for li in layouts}
+    hdrs = {li: [] for li in layouts}
+    for li in layouts:  # containers allocated once, by a first (untimed) encode
+        for w in tensors:
+            h = wc.build_dict(w, li, work)
+            hdrs[li].append(h)
+            conts[li].append(wc.encode_into(h, w, torch.empty(h.total_bytes, dtype=torch.uint8,
+                                                               device=dev), work))
+    out_buf = torch.empty(max(w.numel() for w in tensors), dtype=torch.int16, device=dev)
+
+    def encode_all(li):
+        for k, w in enumerate(tensors):
+            h = wc.build_dict(w, li, work)
+            wc.encode_into(h, w, conts[li][k], work)
+
+    def decode_all(li, check=False):
+        ok = True
+        for k, w in enumerate(tensors):
+            o = out_buf[:w.numel()]
+            wc.decode(hdrs[li][k], conts[li][k], out=o)
+            if check:
+                ok = ok and bool(torch.equal(o, w))
+        return ok
+
+    res = {}
+    exact = True
+    for li in layouts:
+        encode_all(li)
+        exact = decode_all(li, check=True) and exact
+        torch.cuda.synchronize()
+        enc, dec = [], []
+        for _ in range(args.warmup + args.steps):
+            t0 = time.perf_counter()
+            encode_all(li)
+            torch.cuda.synchronize()
+            enc.append(time.perf_counter() - t0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            decode_all(li)
+            b.record(stream)
+            b.synchronize()
+            dec.append(a.elapsed_time(b) * 1e-3)
+        enc = sorted(enc[args.warmup:])[len(enc[args.warmup:]) // 2]
+        dec = sorted(dec[args.warmup:])[len(dec[args.warmup:]) // 2]
+        cbytes = sum(h.total_bytes for h in hdrs[li])
+        res[LAYOUT_NAMES[li]] = {
+            "encode_ms": round(1e3 * enc, 3), "encode_decoded_gbps": round(2 * n_total / enc / 1e9, 1),
+            "decode_ms": round(1e3 * dec, 3), "decode_decoded_gbps": round(2 * n_total / dec / 1e9, 1),
+            "decode_hbm_gbps": round((cbytes + 2 * n_total) / dec / 1e9, 1),
+            "decode_hbm_frac": round((cbytes + 2 * n_total) / dec / 1e9 / HBM_PEAK_GBPS, 4),
+            "bpw": round(8 * cbytes / n_total, 4),
+            "n_esc": int(sum(h.n_esc for h in hdrs[li])),
+        }
+    parity = exact
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        for t in (0, 72):
+            host = tensors[t].cpu().numpy().view(np.uint16)
+            for li in layouts:
+                if not np.array_equal(conts[li][t].cpu().numpy(), oracle.encode(li, host)):
+                    parity = False
+    best = max(layouts, key=lambda li: res[LAYOUT_NAMES[li]]["decode_decoded_gbps"])
+    out = {
+        "metric": METRIC,
+        "value": res[LAYOUT_NAMES[best]]["decode_decoded_gbps"],
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sum(r["encode_ms"] + r["decode_ms"] for r in res.values()), 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": f"layerset: {WORKLOADS['layerset']}", "weights": int(n_total),
+                   "value_definition": "2 bytes x weights / time to decode all 96 containers "
+                                       f"back to back ({LAYOUT_NAMES[best]}, the faster layout); "
+                                       "medians over the timed steps"},
+        "layouts": res,
+        "decode_exact": exact,
+        "parity_vs_oracle": "ok" if parity else "FAILED",
+    }
+    print(json.dumps(out), flush=True)
+    if not parity:
+        sys.exit(1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the codec shards per tensor with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "layerset":
+        run_layerset(args)
+        return
     import numpy as np
     import torch
 
