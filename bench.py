@@ -37,6 +37,7 @@ METRIC = ("decoded BF16 GB/s (% HBM peak); fused decode-GEMV µs vs BF16 GEMV; "
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 LAYOUT_NAMES = {0: "byte-split", 1: "K15"}
 WORKSET_BYTES = 512 << 20  # rotate copies until the inputs span 2x the 256 MB cache
+ENC_THREADS = 4  # layer set: host threads (one stream each) that encode tensors side by side
 
 WORKLOADS = {
     "small": "1024x1024 N(0,0.02), 0.05% entries x1000; batch 1",
@@ -146,7 +147,8 @@ def cpu_baseline(mats, xs, layouts, min_seconds: float, gpu_results):
 def run_layerset(args):
     """The 96-tensor layer set, every container resident: one step encodes all
     96 tensors (dictionary pass, which waits for the GPU, then encode, per
-    tensor) and then decodes them one after another, per layout.  The tensors
+    tensor; 4 host threads on 4 streams take turns, so the waits overlap) and
+    then decodes them one after another on one stream, per layout.  The tensors
     are drawn on the device from a seeded generator with the set's shapes and
     distributions (20 GiB drawn on the host would take minutes); the GPU tests
     check six of the set's tensors as drawn by `synth`.  Every decode is
@@ -184,10 +186,37 @@ def run_layerset(args):
                                                                device=dev), work))
     out_buf = torch.empty(max(w.numel() for w in tensors), dtype=torch.int16, device=dev)
 
+    # Encode runs from ENC_THREADS host threads, each with its own stream and
+    # workspace, so one tensor's dictionary pass (which waits for its stream)
+    # overlaps the other threads' GPU work.
+    import threading
+    enc_streams = [torch.cuda.Stream(device=dev) for _ in range(ENC_THREADS)]
+    enc_work = [torch.empty_like(work) for _ in range(ENC_THREADS)]
+
     def encode_all(li):
-        for k, w in enumerate(tensors):
-            h = wc.build_dict(w, li, work)
-            wc.encode_into(h, w, conts[li][k], work)
+        errors = []
+
+        def worker(i):
+            try:
+                s = enc_streams[i]
+                with torch.cuda.stream(s):
+                    for k in range(i, len(tensors), ENC_THREADS):
+                        h = wc.build_dict(tensors[k], li, enc_work[i], stream=s)
+                        wc.encode_into(h, tensors[k], conts[li][k], enc_work[i], stream=s)
+            except Exception as e:  # reported after the join
+                errors.append(e)
+
+        for s in enc_streams:  # after the work already queued (sources, earlier decodes)
+            s.wait_stream(stream)
+        threads = [threading.Thread(target=worker, args=(i,)) for i in range(ENC_THREADS)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        for s in enc_streams:
+            stream.wait_stream(s)
+        if errors:
+            raise errors[0]
 
     def decode_all(li, check=False):
         ok = True
