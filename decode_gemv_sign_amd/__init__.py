@@ -24,7 +24,8 @@ import torch  # loaded first, so libwc binds to the HIP runtime torch already us
 __all__ = [
     "BYTESPLIT", "K15", "RAW", "AUTO", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into",
     "encode", "decode", "decode_gemv", "gemv_bf16", "bits_per_weight", "read_header",
-    "LIB_PATH",
+    "crc32", "container_crcs", "artifact_write", "artifact_entries", "artifact_read",
+    "artifact_verify", "LIB_PATH",
 ]
 
 BYTESPLIT = 0
@@ -35,7 +36,7 @@ MAX_BATCH = 16
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwc.so")
 
 _CODES = {0: "WC_OK", -1: "WC_E_ARG", -2: "WC_E_SIZE", -3: "WC_E_CORRUPT", -4: "WC_E_HIP",
-          -5: "WC_E_UNSUPPORTED"}
+          -5: "WC_E_UNSUPPORTED", -6: "WC_E_IO"}
 
 
 class WCError(RuntimeError):
@@ -68,6 +69,16 @@ class Header(ctypes.Structure):
 assert ctypes.sizeof(Header) == 128
 
 
+class ArtifactInfo(ctypes.Structure):
+    """wc_artifact_info: one entry of a serialized artifact."""
+    _fields_ = [
+        ("name", ctypes.c_char * 96), ("ndim", ctypes.c_uint32), ("layout", ctypes.c_uint32),
+        ("shape", ctypes.c_uint64 * 4), ("offset", ctypes.c_uint64), ("bytes", ctypes.c_uint64),
+        ("src_crc", ctypes.c_uint32), ("stream_crc", ctypes.c_uint32 * 6),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
 def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
@@ -83,8 +94,20 @@ def _load(path: str = LIB_PATH):
     lib.wc_gemv_bf16.argtypes = [P, U64, U64, P, ctypes.c_uint32, P, P]
     lib.wc_bits_per_weight.argtypes = [HP, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_double)]
+    lib.wc_crc32.argtypes = [ctypes.c_uint32, P, ctypes.c_size_t]
+    lib.wc_crc32.restype = ctypes.c_uint32
+    lib.wc_container_crcs.argtypes = [P, ctypes.c_size_t, P]
+    lib.wc_artifact_write.argtypes = [ctypes.c_char_p, ctypes.c_uint32,
+                                      ctypes.POINTER(ctypes.c_char_p), P, P,
+                                      ctypes.POINTER(ctypes.c_void_p), P, P]
+    lib.wc_artifact_count.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_uint32)]
+    lib.wc_artifact_entry.argtypes = [ctypes.c_char_p, ctypes.c_uint32,
+                                      ctypes.POINTER(ArtifactInfo)]
+    lib.wc_artifact_read.argtypes = [ctypes.c_char_p, ctypes.c_uint32, P, ctypes.c_size_t]
     for f in (lib.wc_build_dict, lib.wc_encode, lib.wc_decode, lib.wc_decode_gemv,
-              lib.wc_gemv_bf16, lib.wc_bits_per_weight):
+              lib.wc_gemv_bf16, lib.wc_bits_per_weight, lib.wc_container_crcs,
+              lib.wc_artifact_write, lib.wc_artifact_count, lib.wc_artifact_entry,
+              lib.wc_artifact_read):
         f.restype = ctypes.c_int
     return lib
 
@@ -215,3 +238,93 @@ def bits_per_weight(h: Header):
     _check(_lib.wc_bits_per_weight(ctypes.byref(h), ctypes.byref(b), ctypes.byref(p)),
            "wc_bits_per_weight")
     return b.value, p.value
+
+
+# ---- serialized artifact (host side; include/wc.h) --------------------------
+
+def _host_u8(a):
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+
+
+def crc32(data, crc: int = 0) -> int:
+    """wc_crc32 over a host buffer (numpy array, bytes or CPU/device tensor)."""
+    if isinstance(data, (bytes, bytearray)):
+        buf = ctypes.create_string_buffer(bytes(data), len(data))
+        return _lib.wc_crc32(crc, buf, len(data))
+    a = _host_u8(data)
+    return _lib.wc_crc32(crc, ctypes.c_void_p(a.ctypes.data), a.size)
+
+
+def container_crcs(container):
+    """The six region CRCs of a container (host copy)."""
+    a = _host_u8(container)
+    out = (ctypes.c_uint32 * 6)()
+    _check(_lib.wc_container_crcs(ctypes.c_void_p(a.ctypes.data), a.size, out), "wc_container_crcs")
+    return list(out)
+
+
+def artifact_write(path: str, items):
+    """items: (name, shape, container, src_crc) per tensor; containers are
+    copied to the host if they are device tensors."""
+    import numpy as np
+    items = list(items)
+    n = len(items)
+    names = (ctypes.c_char_p * max(n, 1))(*[it[0].encode() for it in items])
+    ndims = np.zeros(max(n, 1), dtype=np.uint32)
+    shapes = np.zeros((max(n, 1), 4), dtype=np.uint64)
+    hosts = [_host_u8(it[2]) for it in items]
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[h.ctypes.data for h in hosts])
+    sizes = np.array([h.size for h in hosts] or [0], dtype=np.uint64)
+    crcs = np.array([it[3] for it in items] or [0], dtype=np.uint32)
+    for i, it in enumerate(items):
+        shp = tuple(int(d) for d in it[1])
+        ndims[i] = len(shp)
+        shapes[i, :len(shp)] = shp
+    _check(_lib.wc_artifact_write(path.encode(), n, names, ctypes.c_void_p(ndims.ctypes.data),
+                                  ctypes.c_void_p(shapes.ctypes.data), ptrs,
+                                  ctypes.c_void_p(sizes.ctypes.data),
+                                  ctypes.c_void_p(crcs.ctypes.data)), "wc_artifact_write")
+
+
+def artifact_entries(path: str):
+    """Every entry's metadata (file header and every entry checked)."""
+    cnt = ctypes.c_uint32()
+    _check(_lib.wc_artifact_count(path.encode(), ctypes.byref(cnt)), "wc_artifact_count")
+    out = []
+    for i in range(cnt.value):
+        info = ArtifactInfo()
+        _check(_lib.wc_artifact_entry(path.encode(), i, ctypes.byref(info)), "wc_artifact_entry")
+        out.append({"name": info.name.decode(), "shape": tuple(info.shape[:info.ndim]),
+                    "layout": info.layout, "offset": info.offset, "bytes": info.bytes,
+                    "src_crc": info.src_crc, "stream_crc": list(info.stream_crc)})
+    return out
+
+
+def artifact_read(path: str, i: int):
+    """Container i as a host uint8 array, after every CRC check."""
+    import numpy as np
+    info = ArtifactInfo()
+    _check(_lib.wc_artifact_entry(path.encode(), i, ctypes.byref(info)), "wc_artifact_entry")
+    buf = np.empty(info.bytes, dtype=np.uint8)
+    _check(_lib.wc_artifact_read(path.encode(), i, ctypes.c_void_p(buf.ctypes.data), buf.size),
+           "wc_artifact_read")
+    return buf
+
+
+def artifact_verify(path: str, device="cuda:0"):
+    """Streams every tensor of the artifact through the GPU: read (CRCs
+    checked), upload, exact decode, and the decoded values' CRC-32 against
+    the source's.  Returns (name, matches, bits/weight) per tensor."""
+    out = []
+    for i, e in enumerate(artifact_entries(path)):
+        host = artifact_read(path, i)
+        c = torch.from_numpy(host).to(device)
+        h = Header.from_bytes(host[:128].tobytes())
+        dec = decode(h, c)
+        got = crc32(dec)
+        bpw = bits_per_weight(h)[0] if h.n else 0.0
+        out.append((e["name"], got == e["src_crc"], bpw))
+    return out

@@ -81,6 +81,7 @@ extern "C" {
 #define WC_E_CORRUPT (-3)     /* header fails validation */
 #define WC_E_HIP (-4)         /* a HIP call or kernel launch failed */
 #define WC_E_UNSUPPORTED (-5) /* batch outside 1..WC_MAX_BATCH */
+#define WC_E_IO (-6)          /* a file could not be opened, read or written */
 
 #define WC_MAGIC 0x36314357u /* bytes "WC16" */
 #define WC_VERSION 2u
@@ -183,6 +184,72 @@ int wc_gemv_bf16(const uint16_t *d_w, uint64_t rows, uint64_t cols,
  * Host only.  n == 0 -> WC_E_ARG.
  */
 int wc_bits_per_weight(const wc_header *h, double *bpw, double *payload_bpw);
+
+/*
+ * ---- Serialized artifact (host only) --------------------------------------
+ * The pages ask that a saving be shown on a serialized artifact that holds
+ * the metadata and the escapes, that every tensor be decoded from what was
+ * delivered and compared, and that corruption have a defined outcome (page
+ * "Compresión de pesos LLM sin pérdida vs 8-bit GGUF…", sections "¿Está
+ * listo para producción el resultado de GLM-5.2?" and "Preguntas para un
+ * vendor o equipo de investigación").
+ *
+ * File (little-endian): a 64-byte file header, a table of 256-byte entries,
+ * then the containers, each at a 4096-byte aligned offset, gaps zero.
+ *   file header: magic "WCA1", version u16 = 1, u16 0, count u32, u32 0,
+ *     table offset u64 (64), data offset u64, file bytes u64, 20 zero bytes,
+ *     CRC-32 of bytes [0, 60) at 60.
+ *   entry: name (96 bytes, NUL-terminated, NUL-padded), ndim u32 (1..4),
+ *     layout u32, shape u64[4] (unused dims 0, product = n), container offset
+ *     u64 and bytes u64, the source's CRC-32 (of its n BF16 values as
+ *     little-endian u16, given by the writer), the six stream CRC-32s
+ *     (wc_container_crcs), zeros, and at 252 the CRC-32 of bytes [0, 252).
+ * Reading checks every CRC, the container header and that the entry agrees
+ * with it: any mismatch is WC_E_CORRUPT, a short or unreadable file WC_E_IO
+ * or WC_E_CORRUPT.  The decoded tensor is then compared with src_crc by the
+ * caller (it is the only check of the rebuilt weights themselves).
+ */
+#define WC_ARTIFACT_MAGIC 0x31414357u /* bytes "WCA1" */
+#define WC_ARTIFACT_ALIGN 4096u
+#define WC_ARTIFACT_NAME 96u
+
+typedef struct wc_artifact_info {
+  char name[WC_ARTIFACT_NAME];
+  uint32_t ndim, layout;
+  uint64_t shape[4];
+  uint64_t offset, bytes; /* the container inside the file */
+  uint32_t src_crc;       /* CRC-32 of the source BF16 values */
+  uint32_t stream_crc[6]; /* header, codes, raw, escape positions, symbols, index */
+  uint32_t reserved;
+} wc_artifact_info;
+
+/* CRC-32 (IEEE 802.3, reflected, polynomial 0xEDB88320), continued from
+ * `crc` (0 to start) over data[0, len); the same value zlib's crc32 gives. */
+uint32_t wc_crc32(uint32_t crc, const void *data, size_t len);
+
+/* CRC-32 of each of a container's six regions, which cover every byte once:
+ * [0,128) header, [off_codes, off_raw), [off_raw, off_esc_pos),
+ * [off_esc_pos, off_esc_sym), [off_esc_sym, off_esc_idx),
+ * [off_esc_idx, total_bytes).  h_container is host memory of `bytes` bytes;
+ * its header is validated (WC_E_CORRUPT), bytes >= total_bytes (WC_E_SIZE). */
+int wc_container_crcs(const uint8_t *h_container, size_t bytes, uint32_t crc[6]);
+
+/* Writes `count` containers (host memory, each validated) with their names,
+ * shapes and source CRCs into a new file at `path` (replaced if present). */
+int wc_artifact_write(const char *path, uint32_t count, const char *const *names,
+                      const uint32_t *ndims, const uint64_t *shapes /* [count][4] */,
+                      const uint8_t *const *h_containers, const uint64_t *container_bytes,
+                      const uint32_t *src_crcs);
+
+/* Number of entries, after checking the file header and every entry's CRC. */
+int wc_artifact_count(const char *path, uint32_t *count);
+
+/* Entry i's metadata (file header and entry checked). */
+int wc_artifact_entry(const char *path, uint32_t i, wc_artifact_info *out);
+
+/* Reads container i into h_buf (at least info.bytes bytes) and checks its
+ * header against the entry and every stream CRC. */
+int wc_artifact_read(const char *path, uint32_t i, uint8_t *h_buf, size_t buf_bytes);
 
 #ifdef __cplusplus
 }

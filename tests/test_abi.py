@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "wc.h")
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|double)\s+(wc_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|double|uint32_t)\s+(wc_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +30,8 @@ def wc():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "wc_build_dict", "wc_encode", "wc_decode", "wc_decode_gemv", "wc_gemv_bf16",
-        "wc_bits_per_weight"])
+        "wc_bits_per_weight", "wc_crc32", "wc_container_crcs", "wc_artifact_write",
+        "wc_artifact_count", "wc_artifact_entry", "wc_artifact_read"])
 
 
 def test_library_exports_every_declared_symbol(wc):

@@ -359,6 +359,33 @@ def test_auto_layout_matches_oracle_choice():
             assert np.array_equal(host16(out), w), name
 
 
+def test_artifact_streamed_verify(tmp_path):
+    """Tensors encoded on the GPU, written to an artifact, then streamed back:
+    read (every CRC checked), uploaded, decoded exactly, and the decoded
+    values' CRC-32 equal to the source's."""
+    import zlib
+    tensors = [("small", synth.small()["W"]), ("square", synth.square()["W"]),
+               ("layer.norm", synth.layerset_tensor(72)[1]),
+               ("uniform", synth.random_bits(64 * 4096, 1800, "uniform").reshape(64, 4096))]
+    items, sources = [], {}
+    for name, W in tensors:
+        h, c = gpu_encode(wc.AUTO, W)
+        items.append((name, W.shape, c, zlib.crc32(np.ascontiguousarray(W).tobytes())))
+        sources[name] = (W, h.layout)
+    path = str(tmp_path / "set.wca")
+    wc.artifact_write(path, items)
+    res = wc.artifact_verify(path, DEV)
+    assert [r[0] for r in res] == [t[0] for t in tensors]
+    assert all(r[1] for r in res), res
+    for i, e in enumerate(wc.artifact_entries(path)):
+        W, lay = sources[e["name"]]
+        assert e["layout"] == lay
+        c = torch.from_numpy(wc.artifact_read(path, i)).to(DEV)
+        out = wc.decode(wc.read_header(c), c)
+        torch.cuda.synchronize()
+        assert np.array_equal(host16(out), np.ascontiguousarray(W).reshape(-1)), e["name"]
+
+
 def test_gemv_cols_zero_and_rows_zero():
     w = torch.empty(0, dtype=torch.int16, device=DEV)
     h, c = wc.encode(w, wc.BYTESPLIT)
