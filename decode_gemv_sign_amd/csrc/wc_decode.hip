@@ -37,11 +37,13 @@ struct DecodeArgs {
   Dict dict;
 };
 
-// DEPTH: tiles in flight ahead of the one being rebuilt (1 or 2); the ring
-// has DEPTH + 1 slots.
-template <int LAYOUT, int DEPTH>
+// The ring has two slots per wave, one tile ahead of the one being rebuilt:
+// 34 KB per 256-thread block, so four waves per SIMD fit.  (A third slot, two
+// tiles ahead, costs the fourth wave; it measured the same on the large
+// tensors and 11-13% slower on a 4096 x 4096 tensor, whose 4096 waves of two
+// tiles fill one round only with four waves per SIMD.)
+template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
-  static_assert(DEPTH == 1 || DEPTH == 2, "ring depth");
   __shared__ uint32_t T2[256];
   // per wave: a ring of tile buffers filled by global->LDS loads, 4 KB per
   // slot (codes 1 KB + raw 2 KB + the first escape records); the whole slot
@@ -49,8 +51,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   constexpr int kWpb = kBlockThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint32_t ring0[kWpb][kRingSlotDwords];
   __shared__ __attribute__((aligned(16))) uint32_t ring1[kWpb][kRingSlotDwords];
-  constexpr int kSlot2 = DEPTH == 2 ? kRingSlotDwords : 4;  // the third slot (DEPTH 2 only)
-  __shared__ __attribute__((aligned(16))) uint32_t ring2[DEPTH == 2 ? kWpb : 1][kSlot2];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -73,23 +73,19 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   // the tile's ring slot, free once the tile is in registers.  The tile's
   // first escape records come in `eb` (loaded while the previous tile was
   // processed).  As soon as this tile's escape count is known,
-  // `issue_next(e_next, symrun)` issues the next tile's record loads, then
-  // calls symrun() (a dense tile's symbol run into `stg`), then any further
-  // ring loads, and says whether 3 ring loads followed the run.
+  // `issue_next(e_next)` issues the next tile's record loads; then a dense
+  // tile's symbol run comes into `stg`, the last global->LDS loads issued.
   auto rebuild = [&](uint64_t t, const Lane4& l, const EscBatch& eb, auto&& issue_next,
                      uint32_t out[16], uint32_t* stg) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     const bool dense = cnt_wave > kDenseMin;
-    uint32_t off0 = 0;
-    const bool ahead = issue_next(e + cnt_wave, [&]() {
-      if (dense) off0 = ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg);
-    });
+    issue_next(e + cnt_wave);
+    const uint32_t off0 = dense ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg) : 0u;
     rebuild_lane<LAYOUT>(T2, l, out);
     if (dense) {
-      if (ahead) wait_vm<kRingAhead>();  // the symbol run is complete (ring_wait_ahead)
-      else wait_vm<0>();
+      wait_vm<0>();  // the symbol run is complete
       patch_tile_symrun<LAYOUT>(l, out, stg, off0);
     } else if (cnt_wave) {
       const uint64_t tile_start = t * kTile;
@@ -101,7 +97,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   };
 
   if (t0 < f1) {
-    // Full tiles stream through the LDS ring (wc_tile.h ring_*), DEPTH tiles
+    // Full tiles stream through the LDS ring (wc_tile.h ring_*), one tile
     // ahead.  The loads need no registers, so the prefetch does not cost
     // occupancy.
     auto dma_tile = [&](uint64_t t, uint32_t* buf) {
@@ -116,57 +112,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     };
     uint32_t* const s0 = ring0[wib];
     uint32_t* const s1 = ring1[wib];
-    if constexpr (DEPTH == 2) {
-      // Three slots, two tiles ahead.  A step waits for its tile's ring and
-      // record loads, reads the tile, counts its escapes, then issues the next
-      // tile's records and the ring loads of the tile after it (into the slot
-      // the previous step used), so the records are always followed by exactly
-      // one tile's ring loads, or by none at the run's end (ring_wait_ahead).
-      uint32_t* const s2 = ring2[wib];
-      auto slot3 = [&](auto slc) -> uint32_t* {
-        constexpr int k = decltype(slc)::value % 3;
-        return k == 0 ? s0 : (k == 1 ? s1 : s2);
-      };
-      dma_tile(t0, s0);  // in flight while the escape cursor is read
-      find_cursor();
-      dma_eb(e, s0);
-      if (t0 + 1 < f1) dma_tile(t0 + 1, s1);
-      uint64_t t = t0;
-      auto step = [&](auto slc) {
-        constexpr int sl = decltype(slc)::value;
-        wait_lgkm0();  // tile t-1's LDS reads and stage writes are done before its slot is refilled
-        if (t + 1 < f1) wait_vm<kRingAhead>();
-        else wait_vm<0>();
-        Lane4 l;
-        uint32_t* buf = slot3(slc);
-        read_tile(buf, l);
-        const EscBatch eb = read_eb(buf, e);
-        uint32_t* const n1 = slot3(std::integral_constant<int, sl + 1>{});
-        uint32_t* const n2 = slot3(std::integral_constant<int, sl + 2>{});
-        uint32_t out[16];
-        rebuild(t, l, eb, [&](uint64_t en, auto&& symrun) {
-          if (t + 1 < f1) dma_eb(en, n1);
-          symrun();
-          if (t + 2 >= f1) return false;
-          dma_tile(t + 2, n2);
-          return true;
-        }, out, buf);
-        u32x4* dst = (u32x4*)(a.out + t * kTile) + lane;
-#pragma unroll
-        for (int k = 0; k < kLaneGroups; ++k)
-          __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
-                                      dst + kWave * k);
-        ++t;
-      };
-      while (t + 3 <= f1) {
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        step(std::integral_constant<int, 2>{});
-      }
-      if (t < f1) step(std::integral_constant<int, 0>{});
-      if (t < f1) step(std::integral_constant<int, 1>{});
-      wait_lgkm0();
-    } else {
+    {
       // Two slots, one tile ahead.
       auto slot_buf = [&](auto slc) -> uint32_t* {
         return decltype(slc)::value % 2 == 0 ? s0 : s1;
@@ -203,11 +149,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         read_tile(buf, l);
         const EscBatch eb = read_eb(buf, e);
         uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
-        rebuild(t, l, eb, [&](uint64_t en, auto&& symrun) {
-          dma_eb(en, nbuf);
-          symrun();
-          return false;
-        }, out, buf);
+        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf);
         ++t;
       };
       while (t + 2 <= f1) {
@@ -247,10 +189,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     uint32_t out[16];
     const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
     // no global->LDS load is in flight here: ring0 is free
-    rebuild(full_tiles, l, eb, [](uint64_t, auto&& symrun) {
-      symrun();
-      return false;
-    }, out, ring0[wib]);
+    rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib]);
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
       const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;
@@ -349,16 +288,12 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;
-  // Two tiles ahead, except for escape-heavy tensors (more than one weight
-  // in 8 escapes): their dense tiles wait for their symbol run, and the
-  // fourth wave per SIMD that a two-slot ring leaves room for pays more.
-  const bool deep = h.n_esc <= h.n / 8;
   // Runs of 4 tiles per wave: short runs keep the waves that run at the same
   // time on neighbouring memory (whole-tensor runs per resident wave measured
   // 12% slower).  A tensor that fits in one round of 3-tile runs of the
-  // waves the chip holds at once (3 or 4 per SIMD, LDS-bound) takes runs
-  // that fill exactly one round instead.
-  const uint64_t slots = (uint64_t)cu_count() * 4u * (deep ? 3u : 4u);
+  // waves the chip holds at once (4 per SIMD, LDS-bound) takes runs that
+  // fill exactly one round instead.
+  const uint64_t slots = (uint64_t)cu_count() * 4u * 4u;
   const bool one_round = a.n_tiles <= 3 * slots;
   a.tiles_per_wave = one_round ? (a.n_tiles + slots - 1) / slots : kDecodeTilesPerWave;
   const uint64_t waves = (a.n_tiles + a.tiles_per_wave - 1) / a.tiles_per_wave;
@@ -366,13 +301,10 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb));
   a.dict = dict_of(&h);
   const dim3 blk(kBlockThreads);
-  if (h.layout == WC_LAYOUT_K15) {
-    if (deep) hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, 2>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, 1>), grid, blk, 0, s, a);
-  } else {
-    if (deep) hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, 2>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, 1>), grid, blk, 0, s, a);
-  }
+  if (h.layout == WC_LAYOUT_K15)
+    hipLaunchKernelGGL(k_decode<WC_LAYOUT_K15>, grid, blk, 0, s, a);
+  else
+    hipLaunchKernelGGL(k_decode<WC_LAYOUT_BYTESPLIT>, grid, blk, 0, s, a);
   return hipGetLastError();
 }
 
