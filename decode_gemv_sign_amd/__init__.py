@@ -148,7 +148,7 @@ def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
 
 def workspace_bytes(n: int) -> int:
     """WC_WORKSPACE_BYTES(n)."""
-    return 4096 + 8 * ((n + 8191) // 8192)
+    return 20480 + 8 * ((n + 8191) // 8192)
 
 
 def _workspace(n: int, device) -> torch.Tensor:

@@ -9,9 +9,10 @@
 // weight; byte-split keeps the low byte, K15 the 7-bit mantissa.
 //
 // Kernels, in stream order:
-//   build_dict: k_zero_hist -> k_hist (512 bins of b >> 7; the byte-split
-//               histogram is the pair sum) -> k_top15 (rank by count desc,
-//               symbol asc) -> 48-byte result copied to the host.
+//   build_dict: k_zero_hist -> k_hist (512 bins of b >> 7, merged into 8
+//               global copies; the byte-split histogram is the pair sum) ->
+//               k_top15 (sums the copies; rank by count desc, symbol asc) ->
+//               48-byte result copied to the host.
 //   encode:     k_pack (codes, raw stream, per-block escape counts, header and
 //               zero gaps) -> k_scan (exclusive scan of the block counts) ->
 //               k_emit (escape positions and symbols in weight order, and the
@@ -29,7 +30,7 @@ constexpr int kHistStride = 513;  // odd stride: copies of a bin sit in differen
 
 __global__ void k_zero_hist(uint32_t* hist) {
   const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-  if (i < 512) hist[i] = 0;
+  if (i < 512 * kHistGlobal) hist[i] = 0;
 }
 
 __global__ __launch_bounds__(kBlockThreads) void k_hist(const uint16_t* __restrict__ w, uint64_t n,
@@ -69,11 +70,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_hist(const uint16_t* __restri
   }
   for (uint64_t i = nvec * 8 + gid; i < n; i += stride) atomicAdd(mine + (w[i] >> 7), 1u);
   __syncthreads();
+  // blocks spread their merges over the global copies, so a frequent
+  // symbol's bin takes 1/kHistGlobal of the blocks' atomic adds
+  uint32_t* const g = hist + 512 * (blockIdx.x % kHistGlobal);
   for (int b = threadIdx.x; b < 512; b += kBlockThreads) {
     uint32_t s = 0;
 #pragma unroll
     for (int c = 0; c < kHistCopies; ++c) s += sub[c * kHistStride + b];
-    if (s) atomicAdd(hist + b, s);
+    if (s) atomicAdd(g + b, s);
   }
 }
 
@@ -96,7 +100,13 @@ __global__ __launch_bounds__(512) void k_top15(const uint32_t* __restrict__ hist
   const int wv = i / kWave;
   const int nsym = layout == WC_LAYOUT_K15 ? 512 : 256;
   uint32_t c = 0;
-  if (i < nsym) c = layout == WC_LAYOUT_K15 ? hist[i] : hist[2 * i] + hist[2 * i + 1];
+  if (i < nsym) {
+#pragma unroll
+    for (int k = 0; k < kHistGlobal; ++k) {
+      const uint32_t* hk = hist + 512 * k;
+      c += layout == WC_LAYOUT_K15 ? hk[i] : hk[2 * i] + hk[2 * i + 1];
+    }
+  }
   if (i < 16) dict[i] = 0;
   // compact the occurring symbols, keeping symbol order
   const uint32_t occ = c > 0 ? 1u : 0u;
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(512) void k_top15(const uint32_t* __restrict__ hist
 hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t* work,
                              hipStream_t s) {
   uint32_t* hist = (uint32_t*)(work + kWorkHist);
-  hipLaunchKernelGGL(k_zero_hist, dim3(2), dim3(256), 0, s, hist);
+  hipLaunchKernelGGL(k_zero_hist, dim3(2 * kHistGlobal), dim3(256), 0, s, hist);
   const uint64_t nvec = n / 8;
   uint64_t blocks = (nvec + kBlockThreads - 1) / kBlockThreads;
   if (blocks > 1024) blocks = 1024;

@@ -7,10 +7,12 @@
 namespace wc {
 
 // Byte offsets inside the caller's workspace (WC_WORKSPACE_BYTES(n) bytes).
-constexpr size_t kWorkHist = 0;         // u32[512] symbol counts
-constexpr size_t kWorkResult = 2048;    // DictResult (of the layout asked for; byte-split's under AUTO)
-constexpr size_t kWorkResult2 = 2096;   // DictResult of K15 under AUTO
-constexpr size_t kWorkBlocks = 4096;    // u32[nblk] escape counts, then u32[nblk] offsets
+constexpr int kHistGlobal = 8;          // copies of the global histogram (blocks spread over them)
+constexpr size_t kWorkHist = 0;         // u32[kHistGlobal][512] symbol counts
+constexpr size_t kWorkResult = 16384;   // DictResult (of the layout asked for; byte-split's under AUTO)
+constexpr size_t kWorkResult2 = 16432;  // DictResult of K15 under AUTO
+constexpr size_t kWorkBlocks = 20480;   // u32[nblk] escape counts, then u32[nblk] offsets
+static_assert(kWorkHist + 4u * 512u * kHistGlobal <= kWorkResult, "histogram copies fit");
 
 struct DictResult {
   uint32_t n_dict;

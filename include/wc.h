@@ -90,7 +90,7 @@ extern "C" {
 #define WC_MAX_BATCH 16u
 
 /* Scratch bytes wc_build_dict and wc_encode need for n weights. */
-#define WC_WORKSPACE_BYTES(n) ((size_t)4096 + (size_t)8 * (((uint64_t)(n) + 8191u) / 8192u))
+#define WC_WORKSPACE_BYTES(n) ((size_t)20480 + (size_t)8 * (((uint64_t)(n) + 8191u) / 8192u))
 
 /* The first 128 bytes of every container, byte for byte. */
 typedef struct wc_header {

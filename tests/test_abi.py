@@ -125,7 +125,7 @@ def test_argument_checks_before_device_work(wc):
 
 def test_workspace_formula(wc):
     for n in (0, 1, 8191, 8192, 8193, 10 ** 9):
-        assert wc.workspace_bytes(n) == 4096 + 8 * ((n + 8191) // 8192)
+        assert wc.workspace_bytes(n) == 20480 + 8 * ((n + 8191) // 8192)
 
 
 def test_header_struct_layout(wc):
