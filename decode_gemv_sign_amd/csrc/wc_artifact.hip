@@ -110,7 +110,7 @@ struct File {
 
 // File header checks: magic, version, CRC, the table and data placement,
 // and the recorded size against the file's own.
-int read_file_header(File& file, uint32_t* count, uint64_t* data_off) {
+int read_file_header(File& file, uint32_t* count, uint64_t* data_off, uint64_t* file_bytes) {
   uint8_t fh[kFileHeader];
   if (!file.f) return WC_E_IO;
   if (fseeko(file.f, 0, SEEK_END) != 0) return WC_E_IO;
@@ -131,13 +131,14 @@ int read_file_header(File& file, uint32_t* count, uint64_t* data_off) {
   if (n && (uint64_t)size < doff) return WC_E_CORRUPT;
   *count = (uint32_t)n;
   *data_off = doff;
+  *file_bytes = (uint64_t)size;
   return WC_OK;
 }
 
 int read_entry(File& file, uint32_t i, wc_artifact_info* out) {
   uint32_t count;
-  uint64_t doff;
-  int st = read_file_header(file, &count, &doff);
+  uint64_t doff, fsize;
+  int st = read_file_header(file, &count, &doff, &fsize);
   if (st != WC_OK) return st;
   if (i >= count) return WC_E_ARG;
   uint8_t e[kEntry];
@@ -161,12 +162,6 @@ int read_entry(File& file, uint32_t i, wc_artifact_info* out) {
     if (info.shape[k]) return WC_E_CORRUPT;
   if (info.offset % WC_ARTIFACT_ALIGN || info.offset < doff || info.bytes < WC_HEADER_BYTES)
     return WC_E_CORRUPT;
-  uint64_t fsize;
-  {
-    uint8_t fh[kFileHeader];
-    if (!file.read_at(0, fh, kFileHeader)) return WC_E_IO;
-    fsize = get(fh + 32, 8);
-  }
   if (info.offset > fsize || info.bytes > fsize - info.offset) return WC_E_CORRUPT;
   *out = info;
   return WC_OK;
@@ -207,7 +202,7 @@ extern "C" int wc_artifact_write(const char* path, uint32_t count, const char* c
     uint64_t prod = 1;
     for (uint32_t k = 0; k < 4; ++k) {
       const uint64_t d = shapes[4 * (size_t)i + k];
-      if (k >= ndims[i] ? d != 0 : false) return WC_E_ARG;
+      if (k >= ndims[i] && d != 0) return WC_E_ARG;  // unused dimensions are 0
       if (k < ndims[i]) prod *= d;
     }
     if (prod != h.n) return WC_E_ARG;
@@ -271,8 +266,8 @@ extern "C" int wc_artifact_count(const char* path, uint32_t* count) {
   if (!path || !count) return WC_E_ARG;
   File file(path, "rb");
   uint32_t n;
-  uint64_t doff;
-  int st = read_file_header(file, &n, &doff);
+  uint64_t doff, fsize;
+  int st = read_file_header(file, &n, &doff, &fsize);
   if (st != WC_OK) return st;
   wc_artifact_info info;
   for (uint32_t i = 0; i < n; ++i) {
