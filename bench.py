@@ -508,6 +508,9 @@ def main():
                         "launch_us": round(t_burst, 2),
                         "timing": f"HIP events around {burst_n} back-to-back launches"}
     roofline.pop("_t")
+    # the counter rate: the rocprofv3 HBM bytes of one launch over the same launch time
+    roofline["traffic_gbps"] = (round(roofline["traffic"] / roofline["launch_us"] / 1e3, 1)
+                                if roofline["traffic"] else None)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
