@@ -235,8 +235,12 @@ def test_gemv_every_batch(layout):
     """Batches 1..16 on shapes with a ragged 16-row block and a partial last
     128-column chunk, and on rows of whole 2048-weight tiles (the LDS-ring
     kernel); escapes in the tensor's last weights (the symbol window of the
-    last lanes meets the end of the stream) and one dense band."""
-    for rows, cols, dense in ((19, 160, False), (45, 1056, True), (13, 4096, True)):
+    last lanes meets the end of the stream) and one dense band.  Rows of 12
+    whole tiles (24576 columns) with a dense band (over 1 weight in 32
+    escapes) take the matrix-core kernel's contiguous per-wave ranges at
+    batches 8-16."""
+    for rows, cols, dense in ((19, 160, False), (45, 1056, True), (13, 4096, True),
+                              (21, 24576, True)):
         W = synth.random_bits(rows * cols, 1200 + rows, "normal").reshape(rows, cols)
         flat = W.reshape(-1)
         flat[::211] ^= 0x3000
