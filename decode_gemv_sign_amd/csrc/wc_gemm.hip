@@ -12,7 +12,9 @@
 //
 // Block = 16 consecutive rows x all columns, S waves.  The columns are cut
 // into 128-wide chunks; at step q wave s takes chunk q*S + s, so the block
-// walks the rows left to right in lock step.  Lane l = r + 16 h of a wave
+// walks the rows left to right in lock step (escape-heavy tensors with rows
+// of 12k whole tiles: wave s takes its own contiguous run of chunks
+// instead, see CONTIG below).  Lane l = r + 16 h of a wave
 // owns 32 consecutive weights of row r (columns 32h .. 32h+31 of the chunk,
 // 4 groups of 8): one 16-byte code load, one 32-byte (byte-split) or 28-byte
 // (K15) raw load and one 64-byte load of x row r (batch index r) per step,
@@ -26,12 +28,15 @@
 // section "Cómo funciona la compresión"): the records are in position order,
 // so the records of a lane's weights are one contiguous run of the stream.
 // Each step every wave counts the code-15 marks of its chunk per row and the
-// waves swap these counts through LDS; every lane then knows the first record
-// of its own weights (row cursor + counts of the chunks and lanes to its
-// left), loads the symbols of its run as one window and writes them into the
-// placeholders of its rebuilt weights.  The row cursors start from the
-// escape index: one load for a row that starts on a 2048-weight boundary,
-// else a search of the records of the row start's index tile.
+// waves swap these counts through LDS (not needed with contiguous runs);
+// every lane then knows the first record of its own weights (row cursor +
+// counts of the chunks and lanes to its left) and loads the symbols of its
+// run as one window.  Each group of 8 weights then takes its symbols by rank
+// from its part of that window (v_perm selectors, as in the 1D kernels), or,
+// for K15 with sparse escapes, one record at a time through an LDS stage.
+// The row cursors start from the escape index: one load for a row that
+// starts on a 2048-weight boundary, else a search of the records of the row
+// start's index tile.
 #include "wc_launch.h"
 #include "wc_tile.h"
 
