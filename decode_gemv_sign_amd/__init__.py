@@ -32,7 +32,7 @@ BYTESPLIT = 0
 K15 = 1
 RAW = 2   # fallback layout: the BF16 bit patterns as stored
 AUTO = 3  # build_dict / encode only: the smallest of the three
-MAX_BATCH = 16
+MAX_BATCH = 256
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwc.so")
 
 _CODES = {0: "WC_OK", -1: "WC_E_ARG", -2: "WC_E_SIZE", -3: "WC_E_CORRUPT", -4: "WC_E_HIP",

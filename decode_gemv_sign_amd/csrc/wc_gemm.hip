@@ -63,6 +63,7 @@ struct GemmArgs {
   float* y;
   uint64_t rows, cols, n_esc, sym_last;  // sym_last: last dword of the padded symbol stream
   uint32_t batch, chunks;                // chunks: 128-column chunks per row
+  uint32_t groups, row_blocks;           // wide batches: batch groups, row blocks
   Dict dict;
 };
 
@@ -467,6 +468,288 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   }
 }
 
+// ---- wide batches (17 .. 256) ---------------------------------------------
+//
+// The prefill-like regime: more input rows than one MFMA's 16 columns.  The
+// rebuilt weights are the product's A operand as above, but now every A
+// operand is used by NB batch tiles of 16, so a weight is decoded once per
+// group of 16 NB batch rows instead of once per 16.
+//
+// Block = NW waves x 16 rows each, for one group of NB batch tiles.  Each
+// wave walks all columns of its own 16 rows, 128 at a time, so its row
+// cursors advance by its own escape counts alone.  The block's x chunk (16 NB
+// batch rows x 128 columns, 4 KiB per tile) is staged in LDS by global->LDS
+// DMA and read by all NW waves: piece p (columns 8p .. 8p+7) of tile row q
+// sits at slot p ^ q of that row, so the 16 rows of an operand read fall in
+// 16 different bank groups.
+//
+// Pipeline: at step j the wave has chunk j's raw part, x chunk and symbol
+// window and chunk j+1's codes in hand.  It counts chunk j+1's escapes at
+// once (so its records' cursors are known a step early), issues chunk j+1's
+// window, x, raw loads and chunk j+2's codes, then rebuilds and multiplies
+// chunk j.  Every load is thus issued a full step before it is used and the
+// step never waits on memory in the middle.
+template <int LAYOUT, bool PLAIN, int NW, int NB>
+__global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
+  constexpr bool kK15 = LAYOUT == WC_LAYOUT_K15;
+  constexpr int kRawDw = PLAIN ? 16 : (kK15 ? 7 : 8);  // raw part (or plain weights) per lane
+  constexpr int kWinDwords = kK15 ? 17 : 9;
+  constexpr int kSymBytes = kK15 ? 2 : 1;
+  constexpr int kGroupWin = WinDwords<LAYOUT>::value;
+  constexpr int kWinStride = kWinDwords + kGroupWin - 1;
+  constexpr int kXTile = kMRows * kStepCols * 2;  // bytes of one batch tile's x chunk
+  static_assert((4 * NB) % NW == 0, "x DMA split");
+  __shared__ uint32_t T2[PLAIN ? 1 : 256];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][NB * kXTile];
+  __shared__ uint32_t win[PLAIN ? 1 : NW][PLAIN ? 1 : kWave * kWinStride];
+
+  // Block -> (row block, batch group).  Workgroups go to the 8 XCDs in turn,
+  // so the groups of one row block are given consecutive slots of one XCD:
+  // their weight reads then meet in that XCD's L2.
+  const uint32_t L = blockIdx.x, xcd = L & 7u, li = L >> 3;
+  const uint32_t rb = (li / a.groups) * 8u + xcd, bg = li % a.groups;
+  if (rb >= a.row_blocks) return;  // padding of the grid to whole XCD rounds
+  if constexpr (!PLAIN) build_pair_table<LAYOUT>(T2, a.dict);
+
+  const int lane = lane_id(), r = lane & 15, h = lane >> 4;
+  const int s = wave_in_block();
+  const uint64_t r0 = ((uint64_t)rb * NW + (uint64_t)s) * kMRows;  // the wave's first row
+  const bool row_ok = r0 + r < a.rows;
+  // rows past the matrix re-read its last row; their codes count no escapes
+  // and their outputs are dropped
+  const uint64_t lane_base = (row_ok ? r0 + r : a.rows - 1) * a.cols + (uint64_t)(kLaneCols * h);
+  const uint32_t cmask = row_ok ? ~0u : 0u;
+  const uint32_t b0 = bg * (uint32_t)(kMRows * NB);
+  const uint32_t n_steps = a.chunks;
+  const bool esc = !PLAIN && a.n_esc != 0;
+
+  auto load_codes = [&](uint32_t j, uint32_t c[kLaneGroups]) {
+    const uint64_t e = lane_base + (uint64_t)j * kStepCols;
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.codes + e / 2));
+    c[0] = v[0]; c[1] = v[1]; c[2] = v[2]; c[3] = v[3];
+  };
+  auto load_raw = [&](uint32_t j, uint32_t w[kRawDw]) {
+    const uint64_t e = lane_base + (uint64_t)j * kStepCols;
+    if constexpr (PLAIN) {
+      const u32x4* wp = (const u32x4*)(a.w + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 v = __builtin_nontemporal_load(wp + u);
+        w[4 * u] = v[0]; w[4 * u + 1] = v[1]; w[4 * u + 2] = v[2]; w[4 * u + 3] = v[3];
+      }
+    } else if constexpr (kK15) {
+      const uint32_t* rp = (const uint32_t*)(a.raw + 7 * (e / 8));  // 28 bytes, 4-aligned
+      const u32x4 v0 = __builtin_nontemporal_load((const u32x4a4*)rp);
+      const u32x3 v1 = __builtin_nontemporal_load((const u32x3a4*)(rp + 4));
+      w[0] = v0[0]; w[1] = v0[1]; w[2] = v0[2]; w[3] = v0[3];
+      w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2];
+    } else {
+      const u32x4* rp = (const u32x4*)(a.raw + e);
+      const u32x4 v0 = __builtin_nontemporal_load(rp), v1 = __builtin_nontemporal_load(rp + 1);
+      w[0] = v0[0]; w[1] = v0[1]; w[2] = v0[2]; w[3] = v0[3];
+      w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2]; w[7] = v1[3];
+    }
+  };
+  // The block's x chunk j into xs[j & 1]: 4 NB DMA loads of 1 KiB, NW-way
+  // split.  Load i fills tile i / 4, rows 4 (i % 4) .. +3; lane (r, h)
+  // writes slot r of row q = 4 (i % 4) + h with piece r ^ q.  Batch rows past
+  // the batch re-read its last row (their outputs are dropped).
+  auto load_x = [&](uint32_t j) {
+    uint8_t* dst = xs[j & 1];
+#pragma unroll
+    for (int k = 0; k < 4 * NB / NW; ++k) {
+      const int i = s + k * NW;
+      const int q = 4 * (i & 3) + h;
+      uint32_t bb = b0 + (uint32_t)(kMRows * (i >> 2) + q);
+      bb = bb < a.batch ? bb : a.batch - 1;
+      const uint16_t* src =
+          a.x + (uint64_t)bb * a.cols + (uint64_t)j * kStepCols + 8u * (uint32_t)(r ^ q);
+      lds_dma16(src, (uint32_t*)(dst + 1024 * i));
+    }
+  };
+
+  // Escape bookkeeping of one chunk, from its codes: the lane's marks
+  // (compressed), and its symbol window, loaded into wd when the wave has any
+  // escapes (off = byte of the lane's first symbol in wd).  e_next is row
+  // r's cursor at the chunk's first column and moves past the chunk.
+  uint64_t e_next = 0;
+  auto count_chunk = [&](const uint32_t c[kLaneGroups], uint32_t& M, uint32_t& off, bool& any,
+                         uint32_t wd[kWinDwords]) {
+    Lane4 l;
+#pragma unroll
+    for (int m = 0; m < kLaneGroups; ++m) l.codes[m] = c[m] & cmask;
+    uint32_t marks[kLaneGroups];
+    escape_marks(l, marks);
+    const uint32_t cnt = count_marks(marks);
+    M = compress_marks(marks);
+    const uint32_t c0 = __shfl(cnt, r, kWave), c1 = __shfl(cnt, r + 16, kWave);
+    const uint32_t c2 = __shfl(cnt, r + 32, kWave), c3 = __shfl(cnt, r + 48, kWave);
+    const uint32_t ex = (h > 0 ? c0 : 0u) + (h > 1 ? c1 : 0u) + (h > 2 ? c2 : 0u);
+    const uint64_t e_l = e_next + ex;
+    e_next += c0 + c1 + c2 + c3;
+    any = __ballot(cnt != 0) != 0;
+    off = 0;
+    if (any) {
+      // the dwords holding records e_l .. e_l+31, the window's end clamped to
+      // the stream's padded end (its start may then fall in the container's
+      // earlier streams, which is harmless)
+      const int64_t byte = (int64_t)(e_l * kSymBytes);
+      int64_t b = byte >> 2;
+      const int64_t bmax = (int64_t)a.sym_last - (kWinDwords - 1);
+      b = b < bmax ? b : bmax;
+      off = (uint32_t)(byte - 4 * b);
+      if (cnt != 0) {
+        const uint32_t* sp = (const uint32_t*)a.esc_sym + b;
+#pragma unroll
+        for (int u = 0; u + 4 <= kWinDwords; u += 4) {
+          const u32x4 v = *(const u32x4a4*)(sp + u);
+          wd[u] = v[0]; wd[u + 1] = v[1]; wd[u + 2] = v[2]; wd[u + 3] = v[3];
+        }
+        wd[kWinDwords - 1] = sp[kWinDwords - 1];
+      }
+    }
+  };
+
+  // Row cursors at column 0: lane rr of the first 16 reads row rr's index
+  // entry when rows start on index tiles, else each row is searched for.
+  if (esc) {
+    if (a.cols % WC_INDEX_TILE == 0) {
+      uint32_t v = 0;
+      if (lane < kMRows) {
+        const uint64_t row = r0 + (uint64_t)lane;
+        const uint64_t t = (row < a.rows ? row : a.rows) * (a.cols / WC_INDEX_TILE);
+        const uint32_t x = a.esc_idx[t];
+        v = x < a.n_esc ? x : (uint32_t)a.n_esc;
+      }
+      e_next = (uint32_t)__shfl((int)v, r, kWave);
+    } else {
+      for (int rr = 0; rr < kMRows; ++rr) {
+        const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
+        const uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, t);
+        if (r == rr) e_next = e;
+      }
+    }
+  }
+
+  uint32_t c_cur[kLaneGroups] = {}, c_nxt[kLaneGroups] = {}, c_new[kLaneGroups] = {};
+  uint32_t w_cur[kRawDw], w_nxt[kRawDw] = {};
+  uint32_t wd_cur[kWinDwords] = {}, wd_nxt[kWinDwords] = {};
+  uint32_t M_cur = 0, off_cur = 0, M_nxt = 0, off_nxt = 0;
+  bool win_cur = false, win_nxt = false;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  load_x(0);
+  load_raw(0, w_cur);
+  if constexpr (!PLAIN) {
+    load_codes(0, c_cur);
+    if (n_steps > 1) load_codes(1, c_nxt);
+    if (esc) {
+      wait_vm<0>();
+      count_chunk(c_cur, M_cur, off_cur, win_cur, wd_cur);
+    }
+  }
+
+  for (uint32_t j = 0; j < n_steps; ++j) {
+    wait_vm<0>();
+    if (j > 0) {
+      // everything issued last step has arrived: move the ring along (a
+      // copy made after the wait, so it never stalls on a load)
+#pragma unroll
+      for (int m = 0; m < kLaneGroups; ++m) { c_cur[m] = c_nxt[m]; c_nxt[m] = c_new[m]; }
+#pragma unroll
+      for (int u = 0; u < kRawDw; ++u) w_cur[u] = w_nxt[u];
+#pragma unroll
+      for (int u = 0; u < kWinDwords; ++u) wd_cur[u] = wd_nxt[u];
+      M_cur = M_nxt; off_cur = off_nxt; win_cur = win_nxt;
+    }
+    block_lds_barrier();  // x chunk j of every wave in LDS; chunk j-1's reads done
+    if (j + 1 < n_steps) {
+      if (esc) count_chunk(c_nxt, M_nxt, off_nxt, win_nxt, wd_nxt);
+      load_x(j + 1);
+      load_raw(j + 1, w_nxt);
+      if (!PLAIN && j + 2 < n_steps) load_codes(j + 2, c_new);
+    }
+
+    uint32_t wv[16];
+    if constexpr (PLAIN) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) wv[u] = w_cur[u];
+    } else {
+      Lane4 lr;
+#pragma unroll
+      for (int m = 0; m < kLaneGroups; ++m) {
+        lr.codes[m] = c_cur[m] & cmask;
+        if constexpr (kK15) {
+          const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
+          lr.raw[m][0] = __builtin_amdgcn_alignbit(w_cur[d + 1], w_cur[d], sh);
+          lr.raw[m][1] = __builtin_amdgcn_alignbit(d + 2 < 7 ? w_cur[d + 2] : 0u, w_cur[d + 1], sh);
+        } else {
+          lr.raw[m][0] = w_cur[2 * m];
+          lr.raw[m][1] = w_cur[2 * m + 1];
+        }
+      }
+      rebuild_lane<LAYOUT>(T2, lr, wv);
+      if (win_cur) {
+        // each group takes its symbols by rank from its part of the lane's
+        // window (written to LDS, where a group's dwords can be addressed)
+        uint32_t* wl = win[s] + lane * kWinStride;
+        if (M_cur != 0) {
+#pragma unroll
+          for (int u = 0; u < kWinDwords; ++u) wl[u] = wd_cur[u];
+        }
+        wave_lds_sync();
+        uint32_t fm = 0;
+#pragma unroll
+        for (int m = 0; m < kLaneGroups; ++m) {
+          const uint32_t gm = (M_cur >> (8 * m)) & 0xFFu;
+          if (__ballot(gm != 0)) {
+            const uint32_t o = off_cur + fm * kSymBytes;
+            const uint32_t* gp = wl + (o >> 2);
+            uint32_t w[kGroupWin];
+#pragma unroll
+            for (int u = 0; u < kGroupWin; ++u) w[u] = gp[u];
+            if (gm) expand_window<LAYOUT>(gm, w, o & 3u, wv + 4 * m);
+          }
+          fm += (uint32_t)__popc(gm);
+        }
+        wave_lds_sync();  // the window area is rewritten at the next step
+      }
+    }
+
+    // NB products per group of 8 weights: operand B of tile t is x rows
+    // 16 t + r, columns 32 h + 8 m .. +7 of the chunk (piece 4 h + m).
+    const uint8_t* xb = xs[j & 1];
+#pragma unroll
+    for (int m = 0; m < kLaneGroups; ++m) {
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const u32x4 v = *(const u32x4*)(xb + kXTile * t + 256 * r + 16 * ((4 * h + m) ^ r));
+        const uint32_t bx[4] = {v[0], v[1], v[2], v[3]};
+        acc[t] = mfma_bf16(wv + 4 * m, bx, acc[t]);
+      }
+    }
+  }
+  // matrix-core results are read by vector instructions only after this
+  // many idle cycles
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]));
+#pragma unroll
+  for (int t = 1; t < NB; ++t) asm volatile("" : "+v"(acc[t]));
+  // lane (r, h) holds rows 4h .. 4h+3 of the wave's 16 for batch row 16 t + r
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const uint32_t bb = b0 + (uint32_t)(kMRows * t + r);
+    if (bb < a.batch) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint64_t row = r0 + 4 * h + v;
+        if (row < a.rows) a.y[(uint64_t)bb * a.rows + row] = acc[t][v];
+      }
+    }
+  }
+}
+
 // ---- launchers -----------------------------------------------------------
 
 #ifndef WC_GEMM_SLICES
@@ -509,6 +792,41 @@ static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint3
   return a;
 }
 
+#ifndef WC_WIDE_NB
+#define WC_WIDE_NB 4
+#endif
+
+// Wide batches: WC_WIDE_NB batch tiles per block, 4 waves (64 rows) per
+// block, or 2 when that leaves fewer than two blocks per compute unit.
+template <int LAYOUT, bool PLAIN>
+static void launch_wide(GemmArgs a, hipStream_t s) {
+  constexpr int kCUs = 256;
+  constexpr int nb = WC_WIDE_NB;
+  a.groups = (a.batch + kMRows * nb - 1) / (kMRows * nb);
+  const uint64_t rb4 = (a.rows + 4 * kMRows - 1) / (4 * kMRows);
+  const int nw = rb4 * a.groups >= 2 * kCUs ? 4 : 2;
+  const uint64_t rbs = (a.rows + (uint64_t)nw * kMRows - 1) / ((uint64_t)nw * kMRows);
+  a.row_blocks = (uint32_t)rbs;
+  const dim3 g((unsigned)(((rbs + 7) / 8) * 8 * a.groups));
+  const dim3 t(kWave * nw);
+#define WC_WIDE_LAUNCH(NW, NB) \
+  hipLaunchKernelGGL((k_gemm_wide<LAYOUT, PLAIN, NW, NB>), g, t, 0, s, a)
+  if (nw == 4)
+    WC_WIDE_LAUNCH(4, nb);
+  else
+    WC_WIDE_LAUNCH(2, nb);
+#undef WC_WIDE_LAUNCH
+}
+
+// Batches up to 32 run faster as two launches of the 16-row kernel: the wide
+// kernel's time is set by one memory round trip per 128-column step of a
+// block, whatever its batch (measured on 4096 x 4096 and 6144 x 24576).
+bool gemm_wide_fits(uint64_t rows, uint64_t cols, uint32_t batch) {
+  return rows > 0 && cols > 0 && cols % kStepCols == 0 && batch > 2 * kMRows &&
+         batch <= WC_MAX_BATCH && cols / kStepCols < (1ull << 31) &&
+         rows / (2 * kMRows) < (1ull << 31) / 8;
+}
+
 bool gemm_mfma_fits(uint64_t rows, uint64_t cols, uint32_t batch) {
   return rows > 0 && cols > 0 && cols % kLaneCols == 0 && batch >= 1 && batch <= kMRows &&
          cols / kStepCols < (1ull << 31);
@@ -527,10 +845,16 @@ hipError_t launch_decode_gemm_mfma(const wc_header& h, const uint8_t* container,
   // last dword of the symbol stream's 16-byte padded extent (unused without escapes)
   a.sym_last = h.n_esc ? (h.off_esc_idx - h.off_esc_sym) / 4 - 1 : 0;
   a.dict = dict_of(&h);
-  if (h.layout == WC_LAYOUT_K15)
+  if (batch > kMRows) {
+    if (h.layout == WC_LAYOUT_K15)
+      launch_wide<WC_LAYOUT_K15, false>(a, s);
+    else
+      launch_wide<WC_LAYOUT_BYTESPLIT, false>(a, s);
+  } else if (h.layout == WC_LAYOUT_K15) {
     launch_mfma<WC_LAYOUT_K15, false>(a, s);
-  else
+  } else {
     launch_mfma<WC_LAYOUT_BYTESPLIT, false>(a, s);
+  }
   return hipGetLastError();
 }
 
@@ -538,7 +862,10 @@ hipError_t launch_gemm_bf16_mfma(const uint16_t* w, uint64_t rows, uint64_t cols
                                  const uint16_t* x, uint32_t batch, float* y, hipStream_t s) {
   GemmArgs a = gemm_args(rows, cols, x, batch, y);
   a.w = w;
-  launch_mfma<WC_LAYOUT_BYTESPLIT, true>(a, s);
+  if (batch > kMRows)
+    launch_wide<WC_LAYOUT_BYTESPLIT, true>(a, s);
+  else
+    launch_mfma<WC_LAYOUT_BYTESPLIT, true>(a, s);
   return hipGetLastError();
 }
 

@@ -644,6 +644,18 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
   // raw layout: the stored weights are plain BF16
   if (h.layout == WC_LAYOUT_RAW)
     return launch_gemv_bf16((const uint16_t*)(container + h.off_raw), rows, cols, x, batch, y, s);
+  if (batch > 16) {
+    if (gemm_wide_fits(rows, cols, batch))
+      return launch_decode_gemm_mfma(h, container, rows, cols, x, batch, y, s);
+    // other shapes: batches of at most 16 rows in turn
+    for (uint32_t done = 0; done < batch; done += 16) {
+      const uint32_t b = batch - done < 16 ? batch - done : 16;
+      const hipError_t e = launch_decode_gemv(h, container, rows, cols, x + (uint64_t)done * cols,
+                                              b, y + (uint64_t)done * rows, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
     return launch_decode_gemm_mfma(h, container, rows, cols, x, batch, y, s);
   GemvArgs a{};
@@ -692,6 +704,16 @@ hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, con
     hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, y,
                        count);
     return hipGetLastError();
+  }
+  if (batch > 16) {
+    if (gemm_wide_fits(rows, cols, batch)) return launch_gemm_bf16_mfma(w, rows, cols, x, batch, y, s);
+    for (uint32_t done = 0; done < batch; done += 16) {
+      const uint32_t b = batch - done < 16 ? batch - done : 16;
+      const hipError_t e = launch_gemv_bf16(w, rows, cols, x + (uint64_t)done * cols, b,
+                                            y + (uint64_t)done * rows, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
     return launch_gemm_bf16_mfma(w, rows, cols, x, batch, y, s);

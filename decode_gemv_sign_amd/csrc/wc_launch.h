@@ -53,6 +53,8 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
                               hipStream_t s);
 // Matrix-core paths (wc_gemm.hip): cols a multiple of 32, batch 1..16.
 bool gemm_mfma_fits(uint64_t rows, uint64_t cols, uint32_t batch);
+// Wide batches (33..WC_MAX_BATCH) on the matrix cores: cols a multiple of 128.
+bool gemm_wide_fits(uint64_t rows, uint64_t cols, uint32_t batch);
 hipError_t launch_decode_gemm_mfma(const wc_header& h, const uint8_t* container, uint64_t rows,
                                    uint64_t cols, const uint16_t* x, uint32_t batch, float* y,
                                    hipStream_t s);

@@ -87,7 +87,7 @@ extern "C" {
 #define WC_VERSION 2u
 #define WC_HEADER_BYTES 128u
 #define WC_INDEX_TILE 2048u /* weights per escape-index entry */
-#define WC_MAX_BATCH 16u
+#define WC_MAX_BATCH 256u
 
 /* Scratch bytes wc_build_dict and wc_encode need for n weights. */
 #define WC_WORKSPACE_BYTES(n) ((size_t)20480 + (size_t)8 * (((uint64_t)(n) + 8191u) / 8192u))
@@ -161,7 +161,12 @@ int wc_decode(const wc_header *h, const uint8_t *d_container,
  * with escapes applied and never written to memory.  d_x: BF16 [batch][cols];
  * d_y: fp32 [batch][rows].  Products are exact (BF16 x BF16), sums are fp32
  * in an order that differs from a sequential loop.  batch in
- * 1..WC_MAX_BATCH, else WC_E_UNSUPPORTED.
+ * 1..WC_MAX_BATCH, else WC_E_UNSUPPORTED.  Above 32 input rows (the
+ * prefill regime, where the pages' closest prior art is a fused
+ * decompression-GEMM [P2 "¿Cómo encaja con los sistemas anteriores?"])
+ * each rebuilt weight is used by up to 64 input rows on the matrix cores
+ * when cols is a multiple of 128; other batches above 16 run 16 input rows
+ * at a time.
  */
 int wc_decode_gemv(const wc_header *h, const uint8_t *d_container,
                    size_t container_bytes, uint64_t rows, uint64_t cols,

@@ -114,9 +114,9 @@ def test_argument_checks_before_device_work(wc):
     # a zeroed header is corrupt for decode and GEMV
     assert lib.wc_decode(ctypes.byref(h), ctypes.c_void_p(16), ctypes.c_size_t(1 << 20),
                          ctypes.c_void_p(16), None) == -3
-    # batch outside 1..16
+    # batch outside 1..256
     assert lib.wc_gemv_bf16(ctypes.c_void_p(16), ctypes.c_uint64(4), ctypes.c_uint64(32),
-                            ctypes.c_void_p(16), ctypes.c_uint32(17), ctypes.c_void_p(16),
+                            ctypes.c_void_p(16), ctypes.c_uint32(257), ctypes.c_void_p(16),
                             None) == -5
     assert lib.wc_gemv_bf16(ctypes.c_void_p(16), ctypes.c_uint64(4), ctypes.c_uint64(32),
                             ctypes.c_void_p(16), ctypes.c_uint32(0), ctypes.c_void_p(16),

@@ -405,7 +405,7 @@ def test_gemv_cols_zero_and_rows_zero():
 def test_error_codes():
     W = synth.random_bits(64 * 64, 1, "normal").reshape(64, 64)
     h, c = gpu_encode(0, W)
-    x = dev16(synth.vectors(1, 17, 64))
+    x = dev16(synth.vectors(1, 257, 64))
     with pytest.raises(wc.WCError) as e:
         wc.decode_gemv(h, c, 64, 64, x)
     assert e.value.code == -5
