@@ -77,7 +77,8 @@ def load_workload(name: str, batch: int):
         return [m["W1"], m["W2"]], None
     if name == "banded":
         d = synth.banded()
-        return [d["W"]], d["X"][:batch]
+        # the same draw as the workload's own x, extended to `batch` rows
+        return [d["W"]], synth.vectors(synth.SEEDS["banded"], batch, d["W"].shape[1])
     raise ValueError(name)
 
 
@@ -310,6 +311,11 @@ def main():
               for i, W in enumerate(mats)]
     else:
         xs = [x]
+    # the library is called with args.batch: every x must hold exactly that
+    # many rows of its matrix's columns
+    for W, xx in zip(mats, xs):
+        if xx.shape != (args.batch, W.shape[1]):
+            raise SystemExit(f"x has shape {xx.shape}, expected ({args.batch}, {W.shape[1]})")
     layouts = [wc.BYTESPLIT, wc.K15]
     in_bytes = sum(W.nbytes for W in mats)
     copies = max(1, -(-WORKSET_BYTES // in_bytes))

@@ -63,7 +63,8 @@ struct GemmArgs {
   float* y;
   uint64_t rows, cols, n_esc, sym_last;  // sym_last: last dword of the padded symbol stream
   uint32_t batch, chunks;                // chunks: 128-column chunks per row
-  uint32_t groups, row_blocks;           // wide batches: batch groups, row blocks
+  uint32_t groups, row_blocks;           // wide batches: batch groups x column splits, row blocks
+  uint32_t splits, split_chunks;         // wide batches: column splits, chunks per split
   Dict dict;
 };
 
@@ -489,7 +490,25 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
 // window, x, raw loads and chunk j+2's codes, then rebuilds and multiplies
 // chunk j.  Every load is thus issued a full step before it is used and the
 // step never waits on memory in the middle.
-template <int LAYOUT, bool PLAIN, int NW, int NB>
+// Operand B of NB batch tiles (16-byte LDS reads 4096 bytes apart from
+// addr) behind one wait.  Hand-written: the compiler cannot tell these reads
+// from the x chunk that global->LDS loads are still filling for the next
+// step, and before a plain read it would wait for all of those loads.
+template <int NB>
+__device__ inline void lds_read_tiles(uint32_t addr, u32x4 (&v)[NB]) {
+  static_assert(NB == 2 || NB == 4, "batch tiles per block");
+  if constexpr (NB == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(addr) : "memory");
+  } else {
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:4096\n\t"
+                 "ds_read_b128 %2, %4 offset:8192\n\tds_read_b128 %3, %4 offset:12288\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(addr) : "memory");
+  }
+}
+
+template <int LAYOUT, bool PLAIN, int NW, int NB, int U>
 __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
   constexpr bool kK15 = LAYOUT == WC_LAYOUT_K15;
   constexpr int kRawDw = PLAIN ? 16 : (kK15 ? 7 : 8);  // raw part (or plain weights) per lane
@@ -498,17 +517,24 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
   constexpr int kGroupWin = WinDwords<LAYOUT>::value;
   constexpr int kWinStride = kWinDwords + kGroupWin - 1;
   constexpr int kXTile = kMRows * kStepCols * 2;  // bytes of one batch tile's x chunk
+  constexpr int kXChunk = NB * kXTile;            // the block's x for one chunk
   static_assert((4 * NB) % NW == 0, "x DMA split");
   __shared__ uint32_t T2[PLAIN ? 1 : 256];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][NB * kXTile];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][U * kXChunk];
   __shared__ uint32_t win[PLAIN ? 1 : NW][PLAIN ? 1 : kWave * kWinStride];
 
   // Block -> (row block, batch group).  Workgroups go to the 8 XCDs in turn,
   // so the groups of one row block are given consecutive slots of one XCD:
   // their weight reads then meet in that XCD's L2.
   const uint32_t L = blockIdx.x, xcd = L & 7u, li = L >> 3;
-  const uint32_t rb = (li / a.groups) * 8u + xcd, bg = li % a.groups;
+  const uint32_t rb = (li / a.groups) * 8u + xcd, bgs = li % a.groups;
   if (rb >= a.row_blocks) return;  // padding of the grid to whole XCD rounds
+  // column split sk takes chunks [c0, c0 + n_chunks) of the block's rows
+  const uint32_t sk = bgs % a.splits, bg = bgs / a.splits;
+  const uint32_t c0 = sk * a.split_chunks;
+  if (c0 >= a.chunks) return;
+  const uint32_t n_chunks = a.chunks - c0 < a.split_chunks ? a.chunks - c0 : a.split_chunks;
+  const uint64_t col0 = (uint64_t)c0 * kStepCols;
   if constexpr (!PLAIN) build_pair_table<LAYOUT>(T2, a.dict);
 
   const int lane = lane_id(), r = lane & 15, h = lane >> 4;
@@ -517,10 +543,11 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
   const bool row_ok = r0 + r < a.rows;
   // rows past the matrix re-read its last row; their codes count no escapes
   // and their outputs are dropped
-  const uint64_t lane_base = (row_ok ? r0 + r : a.rows - 1) * a.cols + (uint64_t)(kLaneCols * h);
+  const uint64_t lane_base =
+      (row_ok ? r0 + r : a.rows - 1) * a.cols + col0 + (uint64_t)(kLaneCols * h);
   const uint32_t cmask = row_ok ? ~0u : 0u;
   const uint32_t b0 = bg * (uint32_t)(kMRows * NB);
-  const uint32_t n_steps = a.chunks;
+  const uint32_t n_steps = (n_chunks + U - 1) / U;
   const bool esc = !PLAIN && a.n_esc != 0;
 
   auto load_codes = [&](uint32_t j, uint32_t c[kLaneGroups]) {
@@ -550,12 +577,11 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
       w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2]; w[7] = v1[3];
     }
   };
-  // The block's x chunk j into xs[j & 1]: 4 NB DMA loads of 1 KiB, NW-way
-  // split.  Load i fills tile i / 4, rows 4 (i % 4) .. +3; lane (r, h)
-  // writes slot r of row q = 4 (i % 4) + h with piece r ^ q.  Batch rows past
-  // the batch re-read its last row (their outputs are dropped).
-  auto load_x = [&](uint32_t j) {
-    uint8_t* dst = xs[j & 1];
+  // The block's x chunk j into dst: 4 NB DMA loads of 1 KiB, NW-way split.
+  // Load i fills tile i / 4, rows 4 (i % 4) .. +3; lane (r, h) writes slot r
+  // of row q = 4 (i % 4) + h with piece r ^ q.  Batch rows past the batch
+  // re-read its last row (their outputs are dropped).
+  auto load_x = [&](uint32_t j, uint8_t* dst) {
 #pragma unroll
     for (int k = 0; k < 4 * NB / NW; ++k) {
       const int i = s + k * NW;
@@ -563,7 +589,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
       uint32_t bb = b0 + (uint32_t)(kMRows * (i >> 2) + q);
       bb = bb < a.batch ? bb : a.batch - 1;
       const uint16_t* src =
-          a.x + (uint64_t)bb * a.cols + (uint64_t)j * kStepCols + 8u * (uint32_t)(r ^ q);
+          a.x + (uint64_t)bb * a.cols + col0 + (uint64_t)j * kStepCols + 8u * (uint32_t)(r ^ q);
       lds_dma16(src, (uint32_t*)(dst + 1024 * i));
     }
   };
@@ -610,44 +636,58 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
     }
   };
 
-  // Row cursors at column 0: lane rr of the first 16 reads row rr's index
-  // entry when rows start on index tiles, else each row is searched for.
+  // Row cursors at column col0: lane rr of the first 16 reads row rr's index
+  // entry when those columns start index tiles, else each row is searched
+  // for.
   if (esc) {
-    if (a.cols % WC_INDEX_TILE == 0) {
+    if (a.cols % WC_INDEX_TILE == 0 && col0 % WC_INDEX_TILE == 0) {
       uint32_t v = 0;
       if (lane < kMRows) {
         const uint64_t row = r0 + (uint64_t)lane;
-        const uint64_t t = (row < a.rows ? row : a.rows) * (a.cols / WC_INDEX_TILE);
+        const uint64_t t = row < a.rows ? (row * a.cols + col0) / WC_INDEX_TILE
+                                        : a.rows * (a.cols / WC_INDEX_TILE);
         const uint32_t x = a.esc_idx[t];
         v = x < a.n_esc ? x : (uint32_t)a.n_esc;
       }
       e_next = (uint32_t)__shfl((int)v, r, kWave);
     } else {
       for (int rr = 0; rr < kMRows; ++rr) {
-        const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
+        const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols + col0 : a.rows * a.cols;
         const uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, t);
         if (r == rr) e_next = e;
       }
     }
   }
 
-  uint32_t c_cur[kLaneGroups] = {}, c_nxt[kLaneGroups] = {}, c_new[kLaneGroups] = {};
-  uint32_t w_cur[kRawDw], w_nxt[kRawDw] = {};
-  uint32_t wd_cur[kWinDwords] = {}, wd_nxt[kWinDwords] = {};
-  uint32_t M_cur = 0, off_cur = 0, M_nxt = 0, off_nxt = 0;
-  bool win_cur = false, win_nxt = false;
+  // A step takes U consecutive chunks (the last step may hold fewer): their
+  // loads go out together, so a block's chain of memory round trips is one
+  // per U chunks.
+  uint32_t c_cur[U][kLaneGroups] = {}, c_nxt[U][kLaneGroups] = {}, c_new[U][kLaneGroups] = {};
+  uint32_t w_cur[U][kRawDw] = {}, w_nxt[U][kRawDw] = {};
+  uint32_t wd_cur[U][kWinDwords] = {}, wd_nxt[U][kWinDwords] = {};
+  uint32_t M_cur[U] = {}, off_cur[U] = {}, M_nxt[U] = {}, off_nxt[U] = {};
+  bool win_cur[U] = {}, win_nxt[U] = {};
   f32x4 acc[NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  load_x(0);
-  load_raw(0, w_cur);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if ((uint32_t)u < n_chunks) {
+      load_x(u, xs[0] + u * kXChunk);
+      load_raw(u, w_cur[u]);
+      if constexpr (!PLAIN) load_codes(u, c_cur[u]);
+    }
+  }
   if constexpr (!PLAIN) {
-    load_codes(0, c_cur);
-    if (n_steps > 1) load_codes(1, c_nxt);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if ((uint32_t)(U + u) < n_chunks) load_codes(U + u, c_nxt[u]);
     if (esc) {
       wait_vm<0>();
-      count_chunk(c_cur, M_cur, off_cur, win_cur, wd_cur);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if ((uint32_t)u < n_chunks) count_chunk(c_cur[u], M_cur[u], off_cur[u], win_cur[u], wd_cur[u]);
     }
   }
 
@@ -657,77 +697,91 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
       // everything issued last step has arrived: move the ring along (a
       // copy made after the wait, so it never stalls on a load)
 #pragma unroll
-      for (int m = 0; m < kLaneGroups; ++m) { c_cur[m] = c_nxt[m]; c_nxt[m] = c_new[m]; }
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int u = 0; u < kRawDw; ++u) w_cur[u] = w_nxt[u];
+        for (int m = 0; m < kLaneGroups; ++m) { c_cur[u][m] = c_nxt[u][m]; c_nxt[u][m] = c_new[u][m]; }
 #pragma unroll
-      for (int u = 0; u < kWinDwords; ++u) wd_cur[u] = wd_nxt[u];
-      M_cur = M_nxt; off_cur = off_nxt; win_cur = win_nxt;
+        for (int k = 0; k < kRawDw; ++k) w_cur[u][k] = w_nxt[u][k];
+#pragma unroll
+        for (int k = 0; k < kWinDwords; ++k) wd_cur[u][k] = wd_nxt[u][k];
+        M_cur[u] = M_nxt[u]; off_cur[u] = off_nxt[u]; win_cur[u] = win_nxt[u];
+      }
     }
-    block_lds_barrier();  // x chunk j of every wave in LDS; chunk j-1's reads done
-    if (j + 1 < n_steps) {
-      if (esc) count_chunk(c_nxt, M_nxt, off_nxt, win_nxt, wd_nxt);
-      load_x(j + 1);
-      load_raw(j + 1, w_nxt);
-      if (!PLAIN && j + 2 < n_steps) load_codes(j + 2, c_new);
+    block_lds_barrier();  // step j's x in LDS for every wave; step j-1's reads done
+    const uint32_t q1 = (j + 1) * U, q2 = (j + 2) * U;  // first chunks of the next two steps
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q1 + u < n_chunks) {
+        if (esc) count_chunk(c_nxt[u], M_nxt[u], off_nxt[u], win_nxt[u], wd_nxt[u]);
+        load_x(q1 + u, xs[(j + 1) & 1] + u * kXChunk);
+        load_raw(q1 + u, w_nxt[u]);
+        if (!PLAIN && q2 + u < n_chunks) load_codes(q2 + u, c_new[u]);
+      }
     }
 
-    uint32_t wv[16];
-    if constexpr (PLAIN) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) wv[u] = w_cur[u];
-    } else {
-      Lane4 lr;
+    for (int u = 0; u < U; ++u) {
+      if (j * U + u >= n_chunks) continue;  // the last step's missing chunks (uniform)
+      uint32_t wv[16];
+      if constexpr (PLAIN) {
 #pragma unroll
-      for (int m = 0; m < kLaneGroups; ++m) {
-        lr.codes[m] = c_cur[m] & cmask;
-        if constexpr (kK15) {
-          const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
-          lr.raw[m][0] = __builtin_amdgcn_alignbit(w_cur[d + 1], w_cur[d], sh);
-          lr.raw[m][1] = __builtin_amdgcn_alignbit(d + 2 < 7 ? w_cur[d + 2] : 0u, w_cur[d + 1], sh);
-        } else {
-          lr.raw[m][0] = w_cur[2 * m];
-          lr.raw[m][1] = w_cur[2 * m + 1];
-        }
-      }
-      rebuild_lane<LAYOUT>(T2, lr, wv);
-      if (win_cur) {
-        // each group takes its symbols by rank from its part of the lane's
-        // window (written to LDS, where a group's dwords can be addressed)
-        uint32_t* wl = win[s] + lane * kWinStride;
-        if (M_cur != 0) {
-#pragma unroll
-          for (int u = 0; u < kWinDwords; ++u) wl[u] = wd_cur[u];
-        }
-        wave_lds_sync();
-        uint32_t fm = 0;
+        for (int k = 0; k < 16; ++k) wv[k] = w_cur[u][k];
+      } else {
+        Lane4 lr;
 #pragma unroll
         for (int m = 0; m < kLaneGroups; ++m) {
-          const uint32_t gm = (M_cur >> (8 * m)) & 0xFFu;
-          if (__ballot(gm != 0)) {
-            const uint32_t o = off_cur + fm * kSymBytes;
-            const uint32_t* gp = wl + (o >> 2);
-            uint32_t w[kGroupWin];
-#pragma unroll
-            for (int u = 0; u < kGroupWin; ++u) w[u] = gp[u];
-            if (gm) expand_window<LAYOUT>(gm, w, o & 3u, wv + 4 * m);
+          lr.codes[m] = c_cur[u][m] & cmask;
+          if constexpr (kK15) {
+            const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
+            lr.raw[m][0] = __builtin_amdgcn_alignbit(w_cur[u][d + 1], w_cur[u][d], sh);
+            lr.raw[m][1] =
+                __builtin_amdgcn_alignbit(d + 2 < 7 ? w_cur[u][d + 2] : 0u, w_cur[u][d + 1], sh);
+          } else {
+            lr.raw[m][0] = w_cur[u][2 * m];
+            lr.raw[m][1] = w_cur[u][2 * m + 1];
           }
-          fm += (uint32_t)__popc(gm);
         }
-        wave_lds_sync();  // the window area is rewritten at the next step
+        rebuild_lane<LAYOUT>(T2, lr, wv);
+        if (win_cur[u]) {
+          // each group takes its symbols by rank from its part of the lane's
+          // window (written to LDS, where a group's dwords can be addressed)
+          uint32_t* wl = win[s] + lane * kWinStride;
+          if (M_cur[u] != 0) {
+#pragma unroll
+            for (int k = 0; k < kWinDwords; ++k) wl[k] = wd_cur[u][k];
+          }
+          wave_lds_sync();
+          uint32_t fm = 0;
+#pragma unroll
+          for (int m = 0; m < kLaneGroups; ++m) {
+            const uint32_t gm = (M_cur[u] >> (8 * m)) & 0xFFu;
+            if (__ballot(gm != 0)) {
+              const uint32_t o = off_cur[u] + fm * kSymBytes;
+              const uint32_t* gp = wl + (o >> 2);
+              uint32_t w[kGroupWin];
+#pragma unroll
+              for (int k = 0; k < kGroupWin; ++k) w[k] = gp[k];
+              if (gm) expand_window<LAYOUT>(gm, w, o & 3u, wv + 4 * m);
+            }
+            fm += (uint32_t)__popc(gm);
+          }
+          wave_lds_sync();  // the window area is rewritten by the next chunk
+        }
       }
-    }
 
-    // NB products per group of 8 weights: operand B of tile t is x rows
-    // 16 t + r, columns 32 h + 8 m .. +7 of the chunk (piece 4 h + m).
-    const uint8_t* xb = xs[j & 1];
+      // NB products per group of 8 weights: operand B of tile t is x rows
+      // 16 t + r, columns 32 h + 8 m .. +7 of the chunk (piece 4 h + m).
+      static_assert(kXTile == 4096, "tile stride of lds_read_tiles");
+      const uint32_t xb = lds_addr(xs[j & 1] + u * kXChunk) + 256u * (uint32_t)r;
 #pragma unroll
-    for (int m = 0; m < kLaneGroups; ++m) {
+      for (int m = 0; m < kLaneGroups; ++m) {
+        u32x4 v[NB];
+        lds_read_tiles<NB>(xb + 16u * (uint32_t)((4 * h + m) ^ r), v);
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const u32x4 v = *(const u32x4*)(xb + kXTile * t + 256 * r + 16 * ((4 * h + m) ^ r));
-        const uint32_t bx[4] = {v[0], v[1], v[2], v[3]};
-        acc[t] = mfma_bf16(wv + 4 * m, bx, acc[t]);
+        for (int t = 0; t < NB; ++t) {
+          const uint32_t bx[4] = {v[t][0], v[t][1], v[t][2], v[t][3]};
+          acc[t] = mfma_bf16(wv + 4 * m, bx, acc[t]);
+        }
       }
     }
   }
@@ -736,7 +790,10 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]));
 #pragma unroll
   for (int t = 1; t < NB; ++t) asm volatile("" : "+v"(acc[t]));
-  // lane (r, h) holds rows 4h .. 4h+3 of the wave's 16 for batch row 16 t + r
+  // lane (r, h) holds rows 4h .. 4h+3 of the wave's 16 for batch row 16 t + r.
+  // With two column splits each output is the sum of two partial sums added
+  // into a zeroed y: 0 + p + q and 0 + q + p round to the same value, so the
+  // result does not depend on which split finishes first.
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const uint32_t bb = b0 + (uint32_t)(kMRows * t + r);
@@ -744,7 +801,13 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const uint64_t row = r0 + 4 * h + v;
-        if (row < a.rows) a.y[(uint64_t)bb * a.rows + row] = acc[t][v];
+        if (row < a.rows) {
+          float* yp = a.y + (uint64_t)bb * a.rows + row;
+          if (a.splits > 1)
+            atomicAdd(yp, acc[t][v]);
+          else
+            *yp = acc[t][v];
+        }
       }
     }
   }
@@ -796,22 +859,57 @@ static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint3
 #define WC_WIDE_NB 4
 #endif
 
+#ifndef WC_WIDE_U
+#define WC_WIDE_U 1
+#endif
+
+#ifndef WC_WIDE_NW
+#define WC_WIDE_NW 0
+#endif
+
+#ifndef WC_WIDE_SPLITS
+#define WC_WIDE_SPLITS 2
+#endif
+
 // Wide batches: WC_WIDE_NB batch tiles per block, 4 waves (64 rows) per
 // block, or 2 when that leaves fewer than two blocks per compute unit.
 template <int LAYOUT, bool PLAIN>
 static void launch_wide(GemmArgs a, hipStream_t s) {
   constexpr int kCUs = 256;
   constexpr int nb = WC_WIDE_NB;
-  a.groups = (a.batch + kMRows * nb - 1) / (kMRows * nb);
+  const uint32_t bgroups = (a.batch + kMRows * nb - 1) / (kMRows * nb);
   const uint64_t rb4 = (a.rows + 4 * kMRows - 1) / (4 * kMRows);
-  const int nw = rb4 * a.groups >= 2 * kCUs ? 4 : 2;
+  const int nw = WC_WIDE_NW ? WC_WIDE_NW : (rb4 * bgroups >= 2 * kCUs ? 4 : 2);
   const uint64_t rbs = (a.rows + (uint64_t)nw * kMRows - 1) / ((uint64_t)nw * kMRows);
+  // Column splits: each block walks its rows' chunks one after another, so
+  // when the grid holds fewer than two blocks per compute unit, two blocks on
+  // the two halves of the columns halve that chain (6144 x 24576 at batch
+  // 64: 223 -> 134 us byte-split); on a fuller grid the split measured up to
+  // 25% slower.  The split point is a whole number of 2048-weight index tiles
+  // when the rows are.
+  a.splits = WC_WIDE_SPLITS < 2 || a.chunks < 2 || rbs * bgroups >= 2 * kCUs ? 1u : 2u;
+  a.split_chunks = a.chunks;
+  if (a.splits == 2) {
+    uint32_t half = (a.chunks + 1) / 2;
+    constexpr uint32_t kTileChunks = WC_INDEX_TILE / kStepCols;
+    if (a.cols % WC_INDEX_TILE == 0) half = (half + kTileChunks - 1) / kTileChunks * kTileChunks;
+    a.split_chunks = half;
+    if (half >= a.chunks) a.splits = 1;
+  }
+  if (a.splits == 2) {
+    const uint64_t count = a.rows * a.batch;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, a.y,
+                       count);
+  }
+  a.groups = bgroups * a.splits;
   a.row_blocks = (uint32_t)rbs;
   const dim3 g((unsigned)(((rbs + 7) / 8) * 8 * a.groups));
   const dim3 t(kWave * nw);
 #define WC_WIDE_LAUNCH(NW, NB) \
-  hipLaunchKernelGGL((k_gemm_wide<LAYOUT, PLAIN, NW, NB>), g, t, 0, s, a)
-  if (nw == 4)
+  hipLaunchKernelGGL((k_gemm_wide<LAYOUT, PLAIN, NW, NB, WC_WIDE_U>), g, t, 0, s, a)
+  if (nw == 8)
+    WC_WIDE_LAUNCH(8, nb);
+  else if (nw == 4)
     WC_WIDE_LAUNCH(4, nb);
   else
     WC_WIDE_LAUNCH(2, nb);

@@ -55,6 +55,9 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
 bool gemm_mfma_fits(uint64_t rows, uint64_t cols, uint32_t batch);
 // Wide batches (33..WC_MAX_BATCH) on the matrix cores: cols a multiple of 128.
 bool gemm_wide_fits(uint64_t rows, uint64_t cols, uint32_t batch);
+// y[0 .. count) = 0 (wc_gemv.hip; a kernel rather than a memset, so that a
+// captured launch sequence holds no memset node).
+__global__ void k_fill_zero(float* y, uint64_t count);
 hipError_t launch_decode_gemm_mfma(const wc_header& h, const uint8_t* container, uint64_t rows,
                                    uint64_t cols, const uint16_t* x, uint32_t batch, float* y,
                                    hipStream_t s);
