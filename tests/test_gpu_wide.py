@@ -109,3 +109,23 @@ def test_wide_deterministic():
     y2 = wc.decode_gemv(h, c, 130, 4096, xd)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wide_mlp_sampled(layout):
+    """The MLP pair (14336 x 4096 and 4096 x 14336, row scales over three
+    decades: K15 escapes about 28% of the weights, so nearly every lane patches
+    its symbols every step), batch 64 and 100; 256 sampled rows each."""
+    m = synth.mlp()
+    for name in ("W1", "W2"):
+        W = m[name]
+        rows, cols = W.shape
+        h, c = gpu_encode(layout, W)
+        X = synth.vectors(synth.SEEDS["mlp"] * 10 + 7, 100, cols)
+        sample = np.sort(np.random.default_rng(9).choice(rows, 256, replace=False))
+        y64, a = oracle.gemv_f64(np.ascontiguousarray(W[sample]), X)
+        for batch in (64, 100):
+            y = wc.decode_gemv(h, c, rows, cols, dev16(X[:batch]))
+            torch.cuda.synchronize()
+            assert_gemv_close(y.cpu().numpy()[:, sample], y64[:batch], a[:batch],
+                              f"mlp {name} layout {layout} b={batch}")
