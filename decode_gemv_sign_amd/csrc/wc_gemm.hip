@@ -96,6 +96,26 @@ __device__ inline uint32_t compress_marks(const uint32_t esc[kLaneGroups]) {
   return M;
 }
 
+// A lane's 32 weights as Lane4: its codes (masked) and its raw part as
+// loaded, 32 bytes (byte-split, group m = dwords 2m, 2m+1) or 28 bytes (K15,
+// group m's 56 bits from byte 7m).
+template <int LAYOUT>
+__device__ inline void lane_of_chunk(const uint32_t c[kLaneGroups], uint32_t cmask,
+                                     const uint32_t* wr, Lane4& l) {
+#pragma unroll
+  for (int m = 0; m < kLaneGroups; ++m) {
+    l.codes[m] = c[m] & cmask;
+    if constexpr (LAYOUT == WC_LAYOUT_K15) {
+      const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
+      l.raw[m][0] = __builtin_amdgcn_alignbit(wr[d + 1], wr[d], sh);
+      l.raw[m][1] = __builtin_amdgcn_alignbit(d + 2 < 7 ? wr[d + 2] : 0u, wr[d + 1], sh);
+    } else {
+      l.raw[m][0] = wr[2 * m];
+      l.raw[m][1] = wr[2 * m + 1];
+    }
+  }
+}
+
 template <int LAYOUT, bool PLAIN>
 struct GemmSlot {
   uint32_t c[kLaneGroups];                                     // codes, group m in c[m]
@@ -278,19 +298,7 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
             wd[kWinDwords - 1] = sp[kWinDwords - 1];
           }
           Lane4 lr;
-#pragma unroll
-          for (int m = 0; m < kLaneGroups; ++m) {
-            lr.codes[m] = l.codes[m];
-            if constexpr (kK15) {
-              // group m's 56 bits start at byte 7m of the lane's 28 bytes
-              const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
-              lr.raw[m][0] = __builtin_amdgcn_alignbit(cur.wr[d + 1], cur.wr[d], sh);
-              lr.raw[m][1] = __builtin_amdgcn_alignbit(d + 2 < 7 ? cur.wr[d + 2] : 0u, cur.wr[d + 1], sh);
-            } else {
-              lr.raw[m][0] = cur.wr[2 * m];
-              lr.raw[m][1] = cur.wr[2 * m + 1];
-            }
-          }
+          lane_of_chunk<LAYOUT>(l.codes, ~0u, cur.wr, lr);
           rebuild_lane<LAYOUT>(T2, lr, wv);
           uint32_t* wl = win[s] + lane * kWinStride;
           if (cnt != 0) {
@@ -372,18 +380,7 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
     if constexpr (!PLAIN) {
       if (!rebuilt) {
         Lane4 lr;
-#pragma unroll
-        for (int m = 0; m < kLaneGroups; ++m) {
-          lr.codes[m] = cur.c[m] & cmask;
-          if constexpr (kK15) {
-            const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
-            lr.raw[m][0] = __builtin_amdgcn_alignbit(cur.wr[d + 1], cur.wr[d], sh);
-            lr.raw[m][1] = __builtin_amdgcn_alignbit(d + 2 < 7 ? cur.wr[d + 2] : 0u, cur.wr[d + 1], sh);
-          } else {
-            lr.raw[m][0] = cur.wr[2 * m];
-            lr.raw[m][1] = cur.wr[2 * m + 1];
-          }
-        }
+        lane_of_chunk<LAYOUT>(cur.c, cmask, cur.wr, lr);
         rebuild_lane<LAYOUT>(T2, lr, wv);
       }
     }
@@ -728,19 +725,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
         for (int k = 0; k < 16; ++k) wv[k] = w_cur[u][k];
       } else {
         Lane4 lr;
-#pragma unroll
-        for (int m = 0; m < kLaneGroups; ++m) {
-          lr.codes[m] = c_cur[u][m] & cmask;
-          if constexpr (kK15) {
-            const int d = (7 * m) >> 2, sh = ((7 * m) & 3) * 8;
-            lr.raw[m][0] = __builtin_amdgcn_alignbit(w_cur[u][d + 1], w_cur[u][d], sh);
-            lr.raw[m][1] =
-                __builtin_amdgcn_alignbit(d + 2 < 7 ? w_cur[u][d + 2] : 0u, w_cur[u][d + 1], sh);
-          } else {
-            lr.raw[m][0] = w_cur[u][2 * m];
-            lr.raw[m][1] = w_cur[u][2 * m + 1];
-          }
-        }
+        lane_of_chunk<LAYOUT>(c_cur[u], cmask, w_cur[u], lr);
         rebuild_lane<LAYOUT>(T2, lr, wv);
         if (win_cur[u]) {
           // each group takes its symbols by rank from its part of the lane's
