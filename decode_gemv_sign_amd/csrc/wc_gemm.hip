@@ -493,8 +493,11 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
 // step, and before a plain read it would wait for all of those loads.
 template <int NB>
 __device__ inline void lds_read_tiles(uint32_t addr, u32x4 (&v)[NB]) {
-  static_assert(NB == 2 || NB == 4, "batch tiles per block");
-  if constexpr (NB == 2) {
+  static_assert(NB == 2 || NB == 4 || NB == 8, "batch tiles per block");
+  if constexpr (NB == 8) {
+    lds_read_tiles<4>(addr, *reinterpret_cast<u32x4(*)[4]>(&v[0]));
+    lds_read_tiles<4>(addr + 16384u, *reinterpret_cast<u32x4(*)[4]>(&v[4]));
+  } else if constexpr (NB == 2) {
     asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
                  : "=&v"(v[0]), "=&v"(v[1]) : "v"(addr) : "memory");
   } else {
@@ -841,7 +844,7 @@ static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint3
 }
 
 #ifndef WC_WIDE_NB
-#define WC_WIDE_NB 4
+#define WC_WIDE_NB 0  // batch tiles per block: 0 = chosen per layout and size
 #endif
 
 #ifndef WC_WIDE_U
@@ -849,19 +852,36 @@ static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint3
 #endif
 
 #ifndef WC_WIDE_NW
-#define WC_WIDE_NW 0
+#define WC_WIDE_NW 0  // waves per block: 0 = chosen by grid size
 #endif
 
 #ifndef WC_WIDE_SPLITS
 #define WC_WIDE_SPLITS 2
 #endif
 
-// Wide batches: WC_WIDE_NB batch tiles per block, 4 waves (64 rows) per
-// block, or 2 when that leaves fewer than two blocks per compute unit.
+// Wide batches: 4 or 8 batch tiles per block, 4 waves (64 rows) per block,
+// or 2 when that leaves fewer than two blocks per compute unit.  Eight tiles
+// halve the decode work per product and the weight re-reads, at the cost of
+// LDS (fewer blocks per compute unit).  Measured (us, 4 vs 8 tiles): K15
+// fused on 6144 x 24576 265 -> 225 at batch 64 and 522 -> 462 at 256, but
+// 42 -> 49 on 4096 x 4096 at batch 64; byte-split fused 132 -> 155 and
+// 288 -> 326 on 6144 x 24576; the plain kernel 386 -> 340 at batch 256 and
+// 150 -> 166 at 64.
+static_assert(WC_WIDE_NB == 0 || WC_WIDE_NB == 4 || WC_WIDE_NB == 8, "instantiated tile counts");
+static_assert(WC_WIDE_NW == 0 || WC_WIDE_NW == 2 || WC_WIDE_NW == 4, "instantiated wave counts");
+
+template <int LAYOUT, bool PLAIN>
+static int wide_tiles(const GemmArgs& a) {
+  if (WC_WIDE_NB) return WC_WIDE_NB;
+  if (PLAIN) return a.batch >= 128 ? 8 : 4;
+  if (LAYOUT == WC_LAYOUT_K15) return a.batch > 64 || a.rows * a.cols >= (1ull << 26) ? 8 : 4;
+  return 4;
+}
+
 template <int LAYOUT, bool PLAIN>
 static void launch_wide(GemmArgs a, hipStream_t s) {
   constexpr int kCUs = 256;
-  constexpr int nb = WC_WIDE_NB;
+  const int nb = wide_tiles<LAYOUT, PLAIN>(a);
   const uint32_t bgroups = (a.batch + kMRows * nb - 1) / (kMRows * nb);
   const uint64_t rb4 = (a.rows + 4 * kMRows - 1) / (4 * kMRows);
   const int nw = WC_WIDE_NW ? WC_WIDE_NW : (rb4 * bgroups >= 2 * kCUs ? 4 : 2);
@@ -892,12 +912,14 @@ static void launch_wide(GemmArgs a, hipStream_t s) {
   const dim3 t(kWave * nw);
 #define WC_WIDE_LAUNCH(NW, NB) \
   hipLaunchKernelGGL((k_gemm_wide<LAYOUT, PLAIN, NW, NB, WC_WIDE_U>), g, t, 0, s, a)
-  if (nw == 8)
-    WC_WIDE_LAUNCH(8, nb);
+  if (nw == 4 && nb == 8)
+    WC_WIDE_LAUNCH(4, 8);
   else if (nw == 4)
-    WC_WIDE_LAUNCH(4, nb);
+    WC_WIDE_LAUNCH(4, 4);
+  else if (nb == 8)
+    WC_WIDE_LAUNCH(2, 8);
   else
-    WC_WIDE_LAUNCH(2, nb);
+    WC_WIDE_LAUNCH(2, 4);
 #undef WC_WIDE_LAUNCH
 }
 
