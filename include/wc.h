@@ -164,7 +164,7 @@ int wc_decode(const wc_header *h, const uint8_t *d_container,
  * 1..WC_MAX_BATCH, else WC_E_UNSUPPORTED.  Above 32 input rows (the
  * prefill regime, where the pages' closest prior art is a fused
  * decompression-GEMM [P2 "¿Cómo encaja con los sistemas anteriores?"])
- * each rebuilt weight is used by up to 64 input rows on the matrix cores
+ * each rebuilt weight is used by up to 128 input rows on the matrix cores
  * when cols is a multiple of 128; other batches above 16 run 16 input rows
  * at a time.
  */
