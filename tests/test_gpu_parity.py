@@ -313,15 +313,17 @@ def test_maximum_size_roundtrip(layout):
 
 def test_maximum_size_gemv():
     """65535 x 65536 (n just below 2^32), byte-split, batch 1 (LDS-ring
-    kernel) and 16 (matrix cores): sampled rows against the oracle."""
+    kernel), 16 (matrix cores) and 64 (wide matrix-core kernel): sampled rows
+    against the oracle."""
     rows, cols = 65535, 65536
     print(f"max-size GEMV: {rows}x{cols}", flush=True)
     w = _gpu_normal_bits(rows * cols, 2030)
     h, c = wc.encode(w, wc.BYTESPLIT)
-    X = synth.vectors(2031, 16, cols)
+    X = synth.vectors(2031, 64, cols)
     sample = [0, 1, 2047, 32768, rows - 2, rows - 1]
     Ws = w.view(rows, cols)[sample].cpu().numpy().view(np.uint16)
-    for batch in (1, 16):
+    for batch in (1, 16, 64):
+        print(f"max-size GEMV batch {batch}", flush=True)
         y = wc.decode_gemv(h, c, rows, cols, dev16(X[:batch]))
         torch.cuda.synchronize()
         y64, a = oracle.gemv_f64(Ws, X[:batch])
@@ -400,6 +402,13 @@ def test_gemv_cols_zero_and_rows_zero():
     assert torch.all(y == 0)
     y0 = torch.empty((3, 0), device=DEV)
     wc.decode_gemv(h, c, 0, 17, torch.zeros((3, 17), dtype=torch.int16, device=DEV), out=y0)
+    # the same at a batch for the wide path
+    y = torch.full((64, 5), 7.0, device=DEV)
+    wc.decode_gemv(h, c, 5, 0, torch.zeros((64, 0), dtype=torch.int16, device=DEV), out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+    wc.decode_gemv(h, c, 0, 128, torch.zeros((64, 128), dtype=torch.int16, device=DEV),
+                   out=torch.empty((64, 0), device=DEV))
 
 
 def test_error_codes():

@@ -44,7 +44,7 @@ def _tensor(rows, cols, dense, seed):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS + [wc.RAW])
-@pytest.mark.parametrize("rows,cols,dense", [(19, 128, False), (77, 640, True),
+@pytest.mark.parametrize("rows,cols,dense", [(1, 4096, False), (19, 128, False), (77, 640, True),
                                              (130, 4096, True), (45, 1056, True)])
 def test_wide_batches(layout, rows, cols, dense):
     W = _tensor(rows, cols, dense, 2100 + rows)
