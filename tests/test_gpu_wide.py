@@ -129,3 +129,24 @@ def test_wide_mlp_sampled(layout):
             torch.cuda.synchronize()
             assert_gemv_close(y.cpu().numpy()[:, sample], y64[:batch], a[:batch],
                               f"mlp {name} layout {layout} b={batch}")
+
+
+def test_wide_random_shapes():
+    """Seeded random shapes: rows 1..300, columns a multiple of 128 (on and
+    off the 2048-weight index grid) or not, batches 17..256, both layouts,
+    escape densities from sparse to dense rows."""
+    rng = np.random.default_rng(2400)
+    for case in range(16):
+        rows = int(rng.integers(1, 301))
+        k = int(rng.integers(1, 33))
+        cols = 128 * k if case % 4 else 128 * k + 32
+        batch = int(rng.integers(17, 257))
+        layout = LAYOUTS[case % 2]
+        W = _tensor(rows, cols, bool(case % 3 == 0), 2500 + case)
+        X = synth.vectors(2600 + case, batch, cols)
+        h, c = gpu_encode(layout, W)
+        y = wc.decode_gemv(h, c, rows, cols, dev16(X))
+        torch.cuda.synchronize()
+        y64, a = oracle.gemv_f64(W, X)
+        assert_gemv_close(y.cpu().numpy(), y64, a,
+                          f"case {case}: {rows}x{cols} layout {layout} b={batch}")
