@@ -923,11 +923,21 @@ static void launch_wide(GemmArgs a, hipStream_t s) {
 #undef WC_WIDE_LAUNCH
 }
 
-// Batches up to 32 run faster as two launches of the 16-row kernel: the wide
-// kernel's time is set by one memory round trip per 128-column step of a
-// block, whatever its batch (measured on 4096 x 4096 and 6144 x 24576).
+// The wide kernel's time is set by one memory round trip per 128-column
+// step of a block, whatever its batch.  On tensors of 2^26 weights or more it
+// beats launches of the 16-row kernel from batch 17 (6144 x 24576 at batch
+// 32, byte-split: 129 against 217 us); on 4096 x 4096 only from about batch
+// 32, so smaller tensors take it above 32.
+#ifndef WC_WIDE_MIN_BATCH
+#define WC_WIDE_MIN_BATCH 0  // 0 = by tensor size, as above
+#endif
+
 bool gemm_wide_fits(uint64_t rows, uint64_t cols, uint32_t batch) {
-  return rows > 0 && cols > 0 && cols % kStepCols == 0 && batch > 2 * kMRows &&
+  static_assert(WC_WIDE_MIN_BATCH == 0 || WC_WIDE_MIN_BATCH > kMRows,
+                "the wide kernel is for batches above 16");
+  const uint32_t min_batch = WC_WIDE_MIN_BATCH ? WC_WIDE_MIN_BATCH
+                             : rows * cols >= (1ull << 26) ? kMRows + 1 : 2 * kMRows + 1;
+  return rows > 0 && cols > 0 && cols % kStepCols == 0 && batch >= min_batch &&
          batch <= WC_MAX_BATCH && cols / kStepCols < (1ull << 31) &&
          rows / (2 * kMRows) < (1ull << 31) / 8;
 }

@@ -53,7 +53,8 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
                               hipStream_t s);
 // Matrix-core paths (wc_gemm.hip): cols a multiple of 32, batch 1..16.
 bool gemm_mfma_fits(uint64_t rows, uint64_t cols, uint32_t batch);
-// Wide batches (33..WC_MAX_BATCH) on the matrix cores: cols a multiple of 128.
+// Wide batches on the matrix cores (from 17 on tensors of 2^26 weights or
+// more, else from 33, up to WC_MAX_BATCH): cols a multiple of 128.
 bool gemm_wide_fits(uint64_t rows, uint64_t cols, uint32_t batch);
 // y[0 .. count) = 0 (wc_gemv.hip; a kernel rather than a memset, so that a
 // captured launch sequence holds no memset node).

@@ -161,12 +161,12 @@ int wc_decode(const wc_header *h, const uint8_t *d_container,
  * with escapes applied and never written to memory.  d_x: BF16 [batch][cols];
  * d_y: fp32 [batch][rows].  Products are exact (BF16 x BF16), sums are fp32
  * in an order that differs from a sequential loop.  batch in
- * 1..WC_MAX_BATCH, else WC_E_UNSUPPORTED.  Above 32 input rows (the
- * prefill regime, where the pages' closest prior art is a fused
- * decompression-GEMM [P2 "¿Cómo encaja con los sistemas anteriores?"])
- * each rebuilt weight is used by up to 128 input rows on the matrix cores
- * when cols is a multiple of 128; other batches above 16 run 16 input rows
- * at a time.
+ * 1..WC_MAX_BATCH, else WC_E_UNSUPPORTED.  In the prefill regime, where
+ * the pages' closest prior art is a fused decompression-GEMM [P2 "¿Cómo
+ * encaja con los sistemas anteriores?"], each rebuilt weight is used by up
+ * to 128 input rows on the matrix cores: above 32 input rows (above 16 on
+ * tensors of 2^26 weights or more) when cols is a multiple of 128.  Other
+ * batches above 16 run 16 input rows at a time.
  */
 int wc_decode_gemv(const wc_header *h, const uint8_t *d_container,
                    size_t container_bytes, uint64_t rows, uint64_t cols,

@@ -1,7 +1,8 @@
-"""GPU parity above 16 input rows (33 .. 256 take the wide matrix-core
-path, 17 .. 32 run 16 rows at a time): the fused decode-GEMM and the plain
-BF16 kernel of the same shape against the CPU oracle, to the same
-per-element bar as the GEMV (tests/tolerance.py).
+"""GPU parity above 16 input rows (the wide matrix-core path from batch 33,
+or 17 on tensors of 2^26 weights or more; smaller batches run 16 rows at a
+time): the fused decode-GEMM and the plain BF16 kernel of the same shape
+against the CPU oracle, to the same per-element bar as the GEMV
+(tests/tolerance.py).
 
 This is the prefill regime, where page "Compresión de pesos LLM sin pérdida
 vs 8-bit GGUF: ¿qué está listo para producción?", section "¿Cómo encaja con
@@ -87,18 +88,27 @@ def test_wide_square_workload_sampled(layout):
 
 def test_wide_banded_sampled():
     """6144 x 24576 with 5% escapes in 64-row bands (rows of 12 index
-    tiles), K15 and byte-split, batch 64; 384 sampled rows."""
+    tiles), K15, byte-split and the plain kernel, batches 24 (a tensor this
+    large takes the wide kernel from batch 17) and 64; 384 sampled rows."""
     d = synth.banded()
     W = d["W"]
     rows, cols = W.shape
     X = synth.vectors(synth.SEEDS["banded"] * 10 + 7, 64, cols)
     sample = np.sort(np.random.default_rng(8).choice(rows, 384, replace=False))
     y64, a = oracle.gemv_f64(np.ascontiguousarray(W[sample]), X)
-    for layout in LAYOUTS:
-        h, c = gpu_encode(layout, W)
-        y = wc.decode_gemv(h, c, rows, cols, dev16(X))
+    Wd = dev16(W)
+    for batch in (24, 64):
+        xd = dev16(X[:batch])
+        yb = wc.gemv_bf16(Wd, xd)
         torch.cuda.synchronize()
-        assert_gemv_close(y.cpu().numpy()[:, sample], y64, a, f"banded layout {layout} b=64")
+        assert_gemv_close(yb.cpu().numpy()[:, sample], y64[:batch], a[:batch],
+                          f"banded plain b={batch}")
+        for layout in LAYOUTS:
+            h, c = gpu_encode(layout, W)
+            y = wc.decode_gemv(h, c, rows, cols, xd)
+            torch.cuda.synchronize()
+            assert_gemv_close(y.cpu().numpy()[:, sample], y64[:batch], a[:batch],
+                              f"banded layout {layout} b={batch}")
 
 
 def test_wide_deterministic():
