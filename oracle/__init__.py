@@ -25,6 +25,7 @@ import numpy as np
 BYTESPLIT = 0
 K15 = 1
 RAW = 2
+COMPACT = 1  # container flag: escape symbols only, positions implied by the code-15 marks
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wc_oracle.c")
@@ -59,7 +60,10 @@ def _bind(path: str):
     lib.orc_histogram.argtypes = [I, P, U64, P]
     lib.orc_dictionary.argtypes = [I, P, U64, P, P, P]
     lib.orc_container_size.argtypes = [I, U64, U64, P]
+    lib.orc_container_size_flags.argtypes = [I, I, U64, U64, P]
     lib.orc_encode.argtypes = [I, P, U64, P, U64, P]
+    lib.orc_encode_flags.argtypes = [I, I, P, U64, P, U64, P]
+    lib.orc_header_flags.argtypes = [P, U64, P]
     lib.orc_header_info.argtypes = [P, U64, P, P, P, P, P, P]
     lib.orc_decode.argtypes = [P, U64, P, U64]
     lib.orc_gemv_f32.argtypes = [P, U64, U64, P, ctypes.c_uint32, P]
@@ -69,7 +73,8 @@ def _bind(path: str):
     for f in (lib.orc_histogram, lib.orc_dictionary, lib.orc_container_size,
               lib.orc_encode, lib.orc_header_info, lib.orc_decode,
               lib.orc_gemv_f32, lib.orc_gemv_f64, lib.orc_bits_per_weight,
-              lib.orc_choose_layout):
+              lib.orc_choose_layout, lib.orc_container_size_flags, lib.orc_encode_flags,
+              lib.orc_header_flags):
         f.restype = I
     return lib
 
@@ -128,9 +133,13 @@ def dictionary(layout: int, counts: np.ndarray, n: int):
     return d, nd.value, ne.value
 
 
-def container_size(layout: int, n: int, n_esc: int) -> int:
+def container_size(layout: int, n: int, n_esc: int, flags: int = 0) -> int:
     t = ctypes.c_uint64(0)
-    _check(_load().orc_container_size(layout, n, n_esc, ctypes.byref(t)), "container_size")
+    if flags:
+        st = _load().orc_container_size_flags(layout, flags, n, n_esc, ctypes.byref(t))
+    else:
+        st = _load().orc_container_size(layout, n, n_esc, ctypes.byref(t))
+    _check(st, "container_size")
     return t.value
 
 
@@ -142,17 +151,22 @@ def choose_layout(w) -> int:
     return lay.value
 
 
-def encode(layout: int, w) -> np.ndarray:
+def encode(layout: int, w, flags: int = 0) -> np.ndarray:
+    """The container of w; flags=COMPACT drops the escape-position stream."""
     a = _u16(w)
     n_esc = 0
     if layout != RAW:
         counts = histogram(layout, a)
         _, _, n_esc = dictionary(layout, counts, a.size)
-    cap = container_size(layout, a.size, n_esc)
+    cap = container_size(layout, a.size, n_esc, flags)
     out = np.zeros(cap, dtype=np.uint8)
     size = ctypes.c_uint64(0)
-    _check(_load().orc_encode(layout, _ptr(a), a.size, _ptr(out), cap, ctypes.byref(size)),
-           "encode")
+    if flags:
+        st = _load().orc_encode_flags(layout, flags, _ptr(a), a.size, _ptr(out), cap,
+                                      ctypes.byref(size))
+    else:
+        st = _load().orc_encode(layout, _ptr(a), a.size, _ptr(out), cap, ctypes.byref(size))
+    _check(st, "encode")
     assert size.value == cap
     return out
 
@@ -168,7 +182,10 @@ def header_info(container: np.ndarray) -> dict:
     _check(_load().orc_header_info(_ptr(c), c.size, ctypes.byref(lay), ctypes.byref(nd),
                                    ctypes.byref(n), ctypes.byref(ne), _ptr(d), _ptr(off)),
            "header")
-    return {"layout": lay.value, "n_dict": nd.value, "n": n.value, "n_esc": ne.value,
+    fl = ctypes.c_int(0)
+    _check(_load().orc_header_flags(_ptr(c), c.size, ctypes.byref(fl)), "header")
+    return {"layout": lay.value, "flags": fl.value, "n_dict": nd.value, "n": n.value,
+            "n_esc": ne.value,
             "dict": d, "off_codes": int(off[0]), "off_raw": int(off[1]),
             "off_esc_pos": int(off[2]), "off_esc_sym": int(off[3]),
             "total_bytes": int(off[4]), "off_esc_idx": int(off[5])}

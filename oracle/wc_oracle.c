@@ -47,6 +47,7 @@
 #define ORC_VERSION 2u
 #define ORC_HEADER_BYTES 128u
 #define ORC_INDEX_TILE 2048u /* weights per escape-index entry */
+#define ORC_FLAGS_AT 104u     /* header byte holding the container flags */
 
 /* ---- little-endian field access (byte by byte) ------------------------- */
 
@@ -106,14 +107,20 @@ static int layout_ok(int layout) {
 /* layouts with a dictionary and escapes */
 static int coded(int layout) { return layout != ORC_LAYOUT_RAW; }
 
+/* bytes of the escape-position stream: one u32 per escape, none in the
+ * compact form, whose positions are implied by the code-15 marks */
+static uint64_t pos_bytes(int flags, uint64_t e) {
+  return (flags & ORC_FLAG_COMPACT) ? 0u : 4u * e;
+}
+
 /* stream offsets for n weights and e escapes, in the header's field order:
  * off[0] codes, off[1] raw, off[2] escape positions, off[3] escape symbols,
  * off[4] total container bytes, off[5] escape index (the last stream) */
-static void layout_offsets(int layout, uint64_t n, uint64_t e, uint64_t off[6]) {
+static void layout_offsets(int layout, int flags, uint64_t n, uint64_t e, uint64_t off[6]) {
   off[0] = ORC_HEADER_BYTES;
   off[1] = pad16(off[0] + code_stream_bytes(layout, n));
   off[2] = pad16(off[1] + raw_stream_bytes(layout, n));
-  off[3] = pad16(off[2] + 4u * e);
+  off[3] = pad16(off[2] + pos_bytes(flags, e));
   off[5] = pad16(off[3] + sym_bytes(layout) * e);
   off[4] = pad16(off[5] + 4u * index_entries(n, e));
 }
@@ -156,14 +163,25 @@ int orc_dictionary(int layout, const uint64_t *counts, uint64_t n,
   return ORC_OK;
 }
 
-int orc_container_size(int layout, uint64_t n, uint64_t n_esc, uint64_t *total) {
-  if (!layout_ok(layout) || !total) return ORC_E_ARG;
+/* the flags a layout may carry: the compact escape form needs escapes'
+ * codes, so the raw layout takes none */
+static int flags_ok(int layout, int flags) {
+  return flags == 0 || (flags == ORC_FLAG_COMPACT && coded(layout));
+}
+
+int orc_container_size_flags(int layout, int flags, uint64_t n, uint64_t n_esc,
+                             uint64_t *total) {
+  if (!layout_ok(layout) || !flags_ok(layout, flags) || !total) return ORC_E_ARG;
   if (n >= (1ull << 32)) return ORC_E_SIZE;
   if (n_esc > n || (!coded(layout) && n_esc)) return ORC_E_ARG;
   uint64_t off[6];
-  layout_offsets(layout, n, n_esc, off);
+  layout_offsets(layout, flags, n, n_esc, off);
   *total = off[4];
   return ORC_OK;
+}
+
+int orc_container_size(int layout, uint64_t n, uint64_t n_esc, uint64_t *total) {
+  return orc_container_size_flags(layout, 0, n, n_esc, total);
 }
 
 /* ---- layout choice [the pages ask for a BF16 fallback: page "Compresión
@@ -199,15 +217,16 @@ int orc_choose_layout(const uint16_t *w, uint64_t n, int *layout) {
 
 /* ---- steps 3–6: codes, raw stream, escape stream, container ----------- */
 
-int orc_encode(int layout, const uint16_t *w, uint64_t n,
-               uint8_t *out, uint64_t cap, uint64_t *size) {
-  if (!layout_ok(layout) || !out || !size || (n && !w)) return ORC_E_ARG;
+int orc_encode_flags(int layout, int flags, const uint16_t *w, uint64_t n,
+                     uint8_t *out, uint64_t cap, uint64_t *size) {
+  if (!layout_ok(layout) || !flags_ok(layout, flags) || !out || !size || (n && !w))
+    return ORC_E_ARG;
   if (n >= (1ull << 32)) return ORC_E_SIZE; /* positions are u32 */
 
   if (!coded(layout)) {
     /* raw: header, then every weight as a little-endian u16 */
     uint64_t off[6];
-    layout_offsets(layout, n, 0, off);
+    layout_offsets(layout, 0, n, 0, off);
     if (cap < off[4]) return ORC_E_SIZE;
     memset(out, 0, off[4]);
     for (uint64_t i = 0; i < n; ++i) put_le(out + off[1] + 2u * i, w[i], 2);
@@ -228,7 +247,7 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
   orc_dictionary(layout, counts, n, dict, &n_dict, &n_esc);
 
   uint64_t off[6];
-  layout_offsets(layout, n, n_esc, off);
+  layout_offsets(layout, flags, n, n_esc, off);
   if (cap < off[4]) return ORC_E_SIZE;
   memset(out, 0, off[4]); /* gaps and tails are zero */
 
@@ -260,9 +279,11 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
         raw[bit / 8] |= (uint8_t)(((r >> k) & 1u) << (bit % 8));
       }
     }
-    /* rare symbol: exact escape record (position, symbol) in weight order */
+    /* rare symbol: exact escape record (position, symbol) in weight order;
+     * the compact form keeps the symbol only (its position is the weight's
+     * code-15 mark) */
     if (c == 15) {
-      put_le(esc_pos + 4u * e, i, 4);
+      if (!(flags & ORC_FLAG_COMPACT)) put_le(esc_pos + 4u * e, i, 4);
       put_le(esc_sym + sym_bytes(layout) * e, s, (int)sym_bytes(layout));
       e += 1;
     }
@@ -280,8 +301,14 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
   put_le(h + 16, n_esc, 8);
   for (int k = 0; k < 16; ++k) put_le(h + 24 + 2 * k, dict[k], 2);
   for (int k = 0; k < 6; ++k) put_le(h + 56 + 8 * k, off[k], 8);
+  put_le(h + ORC_FLAGS_AT, (uint64_t)flags, 1);
   *size = off[4];
   return ORC_OK;
+}
+
+int orc_encode(int layout, const uint16_t *w, uint64_t n,
+               uint8_t *out, uint64_t cap, uint64_t *size) {
+  return orc_encode_flags(layout, 0, w, n, out, cap, size);
 }
 
 /* ---- header reader: every field checked against the definition -------- */
@@ -305,19 +332,32 @@ int orc_header_info(const uint8_t *c, uint64_t size, int *layout, int *n_dict,
     for (int j = 0; j < k && k < nd; ++j)
       if (dict[j] == dict[k]) return ORC_E_CORRUPT;
   }
+  int fl = (int)c[ORC_FLAGS_AT];
+  if (!flags_ok(lay, fl)) return ORC_E_CORRUPT;
   uint64_t want[6];
-  layout_offsets(lay, nn, ne, want);
+  layout_offsets(lay, fl, nn, ne, want);
   for (int k = 0; k < 6; ++k) {
     offsets[k] = get_le(c + 56 + 8 * k, 8);
     if (offsets[k] != want[k]) return ORC_E_CORRUPT;
   }
-  for (int k = 104; k < 128; ++k)
+  for (int k = ORC_FLAGS_AT + 1; k < 128; ++k)
     if (c[k] != 0) return ORC_E_CORRUPT;
   if (offsets[4] > size) return ORC_E_CORRUPT;
   *layout = lay;
   *n_dict = nd;
   *n = nn;
   *n_esc = ne;
+  return ORC_OK;
+}
+
+int orc_header_flags(const uint8_t *c, uint64_t size, int *flags) {
+  int layout, n_dict;
+  uint64_t n, n_esc, off[6];
+  uint16_t dict[16];
+  if (!flags) return ORC_E_ARG;
+  int st = orc_header_info(c, size, &layout, &n_dict, &n, &n_esc, dict, off);
+  if (st != ORC_OK) return st;
+  *flags = (int)c[ORC_FLAGS_AT];
   return ORC_OK;
 }
 
@@ -342,6 +382,7 @@ int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap) {
   const uint8_t *esc_pos = c + off[2];
   const uint8_t *esc_sym = c + off[3];
   const uint8_t *esc_idx = c + off[5];
+  const int compact = (c[ORC_FLAGS_AT] & ORC_FLAG_COMPACT) != 0;
   uint64_t e = 0;
   for (uint64_t i = 0; i < n; ++i) {
     /* every index entry must count the escapes before its tile */
@@ -350,7 +391,9 @@ int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap) {
     uint32_t code = (codes[i / 2] >> ((i % 2) * 4)) & 15u;
     uint32_t s;
     if (code == 15) {
-      if (e >= n_esc || get_le(esc_pos + 4u * e, 4) != i) return ORC_E_CORRUPT;
+      /* the e-th escape record belongs to the e-th code-15 weight; a full
+       * record also names that weight's position */
+      if (e >= n_esc || (!compact && get_le(esc_pos + 4u * e, 4) != i)) return ORC_E_CORRUPT;
       s = (uint32_t)get_le(esc_sym + sym_bytes(layout) * e, (int)sym_bytes(layout));
       if (s >= (uint32_t)n_symbols(layout)) return ORC_E_CORRUPT;
       e += 1;
@@ -437,8 +480,9 @@ int orc_bits_per_weight(const uint8_t *c, uint64_t size, double *bpw,
   int st = orc_header_info(c, size, &layout, &n_dict, &n, &n_esc, dict, off);
   if (st != ORC_OK) return st;
   if (!bpw || !payload_bpw || n == 0) return ORC_E_ARG;
-  uint64_t payload = code_stream_bytes(layout, n) + raw_stream_bytes(layout, n) + 4u * n_esc +
-                     sym_bytes(layout) * n_esc + 4u * index_entries(n, n_esc);
+  uint64_t payload = code_stream_bytes(layout, n) + raw_stream_bytes(layout, n) +
+                     pos_bytes(c[ORC_FLAGS_AT], n_esc) + sym_bytes(layout) * n_esc +
+                     4u * index_entries(n, n_esc);
   *bpw = 8.0 * (double)off[4] / (double)n;
   *payload_bpw = 8.0 * (double)payload / (double)n;
   return ORC_OK;

@@ -44,6 +44,11 @@ extern "C" {
 #define ORC_LAYOUT_K15 1
 #define ORC_LAYOUT_RAW 2 /* the BF16 bit patterns stored as they are */
 
+/* Container flags (header byte 104).  ORC_FLAG_COMPACT: the escape stream
+ * holds the symbols only, in weight order; the k-th weight whose code is 15
+ * takes the k-th symbol (no position stream).  Coded layouts only. */
+#define ORC_FLAG_COMPACT 1
+
 #define ORC_OK 0
 #define ORC_E_ARG (-1)
 #define ORC_E_SIZE (-2)
@@ -58,16 +63,22 @@ int orc_histogram(int layout, const uint16_t *w, uint64_t n, uint64_t *counts);
 int orc_dictionary(int layout, const uint64_t *counts, uint64_t n,
                    uint16_t dict[16], int *n_dict, uint64_t *n_esc);
 
-/* Exact container size for n weights with n_esc escapes. */
+/* Exact container size for n weights with n_esc escapes (flags 0, or
+ * with the given flags). */
 int orc_container_size(int layout, uint64_t n, uint64_t n_esc, uint64_t *total);
+int orc_container_size_flags(int layout, int flags, uint64_t n, uint64_t n_esc,
+                             uint64_t *total);
 
 /* The layout whose container is smallest for w[0..n): byte-split, K15 or
  * raw, ties to the lower layout number. */
 int orc_choose_layout(const uint16_t *w, uint64_t n, int *layout);
 
-/* Full encode into out[0..cap); *size receives the container size. */
+/* Full encode into out[0..cap); *size receives the container size
+ * (orc_encode: flags 0). */
 int orc_encode(int layout, const uint16_t *w, uint64_t n,
                uint8_t *out, uint64_t cap, uint64_t *size);
+int orc_encode_flags(int layout, int flags, const uint16_t *w, uint64_t n,
+                     uint8_t *out, uint64_t cap, uint64_t *size);
 
 /* Header fields of a container (parsed by the oracle's own reader).
  * offsets: codes, raw, escape positions, escape symbols, total bytes,
@@ -75,6 +86,9 @@ int orc_encode(int layout, const uint16_t *w, uint64_t n,
 int orc_header_info(const uint8_t *c, uint64_t size, int *layout, int *n_dict,
                     uint64_t *n, uint64_t *n_esc, uint16_t dict[16],
                     uint64_t offsets[6]);
+
+/* The flags byte of a valid container. */
+int orc_header_flags(const uint8_t *c, uint64_t size, int *flags);
 
 /* Decode a container into out[0..n). */
 int orc_decode(const uint8_t *c, uint64_t size, uint16_t *out, uint64_t n_cap);

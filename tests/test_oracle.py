@@ -445,6 +445,102 @@ def test_banded_escape_fraction():
 
 # ------------------------------------------- planted mistakes are caught
 
+# ---------------------------------------------- compact escape form (flags)
+#
+# The compact form drops the escape-position stream: the k-th weight whose
+# code is 15 takes the k-th escape symbol.  Its expected container follows
+# from a full one by the format's own definition (16-byte aligned streams,
+# header fields at fixed offsets), written out here without the oracle.
+
+
+def _le(b, off, size):
+    return int.from_bytes(b[off:off + size], "little")
+
+
+def compact_from_full(full: bytes) -> bytes:
+    """The compact container with the same content as `full`: the position
+    stream removed, the later streams moved up, the flag byte set."""
+    pad = lambda x: (x + 15) // 16 * 16  # noqa: E731
+    layout, n, n_esc = full[6], _le(full, 8, 8), _le(full, 16, 8)
+    off_pos, off_sym, off_idx = _le(full, 72, 8), _le(full, 80, 8), _le(full, 96, 8)
+    sym_len = n_esc * (2 if layout == oracle.K15 else 1)
+    idx_len = 4 * ((n + 2047) // 2048 + 1) if n_esc else 0
+    new_sym = off_pos
+    new_idx = pad(new_sym + sym_len)
+    total = pad(new_idx + idx_len)
+    out = bytearray(total)
+    out[:off_pos] = full[:off_pos]                  # header, codes, raw part
+    out[new_sym:new_sym + sym_len] = full[off_sym:off_sym + sym_len]
+    out[new_idx:new_idx + idx_len] = full[off_idx:off_idx + idx_len]
+    out[80:88] = new_sym.to_bytes(8, "little")
+    out[88:96] = total.to_bytes(8, "little")
+    out[96:104] = new_idx.to_bytes(8, "little")
+    out[104] = oracle.COMPACT
+    return bytes(out)
+
+
+CODED_GOLDEN = [c for c in GOLDEN if c["layout"] != oracle.RAW]
+
+
+@pytest.mark.parametrize("case", CODED_GOLDEN, ids=[c["name"] for c in CODED_GOLDEN])
+def test_compact_golden(case):
+    """Compact encode equals the hand-derived golden with its positions
+    removed; decoding it rebuilds the weights."""
+    want = compact_from_full(expected_container(case))
+    got = oracle.encode(case["layout"], weights_of(case), oracle.COMPACT)
+    assert got.tobytes() == want
+    assert oracle.header_info(got)["flags"] == oracle.COMPACT
+    assert np.array_equal(oracle.decode(got), weights_of(case))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_compact_roundtrip_and_structure(layout):
+    """Every bit pattern, and ragged random tensors across several index
+    tiles: exact round trip, and the compact container is the full one
+    without its positions."""
+    cases = [synth.all_patterns(5)] + [synth.random_bits(n, 40 + n % 7, kind)
+                                       for n, kind in ((1, "normal"), (2049, "uniform"),
+                                                       (6150, "normal"), (10007, "uniform"))]
+    for w in cases:
+        full = oracle.encode(layout, w)
+        comp = oracle.encode(layout, w, oracle.COMPACT)
+        assert comp.tobytes() == compact_from_full(full.tobytes())
+        assert np.array_equal(oracle.decode(comp), w)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_compact_accounting(layout):
+    """The compact payload is the full one less 32 bits per escape."""
+    w = synth.random_bits(20000, 77, "uniform")
+    full = oracle.encode(layout, w)
+    comp = oracle.encode(layout, w, oracle.COMPACT)
+    n_esc = oracle.header_info(full)["n_esc"]
+    assert n_esc > 0
+    _, pay_full = oracle.bits_per_weight(full)
+    _, pay_comp = oracle.bits_per_weight(comp)
+    assert pay_full - pay_comp == pytest.approx(32.0 * n_esc / w.size, rel=1e-12)
+    assert oracle.container_size(layout, w.size, n_esc, oracle.COMPACT) == comp.size
+
+
+def test_compact_rejects():
+    w = synth.random_bits(3000, 78, "uniform")
+    with pytest.raises(oracle.OracleError):
+        oracle.encode(oracle.RAW, w, oracle.COMPACT)
+    with pytest.raises(oracle.OracleError):
+        oracle.encode(oracle.K15, w, 2)
+    full = oracle.encode(oracle.K15, w)
+    bad = full.copy()
+    bad[104] = oracle.COMPACT  # the flag without moving the streams
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.decode(bad)
+    assert e.value.code == -3
+    comp = oracle.encode(oracle.K15, w, oracle.COMPACT)
+    bad = comp.copy()
+    bad[104] = 3
+    with pytest.raises(oracle.OracleError):
+        oracle.decode(bad)
+
+
 MUTATIONS = {
     "nibble_order": [(r"\(i % 2\) \* 4", "(1 - i % 2) * 4")],
     "tie_break": [(r"counts\[s\] > counts\[best\]", "counts[s] >= counts[best]")],
@@ -464,6 +560,7 @@ MUTATIONS = {
                        (r"out\[i\] = \(uint16_t\)get_le\(c \+ off\[1\] \+ 2u \* i, 2\);",
                         "{ uint16_t v = (uint16_t)get_le(c + off[1] + 2u * i, 2); out[i] = (uint16_t)((v >> 8) | (v << 8)); }")],
     "choice_tie": [(r"if \(best < 0 \|\| total < best_total\)", "if (best < 0 || total <= best_total)")],
+    "compact_keeps_positions": [(r"return \(flags & ORC_FLAG_COMPACT\) \? 0u : 4u \* e;", "return 4u * e;")],
     "index_inclusive": [(r"if \(n_esc && i % ORC_INDEX_TILE == 0\) put_le\(esc_idx \+ 4u \* \(i / ORC_INDEX_TILE\), e, 4\);\n    uint32_t s = symbol_of\(layout, w\[i\]\);",
                          "uint32_t s = symbol_of(layout, w[i]);\n    if (n_esc && i % ORC_INDEX_TILE == 0) put_le(esc_idx + 4u * (i / ORC_INDEX_TILE), e + (code_of[s] == 15), 4);"),
                         (r"get_le\(esc_idx \+ 4u \* \(i / ORC_INDEX_TILE\), 4\) != e\)",
@@ -495,6 +592,10 @@ def _pins_pass():
                 return False
         for _, w, want in _choice_cases():
             if oracle.choose_layout(w) != want:
+                return False
+        for case in CODED_GOLDEN:
+            got = oracle.encode(case["layout"], weights_of(case), oracle.COMPACT)
+            if got.tobytes() != compact_from_full(expected_container(case)):
                 return False
     except oracle.OracleError:
         return False
