@@ -22,7 +22,7 @@ import os
 import torch  # loaded first, so libwc binds to the HIP runtime torch already uses
 
 __all__ = [
-    "BYTESPLIT", "K15", "RAW", "AUTO", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into",
+    "BYTESPLIT", "K15", "RAW", "AUTO", "COMPACT", "FLAG_COMPACT", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into",
     "encode", "decode", "decode_gemv", "gemv_bf16", "bits_per_weight", "read_header",
     "crc32", "container_crcs", "artifact_write", "artifact_entries", "artifact_read",
     "artifact_verify", "LIB_PATH",
@@ -32,6 +32,8 @@ BYTESPLIT = 0
 K15 = 1
 RAW = 2   # fallback layout: the BF16 bit patterns as stored
 AUTO = 3  # build_dict / encode only: the smallest of the three
+COMPACT = 0x10  # OR into a layout: escape symbols only (header flag FLAG_COMPACT)
+FLAG_COMPACT = 1
 MAX_BATCH = 256
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwc.so")
 
@@ -53,7 +55,8 @@ class Header(ctypes.Structure):
         ("dict", ctypes.c_uint16 * 16), ("off_codes", ctypes.c_uint64),
         ("off_raw", ctypes.c_uint64), ("off_esc_pos", ctypes.c_uint64),
         ("off_esc_sym", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
-        ("off_esc_idx", ctypes.c_uint64), ("reserved", ctypes.c_uint8 * 24),
+        ("off_esc_idx", ctypes.c_uint64), ("flags", ctypes.c_uint8),
+        ("reserved", ctypes.c_uint8 * 23),
     ]
 
     def to_bytes(self) -> bytes:

@@ -24,7 +24,11 @@ bool layout_ok(int layout) {
 
 extern "C" int wc_build_dict(int layout, const uint16_t* d_w, uint64_t n, void* d_work,
                              size_t work_bytes, void* stream, wc_header* h_out) {
+  // WC_COMPACT asks for the compact escape form of a coded layout
+  const bool compact = (layout & WC_COMPACT) != 0;
+  layout &= ~WC_COMPACT;
   if (!h_out || !layout_ok(layout)) return WC_E_ARG;
+  const uint32_t cflags = compact ? WC_FLAG_COMPACT : 0u;
   if (n >= (1ull << 32)) return WC_E_SIZE;
   if (n && (!d_w || !wc::aligned16(d_w))) return WC_E_ARG;
   if (!d_work || !wc::aligned16(d_work)) return WC_E_ARG;
@@ -50,8 +54,8 @@ extern "C" int wc_build_dict(int layout, const uint16_t* d_w, uint64_t n, void* 
   }
   if (layout == WC_LAYOUT_AUTO) {
     // the smallest container, ties to the lower layout number
-    const uint64_t t0 = wc::geometry(WC_LAYOUT_BYTESPLIT, n, r[0].n_esc).total;
-    const uint64_t t1 = wc::geometry(WC_LAYOUT_K15, n, r[1].n_esc).total;
+    const uint64_t t0 = wc::geometry(WC_LAYOUT_BYTESPLIT, n, r[0].n_esc, cflags).total;
+    const uint64_t t1 = wc::geometry(WC_LAYOUT_K15, n, r[1].n_esc, cflags).total;
     const uint64_t t2 = wc::geometry(WC_LAYOUT_RAW, n, 0).total;
     layout = WC_LAYOUT_BYTESPLIT;
     uint64_t best = t0;
@@ -73,8 +77,9 @@ extern "C" int wc_build_dict(int layout, const uint16_t* d_w, uint64_t n, void* 
     h.n_dict = (uint8_t)rr.n_dict;
     h.n_esc = rr.n_esc;
     for (int k = 0; k < 16; ++k) h.dict[k] = k < (int)rr.n_dict ? rr.dict[k] : 0;
+    h.flags = (uint8_t)cflags;
   }
-  const wc::Geometry g = wc::geometry(layout, n, h.n_esc);
+  const wc::Geometry g = wc::geometry(layout, n, h.n_esc, h.flags);
   h.off_codes = g.off_codes;
   h.off_raw = g.off_raw;
   h.off_esc_pos = g.off_esc_pos;
@@ -114,6 +119,7 @@ extern "C" int wc_decode_gemv(const wc_header* h, const uint8_t* d_container,
   if (v != WC_OK) return v;
   if (container_bytes < h->total_bytes) return WC_E_SIZE;
   if (batch < 1 || batch > WC_MAX_BATCH) return WC_E_UNSUPPORTED;
+  if (h->flags & WC_FLAG_COMPACT) return WC_E_UNSUPPORTED;  // decode only, for now
   if (cols && rows > h->n / cols) return WC_E_ARG;
   if (rows * cols != h->n) return WC_E_ARG;
   if (rows && (!d_y || ((uintptr_t)d_y & 3u))) return WC_E_ARG;
@@ -136,8 +142,9 @@ extern "C" int wc_bits_per_weight(const wc_header* h, double* bpw, double* paylo
   const int v = wc::validate_header(h);
   if (v != WC_OK) return v;
   if (h->n == 0) return WC_E_ARG;
-  const uint64_t payload = wc::code_bytes(h->layout, h->n) + wc::raw_bytes(h->layout, h->n) + 4u * h->n_esc +
-                           wc::sym_bytes(h->layout) * h->n_esc + 4u * wc::index_entries(h->n, h->n_esc);
+  const uint64_t payload = wc::code_bytes(h->layout, h->n) + wc::raw_bytes(h->layout, h->n) +
+                           wc::pos_bytes(h->flags, h->n_esc) + wc::sym_bytes(h->layout) * h->n_esc +
+                           4u * wc::index_entries(h->n, h->n_esc);
   *bpw = 8.0 * (double)h->total_bytes / (double)h->n;
   *payload_bpw = 8.0 * (double)payload / (double)h->n;
   return WC_OK;

@@ -43,12 +43,18 @@ struct Geometry {
   uint64_t off_codes, off_raw, off_esc_pos, off_esc_sym, off_esc_idx, total;
 };
 
-__host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_esc) {
+// Bytes of the escape-position stream: none in the compact form.
+__host__ __device__ inline uint64_t pos_bytes(uint32_t flags, uint64_t n_esc) {
+  return (flags & WC_FLAG_COMPACT) ? 0u : 4u * n_esc;
+}
+
+__host__ __device__ inline Geometry geometry(int layout, uint64_t n, uint64_t n_esc,
+                                             uint32_t flags = 0) {
   Geometry g;
   g.off_codes = WC_HEADER_BYTES;
   g.off_raw = pad16(g.off_codes + code_bytes(layout, n));
   g.off_esc_pos = pad16(g.off_raw + raw_bytes(layout, n));
-  g.off_esc_sym = pad16(g.off_esc_pos + 4u * n_esc);
+  g.off_esc_sym = pad16(g.off_esc_pos + pos_bytes(flags, n_esc));
   g.off_esc_idx = pad16(g.off_esc_sym + sym_bytes(layout) * n_esc);
   g.total = pad16(g.off_esc_idx + 4u * index_entries(n, n_esc));
   return g;
@@ -197,6 +203,8 @@ inline int validate_header(const wc_header* h) {
     return WC_E_CORRUPT;
   if (h->n_dict > 15) return WC_E_CORRUPT;
   if (h->layout == WC_LAYOUT_RAW && (h->n_dict != 0 || h->n_esc != 0)) return WC_E_CORRUPT;
+  if (h->flags != 0 && (h->flags != WC_FLAG_COMPACT || h->layout == WC_LAYOUT_RAW))
+    return WC_E_CORRUPT;
   if (h->n >= (1ull << 32) || h->n_esc > h->n) return WC_E_CORRUPT;
   const uint32_t nsym = h->layout == WC_LAYOUT_K15 ? 512u : 256u;
   for (int k = 0; k < 16; ++k) {
@@ -208,11 +216,11 @@ inline int validate_header(const wc_header* h) {
     for (int j = 0; j < k; ++j)
       if (h->dict[j] == h->dict[k]) return WC_E_CORRUPT;
   }
-  const Geometry g = geometry(h->layout, h->n, h->n_esc);
+  const Geometry g = geometry(h->layout, h->n, h->n_esc, h->flags);
   if (h->off_codes != g.off_codes || h->off_raw != g.off_raw || h->off_esc_pos != g.off_esc_pos ||
       h->off_esc_sym != g.off_esc_sym || h->off_esc_idx != g.off_esc_idx || h->total_bytes != g.total)
     return WC_E_CORRUPT;
-  for (int k = 0; k < 24; ++k)
+  for (int k = 0; k < 23; ++k)
     if (h->reserved[k] != 0) return WC_E_CORRUPT;
   return WC_OK;
 }

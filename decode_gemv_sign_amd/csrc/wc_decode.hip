@@ -34,6 +34,10 @@ struct DecodeArgs {
   uint16_t* out;
   uint64_t n, n_esc, esc_last, raw_last, n_tiles, tiles_per_wave;
   uint64_t sym_last;  // last dword of the symbol stream's padded extent
+  // Records the sparse path may prefetch by position (n_esc, or 0 in the
+  // compact form, whose tiles all take symbols by rank from their run).
+  uint64_t rec_n;
+  uint32_t dense_min;  // tiles with more escapes take the run path
   Dict dict;
 };
 
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
-    const bool dense = cnt_wave > kDenseMin;
+    const bool dense = cnt_wave > a.dense_min;
     issue_next(e + cnt_wave);
     const uint32_t off0 = dense ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg) : 0u;
     rebuild_lane<LAYOUT>(T2, l, out);
@@ -105,10 +109,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     };
     auto read_tile = [&](const uint32_t* buf, Lane4& l) { ring_read_tile<LAYOUT>(buf, l); };
     auto dma_eb = [&](uint64_t e0, uint32_t* buf) {
-      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e0, buf);
+      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e0, buf);
     };
     auto read_eb = [&](const uint32_t* buf, uint64_t e0) {
-      return ring_read_esc<LAYOUT>(buf, e0, a.n_esc, a.esc_last);
+      return ring_read_esc<LAYOUT>(buf, e0, a.rec_n, a.esc_last);
     };
     uint32_t* const s0 = ring0[wib];
     uint32_t* const s1 = ring1[wib];
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
       }
     }
     uint32_t out[16];
-    const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+    const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e);
     // no global->LDS load is in flight here: ring0 is free
     rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib]);
 #pragma unroll
@@ -285,6 +289,16 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
     a.esc_pos = (const uint32_t*)container;
     a.esc_sym = container;
     a.esc_idx = (const uint32_t*)container;
+  }
+  a.rec_n = h.n_esc;
+  a.dense_min = kDenseMin;
+  if (h.flags & WC_FLAG_COMPACT) {
+    // no positions: every tile with escapes places its symbols by rank from
+    // its run, and the (never used) position prefetch reads the header
+    a.rec_n = 0;
+    a.esc_last = 0;
+    a.esc_pos = (const uint32_t*)container;
+    a.dense_min = 0;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;

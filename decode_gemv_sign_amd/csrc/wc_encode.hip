@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
   if (blockIdx.x == 0) {
     if (tid < 32) ((uint32_t*)a.container)[tid] = ((const uint32_t*)&a.h)[tid];
     if (tid == 32) {
-      const uint64_t pe = h.off_esc_pos + 4u * h.n_esc;
+      const uint64_t pe = h.off_esc_pos + pos_bytes(h.flags, h.n_esc);
       for (uint64_t o = pe; o < h.off_esc_sym; ++o) a.container[o] = 0;
       const uint64_t se = h.off_esc_sym + sym_bytes(LAYOUT) * h.n_esc;
       for (uint64_t o = se; o < h.off_esc_idx; ++o) a.container[o] = 0;
@@ -390,13 +390,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
   if (lane_id() == 0 && my_tile < n_tiles) index[my_tile] = (uint32_t)o;  // ex == 0 in lane 0
   uint32_t* pos = (uint32_t*)(a.container + a.h.off_esc_pos);
   uint8_t* sym = a.container + a.h.off_esc_sym;
+  const bool compact = (a.h.flags & WC_FLAG_COMPACT) != 0;
   while (mask) {
     const int i = __builtin_ctz(mask);
     mask &= mask - 1u;
     if (o < a.h.n_esc) {
       const uint64_t p = base + (uint64_t)i;
       const uint32_t s = (uint32_t)a.w[p] >> (LAYOUT == WC_LAYOUT_K15 ? 7 : 8);
-      pos[o] = (uint32_t)p;
+      if (!compact) pos[o] = (uint32_t)p;  // the compact form keeps symbols only
       if (LAYOUT == WC_LAYOUT_K15)
         ((uint16_t*)sym)[o] = (uint16_t)s;
       else

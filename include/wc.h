@@ -89,6 +89,13 @@ extern "C" {
 #define WC_INDEX_TILE 2048u /* weights per escape-index entry */
 #define WC_MAX_BATCH 256u
 
+/* Header flags.  WC_FLAG_COMPACT: the escape stream holds the symbols only,
+ * in weight order, and the k-th weight whose code is 15 takes the k-th
+ * symbol (no position stream: off_esc_sym == off_esc_pos).  Coded layouts
+ * only.  Request it by OR-ing WC_COMPACT into wc_build_dict's layout. */
+#define WC_FLAG_COMPACT 1u
+#define WC_COMPACT 0x10
+
 /* Scratch bytes wc_build_dict and wc_encode need for n weights. */
 #define WC_WORKSPACE_BYTES(n) ((size_t)20480 + (size_t)8 * (((uint64_t)(n) + 8191u) / 8192u))
 
@@ -107,7 +114,8 @@ typedef struct wc_header {
   uint64_t off_esc_sym; /* = pad16(off_esc_pos + 4 n_esc) */
   uint64_t total_bytes; /* = pad16(off_esc_idx + 4 (T + 1)), or off_esc_idx when n_esc == 0 */
   uint64_t off_esc_idx; /* = pad16(off_esc_sym + symbol bytes) */
-  uint8_t reserved[24]; /* zero */
+  uint8_t flags;        /* WC_FLAG_* */
+  uint8_t reserved[23]; /* zero */
 } wc_header;
 
 /*

@@ -132,7 +132,8 @@ def test_header_struct_layout(wc):
     offs = {f[0]: getattr(wc.Header, f[0]).offset for f in wc.Header._fields_}
     assert offs == {"magic": 0, "version": 4, "layout": 6, "n_dict": 7, "n": 8, "n_esc": 16,
                     "dict": 24, "off_codes": 56, "off_raw": 64, "off_esc_pos": 72,
-                    "off_esc_sym": 80, "total_bytes": 88, "off_esc_idx": 96, "reserved": 104}
+                    "off_esc_sym": 80, "total_bytes": 88, "off_esc_idx": 96, "flags": 104,
+                    "reserved": 105}
     # and a container header written by the oracle parses field by field
     w = np.array([0x3F80, 0xBF80, 0x3F80, 0x4000, 0x3F81], dtype=np.uint16)
     h, _ = _header_from_oracle(0, w)
