@@ -28,7 +28,9 @@
  *   off_raw          byte-split: the low byte of every weight, n bytes;
  *                    K15: the 7-bit mantissas as one LSB-first bitstream,
  *                    mantissa i at stream bits [7i, 7i+7), ceil(7n/8) bytes
- *   off_esc_pos      n_esc u32 positions (flat weight index), ascending
+ *   off_esc_pos      n_esc u32 positions (flat weight index), ascending;
+ *                    empty in the compact form (flags & WC_FLAG_COMPACT),
+ *                    where the k-th code-15 weight is the k-th record
  *   off_esc_sym      n_esc symbols: u8 (byte-split) or u16 (K15)
  *   off_esc_idx      escape index, only when n_esc > 0: for j = 0..T with
  *                    T = ceil(n / WC_INDEX_TILE), u32 entry j = the number of
@@ -130,7 +132,8 @@ typedef struct wc_header {
  * no device work and does not wait.  The pages ask for a BF16 fallback
  * where the coding does not pay (page "Compresión de pesos LLM sin pérdida
  * vs 8-bit GGUF…", section "Preguntas para un vendor o equipo de
- * investigación").
+ * investigación").  layout | WC_COMPACT gives a coded layout the compact
+ * escape form (WC_FLAG_COMPACT; the raw layout ignores it).
  * d_work: WC_WORKSPACE_BYTES(n) bytes of device scratch (contents ignored
  * and overwritten).  Waits for `stream`.  n == 0 is allowed (empty tensor).
  */
@@ -157,7 +160,8 @@ int wc_encode(const wc_header *h, const uint16_t *d_w, uint8_t *d_container,
  * index entries are clamped to [0, n_esc], and escape records whose position
  * lies outside the tile being decoded, or past n_esc, are ignored, so a
  * corrupt stream body cannot make the kernel read or write outside the
- * container and d_out.
+ * container and d_out.  In the compact form (WC_FLAG_COMPACT) the k-th
+ * code-15 weight takes the k-th symbol, placed by its rank in the tile.
  */
 int wc_decode(const wc_header *h, const uint8_t *d_container,
               size_t container_bytes, uint16_t *d_out, void *stream);
@@ -174,7 +178,8 @@ int wc_decode(const wc_header *h, const uint8_t *d_container,
  * encaja con los sistemas anteriores?"], each rebuilt weight is used by up
  * to 128 input rows on the matrix cores: above 32 input rows (above 16 on
  * tensors of 2^26 weights or more) when cols is a multiple of 128.  Other
- * batches above 16 run 16 input rows at a time.
+ * batches above 16 run 16 input rows at a time.  A container in the compact
+ * escape form (WC_FLAG_COMPACT) gives WC_E_UNSUPPORTED.
  */
 int wc_decode_gemv(const wc_header *h, const uint8_t *d_container,
                    size_t container_bytes, uint64_t rows, uint64_t cols,
