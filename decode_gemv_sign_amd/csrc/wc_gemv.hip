@@ -466,6 +466,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16(GemvArgs a) {
 }
 
 // ---- generic shapes (cols % 8 != 0): one weight per lane per step ---------
+// The launchers hand these kernels at most 16 input rows at a time.
+constexpr int kGenericBatch = 16;
 
 __device__ inline float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -481,9 +483,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_generic(GemvArgs 
   const uint64_t n = a.rows * a.cols;
   const uint64_t raw_len = raw_bytes(LAYOUT, n);
   uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, n, row_start);
-  float acc[WC_MAX_BATCH];
+  float acc[kGenericBatch];
 #pragma unroll
-  for (int b = 0; b < (int)WC_MAX_BATCH; ++b) acc[b] = 0.0f;
+  for (int b = 0; b < kGenericBatch; ++b) acc[b] = 0.0f;
   const uint64_t below = (1ull << lane) - 1ull;
   for (uint64_t c0 = 0; c0 < a.cols; c0 += kWave) {
     const uint64_t c = c0 + (uint64_t)lane;
@@ -514,13 +516,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_generic(GemvArgs 
     const float wf = bf16f((s << (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)) | rawv);
     if (valid) {
 #pragma unroll
-      for (int b = 0; b < (int)WC_MAX_BATCH; ++b)
+      for (int b = 0; b < kGenericBatch; ++b)
         if (b < (int)a.batch) acc[b] = fmaf(wf, bf16f(a.x[(uint64_t)b * a.cols + c]), acc[b]);
     }
     e += (uint64_t)__popcll(m);
   }
 #pragma unroll
-  for (int b = 0; b < (int)WC_MAX_BATCH; ++b) {
+  for (int b = 0; b < kGenericBatch; ++b) {
     if (b < (int)a.batch) {
       const float s = wave_sum_f32(acc[b]);
       if (lane == 0) a.y[(uint64_t)b * a.rows + r] = s;
@@ -532,17 +534,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemv_bf16_generic(GemvArgs a)
   const int lane = lane_id();
   const uint64_t r = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wave_in_block();
   if (r >= a.rows) return;
-  float acc[WC_MAX_BATCH];
+  float acc[kGenericBatch];
 #pragma unroll
-  for (int b = 0; b < (int)WC_MAX_BATCH; ++b) acc[b] = 0.0f;
+  for (int b = 0; b < kGenericBatch; ++b) acc[b] = 0.0f;
   for (uint64_t c = (uint64_t)lane; c < a.cols; c += kWave) {
     const float wf = bf16f(a.w[r * a.cols + c]);
 #pragma unroll
-    for (int b = 0; b < (int)WC_MAX_BATCH; ++b)
+    for (int b = 0; b < kGenericBatch; ++b)
       if (b < (int)a.batch) acc[b] = fmaf(wf, bf16f(a.x[(uint64_t)b * a.cols + c]), acc[b]);
   }
 #pragma unroll
-  for (int b = 0; b < (int)WC_MAX_BATCH; ++b) {
+  for (int b = 0; b < kGenericBatch; ++b) {
     if (b < (int)a.batch) {
       const float s = wave_sum_f32(acc[b]);
       if (lane == 0) a.y[(uint64_t)b * a.rows + r] = s;
