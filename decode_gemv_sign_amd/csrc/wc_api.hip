@@ -119,7 +119,6 @@ extern "C" int wc_decode_gemv(const wc_header* h, const uint8_t* d_container,
   if (v != WC_OK) return v;
   if (container_bytes < h->total_bytes) return WC_E_SIZE;
   if (batch < 1 || batch > WC_MAX_BATCH) return WC_E_UNSUPPORTED;
-  if (h->flags & WC_FLAG_COMPACT) return WC_E_UNSUPPORTED;  // decode only, for now
   if (cols && rows > h->n / cols) return WC_E_ARG;
   if (rows * cols != h->n) return WC_E_ARG;
   if (rows && (!d_y || ((uintptr_t)d_y & 3u))) return WC_E_ARG;

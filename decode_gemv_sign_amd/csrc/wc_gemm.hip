@@ -65,6 +65,7 @@ struct GemmArgs {
   uint32_t batch, chunks;                // chunks: 128-column chunks per row
   uint32_t groups, row_blocks;           // wide batches: batch groups x column splits, row blocks
   uint32_t splits, split_chunks;         // wide batches: column splits, chunks per split
+  uint32_t compact;                      // escape symbols only (no position stream)
   Dict dict;
 };
 
@@ -429,7 +430,8 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
     if (esc) {
       for (int rr = s; rr < kMRows; rr += S) {
         const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols : a.rows * a.cols;
-        const uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, t);
+        const uint64_t e = escape_cursor_at(a.compact, a.esc_idx, a.esc_pos, a.codes, a.n_esc,
+                                            a.rows * a.cols, t);
         if (lane == 0) erow0[rr] = e;
       }
     }
@@ -653,7 +655,8 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
     } else {
       for (int rr = 0; rr < kMRows; ++rr) {
         const uint64_t t = r0 + rr < a.rows ? (r0 + rr) * a.cols + col0 : a.rows * a.cols;
-        const uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, t);
+        const uint64_t e = escape_cursor_at(a.compact, a.esc_idx, a.esc_pos, a.codes, a.n_esc,
+                                            a.rows * a.cols, t);
         if (r == rr) e_next = e;
       }
     }
@@ -960,6 +963,7 @@ hipError_t launch_decode_gemm_mfma(const wc_header& h, const uint8_t* container,
   // last dword of the symbol stream's 16-byte padded extent (unused without escapes)
   a.sym_last = h.n_esc ? (h.off_esc_idx - h.off_esc_sym) / 4 - 1 : 0;
   a.dict = dict_of(&h);
+  a.compact = (h.flags & WC_FLAG_COMPACT) ? 1u : 0u;
   if (batch > kMRows) {
     if (h.layout == WC_LAYOUT_K15)
       launch_wide<WC_LAYOUT_K15, false>(a, s);

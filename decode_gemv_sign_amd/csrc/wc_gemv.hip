@@ -46,6 +46,11 @@ struct GemvArgs {
   float* y;
   uint64_t rows, cols, n_esc, esc_last, raw_last, rows_per_wave;
   uint64_t sym_last;  // last dword of the symbol stream's padded extent
+  // Records the sparse paths may prefetch by position (n_esc, or 0 in the
+  // compact form, whose tiles all take their symbols by rank).
+  uint64_t rec_n;
+  uint32_t dense_min;  // tiles with more escapes take the rank path
+  uint32_t compact;    // escape symbols only (no position stream)
   uint32_t batch;
   Dict dict;
 };
@@ -217,10 +222,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     const bool any = escape_marks(s.l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     // the next tile's first records, in flight while this tile is rebuilt
-    sn.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e + cnt_wave);
+    sn.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e + cnt_wave);
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, s.l, w);
-    if (cnt_wave > kDenseMin) {
+    if (cnt_wave > a.dense_min) {
       patch_tile_windows<LAYOUT>(s.l, w, a.esc_sym, a.sym_last, e);
     } else if (cnt_wave) {
       const uint64_t tile_start = c.r * a.cols + c.ct * kTile;
@@ -256,8 +261,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   };
 
   auto init = [&](Slot& s0) {
-    e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, a.rows * a.cols, r0 * a.cols);
-    s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e);
+    e = escape_cursor_at(a.compact, a.esc_idx, a.esc_pos, a.codes, a.n_esc, a.rows * a.cols,
+                         r0 * a.cols);
+    s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e);
   };
   run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, init, load_tile, process);
 }
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
   load_next(s0, x0);  // in flight while the escape index is read
   load_iv();
-  ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, cursor(0), s0);
+  ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, cursor(0), s0);
   TileCursor pc{r0, 0};
 
   auto step = [&](uint64_t q, uint32_t* buf, uint32_t* nbuf, uint32_t xv[16], uint32_t xn[16]) {
@@ -344,14 +350,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     // tiles' loads were issued before the previous tile's full wait.
     if (q + 1 < nq) {
       load_next(nbuf, xn);
-      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, cursor(q + 1), nbuf);
+      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, cursor(q + 1), nbuf);
       if (q == 0) wait_vm<kRingAheadEsc>();
     } else if (q == 0) {
       wait_vm<0>();
     }
     Lane4 l;
     ring_read_tile<LAYOUT>(buf, l);
-    const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, a.n_esc, a.esc_last);
+    const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, a.rec_n, a.esc_last);
     uint32_t xb1[kXpf ? 1 : 16];
     if (!kXpf && B == 1) load_x_lane(a.x + pc.ct * kTile, lg, xb1);
     uint32_t marks[kLaneGroups];
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     // a dense tile's symbol run goes into its own slot (free: the tile is in
     // registers)
-    const bool dense = cnt_wave > kDenseMin;
+    const bool dense = cnt_wave > a.dense_min;
     const uint32_t off0 = dense ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, l, w);
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_generic(GemvArgs 
   const uint64_t row_start = r * a.cols;
   const uint64_t n = a.rows * a.cols;
   const uint64_t raw_len = raw_bytes(LAYOUT, n);
-  uint64_t e = escape_cursor(a.esc_idx, a.esc_pos, a.n_esc, n, row_start);
+  uint64_t e = escape_cursor_at(a.compact, a.esc_idx, a.esc_pos, a.codes, a.n_esc, n, row_start);
   float acc[kGenericBatch];
 #pragma unroll
   for (int b = 0; b < kGenericBatch; ++b) acc[b] = 0.0f;
@@ -681,6 +687,17 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
     a.esc_idx = (const uint32_t*)container;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
+  a.rec_n = h.n_esc;
+  a.dense_min = kDenseMin;
+  if (h.flags & WC_FLAG_COMPACT) {
+    // no positions: every tile with escapes places its symbols by rank, and
+    // the (never used) position prefetch reads the header
+    a.compact = 1;
+    a.rec_n = 0;
+    a.esc_last = 0;
+    a.esc_pos = (const uint32_t*)container;
+    a.dense_min = 0;
+  }
   a.batch = batch;
   a.dict = dict_of(&h);
   if (cols % kGroup == 0) {

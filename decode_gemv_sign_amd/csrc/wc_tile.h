@@ -149,6 +149,43 @@ __device__ inline bool escape_marks(const Lane4& l, uint32_t esc[kLaneGroups]) {
   return any != 0;
 }
 
+// The first escape record at or after weight t (count if none), in either
+// escape form: a search of the positions (escape_cursor), or, in the
+// compact form, which has no positions, the index entry of t's tile plus the
+// code-15 marks between the tile start and t, counted by the wave (lane l
+// takes weights 32 l .. 32 l + 31 of the tile).  Wave-uniform.
+__device__ inline uint64_t escape_cursor_at(bool compact, const uint32_t* __restrict__ idx,
+                                            const uint32_t* __restrict__ pos,
+                                            const uint8_t* __restrict__ codes, uint64_t count,
+                                            uint64_t n, uint64_t t) {
+  if (!compact) return escape_cursor(idx, pos, count, n, t);
+  if (count == 0 || t >= n) return count;
+  const uint64_t j = t / WC_INDEX_TILE;
+  uint64_t lo = idx[j];
+  lo = lo < count ? lo : count;
+  const uint32_t rem = (uint32_t)(t % WC_INDEX_TILE);
+  if (rem == 0) return lo;
+  const uint32_t lw = 32u * (uint32_t)lane_id();
+  uint32_t c = 0;
+  if (lw < rem) {
+    // 16 aligned bytes of codes: the lane's 32 weights, all before n
+    const u32x4 v = *(const u32x4*)(codes + (j * WC_INDEX_TILE + lw) / 2);
+    const uint32_t k = rem - lw;  // the lane's weights below t
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t m = nibble15(v[d]);  // bit 4i + 3: weight 8d + i escapes
+      const uint32_t w0 = 8u * (uint32_t)d;
+      if (w0 >= k)
+        m = 0;
+      else if (w0 + 8u > k)
+        m &= (1u << (4u * (k - w0))) - 1u;
+      c += (uint32_t)__popc(m);
+    }
+  }
+  lo += wave_sum_u32(c);
+  return lo < count ? lo : count;
+}
+
 // Escape count of the lane.
 __device__ inline uint32_t count_marks(const uint32_t esc[kLaneGroups]) {
   uint32_t n = 0;
