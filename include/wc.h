@@ -178,8 +178,10 @@ int wc_decode(const wc_header *h, const uint8_t *d_container,
  * encaja con los sistemas anteriores?"], each rebuilt weight is used by up
  * to 128 input rows on the matrix cores: above 32 input rows (above 16 on
  * tensors of 2^26 weights or more) when cols is a multiple of 128.  Other
- * batches above 16 run 16 input rows at a time.  A container in the compact
- * escape form (WC_FLAG_COMPACT) gives WC_E_UNSUPPORTED.
+ * batches above 16 run 16 input rows at a time.  Both escape forms are
+ * taken; in the compact one (WC_FLAG_COMPACT) a row that starts inside an
+ * index tile finds its first record by counting the code-15 marks from the
+ * tile start.
  */
 int wc_decode_gemv(const wc_header *h, const uint8_t *d_container,
                    size_t container_bytes, uint64_t rows, uint64_t cols,
