@@ -484,6 +484,11 @@ def main():
         bpw[tag] = {"bpw": round(b, 4), "payload_bpw": round(p, 4),
                     "saving": round(1 - b / 16, 5), "n_esc": int(h.n_esc),
                     "escape_frac": round(h.n_esc / n, 6)}
+        # the same tensor in the compact escape form (symbols only): header only
+        hc = wc.build_dict(Wd[0][mi], layouts[li] | wc.COMPACT, work[0])
+        bc, pc = wc.bits_per_weight(hc)
+        bpw[tag]["compact_bpw"] = round(bc, 4)
+        bpw[tag]["compact_payload_bpw"] = round(pc, 4)
         t_dec = avg_us("decode", (li, mi))
         t_burst = burst[(li, mi)]
         dec_bytes = h.total_bytes + 2 * n

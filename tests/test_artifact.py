@@ -40,6 +40,8 @@ def _containers():
     d = synth.small()
     out.append(("small.bytesplit", d["W"].shape, d["W"], oracle.encode(oracle.BYTESPLIT, d["W"])))
     out.append(("small.k15", d["W"].shape, d["W"], oracle.encode(oracle.K15, d["W"])))
+    out.append(("small.k15.compact", d["W"].shape, d["W"],
+                oracle.encode(oracle.K15, d["W"], oracle.COMPACT)))
     u = synth.random_bits(3 * 4097, 11, "uniform").reshape(3, 4097)
     out.append(("uniform.raw", u.shape, u, oracle.encode(oracle.RAW, u)))
     e = np.full((2, 2, 2, 5), 0x3F80, dtype=np.uint16)  # no escapes, 4-d
