@@ -38,6 +38,7 @@ struct DecodeArgs {
   // compact form, whose tiles all take symbols by rank from their run).
   uint64_t rec_n;
   uint32_t dense_min;  // tiles with more escapes take the run path
+  uint32_t compact;    // escape symbols only: runs prefetched with the tiles
   Dict dict;
 };
 
@@ -80,15 +81,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   // `issue_next(e_next)` issues the next tile's record loads; then a dense
   // tile's symbol run comes into `stg`, the last global->LDS loads issued.
   auto rebuild = [&](uint64_t t, const Lane4& l, const EscBatch& eb, auto&& issue_next,
-                     uint32_t out[16], uint32_t* stg) {
+                     uint32_t out[16], uint32_t* stg, bool ahead_ok) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     const bool dense = cnt_wave > a.dense_min;
+    // compact form: a run that came with the tile serves it when it fits
+    const bool ahead = ahead_ok && cnt_wave <= AheadSyms<LAYOUT>::value;
     issue_next(e + cnt_wave);
-    const uint32_t off0 = dense ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg) : 0u;
+    const uint32_t off0 =
+        dense && !ahead ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg) : 0u;
     rebuild_lane<LAYOUT>(T2, l, out);
-    if (dense) {
+    if (dense && ahead) {
+      patch_tile_symrun<LAYOUT>(l, out, stg + 768,
+                                (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u));
+    } else if (dense) {
       wait_vm<0>();  // the symbol run is complete
       patch_tile_symrun<LAYOUT>(l, out, stg, off0);
     } else if (cnt_wave) {
@@ -109,7 +116,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     };
     auto read_tile = [&](const uint32_t* buf, Lane4& l) { ring_read_tile<LAYOUT>(buf, l); };
     auto dma_eb = [&](uint64_t e0, uint32_t* buf) {
-      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e0, buf);
+      if (a.compact)
+        ring_load_symrun_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, buf);
+      else
+        ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e0, buf);
     };
     auto read_eb = [&](const uint32_t* buf, uint64_t e0) {
       return ring_read_esc<LAYOUT>(buf, e0, a.rec_n, a.esc_last);
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         read_tile(buf, l);
         const EscBatch eb = read_eb(buf, e);
         uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
-        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf);
+        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf, a.compact != 0);
         ++t;
       };
       while (t + 2 <= f1) {
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     uint32_t out[16];
     const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e);
     // no global->LDS load is in flight here: ring0 is free
-    rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib]);
+    rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib], false);
 #pragma unroll
     for (int k = 0; k < kLaneGroups; ++k) {
       const uint64_t w0 = tile_start + (uint64_t)(lane + kWave * k) * kGroup;
@@ -299,6 +309,7 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
     a.esc_last = 0;
     a.esc_pos = (const uint32_t*)container;
     a.dense_min = 0;
+    a.compact = 1;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;

@@ -338,7 +338,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
   load_next(s0, x0);  // in flight while the escape index is read
   load_iv();
-  ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, cursor(0), s0);
+  // a tile's first records go out with its ring loads; in the compact form,
+  // the start of its symbol run instead (the same number of loads)
+  auto load_records = [&](uint64_t e0, uint32_t* buf) {
+    if (a.compact)
+      ring_load_symrun_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, buf);
+    else
+      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e0, buf);
+  };
+  load_records(cursor(0), s0);
   TileCursor pc{r0, 0};
 
   auto step = [&](uint64_t q, uint32_t* buf, uint32_t* nbuf, uint32_t xv[16], uint32_t xn[16]) {
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     // tiles' loads were issued before the previous tile's full wait.
     if (q + 1 < nq) {
       load_next(nbuf, xn);
-      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, cursor(q + 1), nbuf);
+      load_records(cursor(q + 1), nbuf);
       if (q == 0) wait_vm<kRingAheadEsc>();
     } else if (q == 0) {
       wait_vm<0>();
@@ -366,10 +374,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     // a dense tile's symbol run goes into its own slot (free: the tile is in
     // registers)
     const bool dense = cnt_wave > a.dense_min;
-    const uint32_t off0 = dense ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
+    const bool ahead = a.compact && cnt_wave <= AheadSyms<LAYOUT>::value;
+    const uint32_t off0 =
+        dense && !ahead ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, l, w);
-    if (dense) {
+    if (dense && ahead) {
+      patch_tile_symrun<LAYOUT>(l, w, buf + 768,
+                                (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u));
+    } else if (dense) {
       wait_vm<0>();
       patch_tile_symrun<LAYOUT>(l, w, buf, off0);
     } else if (cnt_wave) {

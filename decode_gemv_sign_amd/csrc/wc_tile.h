@@ -636,6 +636,37 @@ __device__ inline uint32_t ring_load_symrun(const uint8_t* esc_sym, uint64_t sym
   return (uint32_t)(b0 - base);
 }
 
+// Compact form (no positions): instead of a tile's first records, the first
+// 512 bytes of its symbol run, from the 16-byte chunk that holds record e0,
+// go into buf[768 .. 896) with the tile's ring loads: two global->LDS loads,
+// as many as ring_load_esc issues, so the ring's waits stay the same.  A
+// tile whose symbols fit (kAheadSyms) is patched from there without a load
+// of its own.  Without escapes the loads read the stream's first chunk.
+constexpr uint32_t kAheadRunBytes = 512;
+template <int LAYOUT>
+__device__ inline void ring_load_symrun_ahead(const uint8_t* esc_sym, uint64_t sym_last, uint64_t n_esc,
+                                              uint64_t e0, uint32_t* buf) {
+  constexpr uint64_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  const uint32_t lane = (uint32_t)lane_id();
+  uint64_t c0 = 0, c1 = 0;
+  if (n_esc) {
+    const uint64_t last_chunk = (4 * (sym_last + 1) - 16) >> 4;  // the padded extent is 16-byte whole
+    const uint64_t base = (e0 * kSymBytes) >> 4;
+    c0 = base + lane;
+    c1 = base + 16 + lane;
+    c0 = c0 < last_chunk ? c0 : last_chunk;
+    c1 = c1 < last_chunk ? c1 : last_chunk;
+  }
+  if (lane < 16) {
+    lds_dma16(esc_sym + 16 * c0, buf + 768);
+    lds_dma16(esc_sym + 16 * c1, buf + 832);
+  }
+}
+template <int LAYOUT>
+struct AheadSyms {  // records a prefetched run holds whatever its alignment
+  static constexpr uint32_t value = (kAheadRunBytes - 16) / (LAYOUT == WC_LAYOUT_K15 ? 2 : 1);
+};
+
 // Patch a dense tile from its symbol run in LDS (ring_load_symrun, run byte
 // offset off0): each group reads the window that starts at its first record
 // and writes the symbols into its code-15 weights.
