@@ -46,10 +46,6 @@ struct GemvArgs {
   float* y;
   uint64_t rows, cols, n_esc, esc_last, raw_last, rows_per_wave;
   uint64_t sym_last;  // last dword of the symbol stream's padded extent
-  // Records the sparse paths may prefetch by position (n_esc, or 0 in the
-  // compact form, whose tiles all take their symbols by rank).
-  uint64_t rec_n;
-  uint32_t dense_min;  // tiles with more escapes take the rank path
   uint32_t compact;    // escape symbols only (no position stream)
   uint32_t batch;
   Dict dict;
@@ -172,7 +168,9 @@ __device__ inline RowTile row_tile(uint64_t ct, uint64_t gpr) {
 // batch 1) are in flight while tile q is rebuilt, patched and multiplied, two
 // register sets alternating (the loop is unrolled by two), and the escape
 // cursor found for the run's first row is carried to its end.
-template <int LAYOUT, int B>
+// CMP: the compact escape form (symbols only), a template argument so that
+// the full form's kernels carry none of its branches.
+template <int LAYOUT, int B, bool CMP>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   __shared__ uint32_t T2[256];
   __shared__ __attribute__((aligned(16))) uint32_t stage[kBlockThreads / kWave][kStageDwords];
@@ -222,10 +220,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
     const bool any = escape_marks(s.l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     // the next tile's first records, in flight while this tile is rebuilt
-    sn.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e + cnt_wave);
+    sn.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, (CMP ? 0ull : a.n_esc), a.esc_last, e + cnt_wave);
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, s.l, w);
-    if (cnt_wave > a.dense_min) {
+    if (cnt_wave > (CMP ? 0u : kDenseMin)) {
       patch_tile_windows<LAYOUT>(s.l, w, a.esc_sym, a.sym_last, e);
     } else if (cnt_wave) {
       const uint64_t tile_start = c.r * a.cols + c.ct * kTile;
@@ -261,9 +259,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
   };
 
   auto init = [&](Slot& s0) {
-    e = escape_cursor_at(a.compact, a.esc_idx, a.esc_pos, a.codes, a.n_esc, a.rows * a.cols,
+    e = escape_cursor_at(CMP, a.esc_idx, a.esc_pos, a.codes, a.n_esc, a.rows * a.cols,
                          r0 * a.cols);
-    s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e);
+    s0.eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, (CMP ? 0ull : a.n_esc), a.esc_last, e);
   };
   run_ring<kGemvDepth, Slot>((r1 - r0) * tpr, TileCursor{r0, 0}, tpr, init, load_tile, process);
 }
@@ -274,7 +272,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
 // of the register ring.  At batch 1, x for the next tile rides in
 // registers; larger batches read x when the tile is used.  Each step issues
 // the next tile's loads first and waits for them before its dot product.
-template <int LAYOUT, int B>
+template <int LAYOUT, int B, bool CMP>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) {
   __shared__ uint32_t T2[256];
   __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][kRingSlotDwords];
@@ -341,10 +339,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   // a tile's first records go out with its ring loads; in the compact form,
   // the start of its symbol run instead (the same number of loads)
   auto load_records = [&](uint64_t e0, uint32_t* buf) {
-    if (a.compact)
+    if constexpr (CMP)
       ring_load_symrun_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, buf);
     else
-      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e0, buf);
+      ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, (CMP ? 0ull : a.n_esc), a.esc_last, e0, buf);
   };
   load_records(cursor(0), s0);
   TileCursor pc{r0, 0};
@@ -365,7 +363,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     }
     Lane4 l;
     ring_read_tile<LAYOUT>(buf, l);
-    const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, a.rec_n, a.esc_last);
+    const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, (CMP ? 0ull : a.n_esc), a.esc_last);
     uint32_t xb1[kXpf ? 1 : 16];
     if (!kXpf && B == 1) load_x_lane(a.x + pc.ct * kTile, lg, xb1);
     uint32_t marks[kLaneGroups];
@@ -373,8 +371,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
     // a dense tile's symbol run goes into its own slot (free: the tile is in
     // registers)
-    const bool dense = cnt_wave > a.dense_min;
-    const bool ahead = a.compact && cnt_wave <= AheadSyms<LAYOUT>::value;
+    const bool dense = cnt_wave > (CMP ? 0u : kDenseMin);
+    const bool ahead = CMP && cnt_wave <= AheadSyms<LAYOUT>::value;
     const uint32_t off0 =
         dense && !ahead ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
     uint32_t w[16];
@@ -617,7 +615,7 @@ static dim3 wave_grid(uint64_t rows, uint64_t rpw) {
   return dim3((unsigned)((waves + wpb - 1) / wpb));
 }
 
-template <int LAYOUT>
+template <int LAYOUT, bool CMP>
 static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
   GemvArgs a = a0;
   a.rows_per_wave = rows_per_wave(a.rows, a.cols);
@@ -635,17 +633,17 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
     // (batches of 8 and 16 with whole-tile rows take the matrix-core kernel)
     if (kGemvRing && a.cols % kTile == 0 && b <= 4) {
       switch (b) {
-        case 4: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4>), g, t, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2>), g, t, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1>), g, t, 0, s, p); break;
+        case 4: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP>), g, t, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2, CMP>), g, t, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP>), g, t, 0, s, p); break;
       }
     } else {
       switch (b) {
-        case 16: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 16>), g, t, 0, s, p); break;
-        case 8: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 8>), g, t, 0, s, p); break;
-        case 4: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 4>), g, t, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 2>), g, t, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 1>), g, t, 0, s, p); break;
+        case 16: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 16, CMP>), g, t, 0, s, p); break;
+        case 8: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 8, CMP>), g, t, 0, s, p); break;
+        case 4: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 4, CMP>), g, t, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 2, CMP>), g, t, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 1, CMP>), g, t, 0, s, p); break;
       }
     }
     done += b;
@@ -700,24 +698,22 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
     a.esc_idx = (const uint32_t*)container;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
-  a.rec_n = h.n_esc;
-  a.dense_min = kDenseMin;
   if (h.flags & WC_FLAG_COMPACT) {
     // no positions: every tile with escapes places its symbols by rank, and
     // the (never used) position prefetch reads the header
     a.compact = 1;
-    a.rec_n = 0;
     a.esc_last = 0;
     a.esc_pos = (const uint32_t*)container;
-    a.dense_min = 0;
   }
   a.batch = batch;
   a.dict = dict_of(&h);
   if (cols % kGroup == 0) {
     if (h.layout == WC_LAYOUT_K15)
-      launch_fused_fast<WC_LAYOUT_K15>(a, s);
+      a.compact ? launch_fused_fast<WC_LAYOUT_K15, true>(a, s)
+                : launch_fused_fast<WC_LAYOUT_K15, false>(a, s);
     else
-      launch_fused_fast<WC_LAYOUT_BYTESPLIT>(a, s);
+      a.compact ? launch_fused_fast<WC_LAYOUT_BYTESPLIT, true>(a, s)
+                : launch_fused_fast<WC_LAYOUT_BYTESPLIT, false>(a, s);
   } else if (h.layout == WC_LAYOUT_K15) {
     hipLaunchKernelGGL(k_decode_gemv_generic<WC_LAYOUT_K15>, row_grid(rows), dim3(kBlockThreads), 0,
                        s, a);
