@@ -34,11 +34,6 @@ struct DecodeArgs {
   uint16_t* out;
   uint64_t n, n_esc, esc_last, raw_last, n_tiles, tiles_per_wave;
   uint64_t sym_last;  // last dword of the symbol stream's padded extent
-  // Records the sparse path may prefetch by position (n_esc, or 0 in the
-  // compact form, whose tiles all take symbols by rank from their run).
-  uint64_t rec_n;
-  uint32_t dense_min;  // tiles with more escapes take the run path
-  uint32_t compact;    // escape symbols only: runs prefetched with the tiles
   Dict dict;
 };
 
@@ -47,7 +42,10 @@ struct DecodeArgs {
 // tiles ahead, costs the fourth wave; it measured the same on the large
 // tensors and 11-13% slower on a 4096 x 4096 tensor, whose 4096 waves of two
 // tiles fill one round only with four waves per SIMD.)
-template <int LAYOUT>
+// CMP: the compact escape form (symbols only; every tile with escapes takes
+// its symbols by rank from its run), a template argument so that the full
+// form's kernel carries none of its branches.
+template <int LAYOUT, bool CMP>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   __shared__ uint32_t T2[256];
   // per wave: a ring of tile buffers filled by global->LDS loads, 4 KB per
@@ -85,7 +83,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
-    const bool dense = cnt_wave > a.dense_min;
+    const bool dense = cnt_wave > (CMP ? 0u : kDenseMin);
     // compact form: a run that came with the tile serves it when it fits
     const bool ahead = ahead_ok && cnt_wave <= AheadSyms<LAYOUT>::value;
     issue_next(e + cnt_wave);
@@ -116,13 +114,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
     };
     auto read_tile = [&](const uint32_t* buf, Lane4& l) { ring_read_tile<LAYOUT>(buf, l); };
     auto dma_eb = [&](uint64_t e0, uint32_t* buf) {
-      if (a.compact)
+      if constexpr (CMP)
         ring_load_symrun_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, buf);
       else
-        ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e0, buf);
+        ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, (CMP ? 0ull : a.n_esc), a.esc_last, e0, buf);
     };
     auto read_eb = [&](const uint32_t* buf, uint64_t e0) {
-      return ring_read_esc<LAYOUT>(buf, e0, a.rec_n, a.esc_last);
+      return ring_read_esc<LAYOUT>(buf, e0, (CMP ? 0ull : a.n_esc), a.esc_last);
     };
     uint32_t* const s0 = ring0[wib];
     uint32_t* const s1 = ring1[wib];
@@ -163,7 +161,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         read_tile(buf, l);
         const EscBatch eb = read_eb(buf, e);
         uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
-        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf, a.compact != 0);
+        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf, CMP);
         ++t;
       };
       while (t + 2 <= f1) {
@@ -201,7 +199,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
       }
     }
     uint32_t out[16];
-    const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, a.rec_n, a.esc_last, e);
+    const EscBatch eb = load_esc<LAYOUT>(a.esc_pos, a.esc_sym, (CMP ? 0ull : a.n_esc), a.esc_last, e);
     // no global->LDS load is in flight here: ring0 is free
     rebuild(full_tiles, l, eb, [](uint64_t) {}, out, ring0[wib], false);
 #pragma unroll
@@ -300,16 +298,11 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
     a.esc_sym = container;
     a.esc_idx = (const uint32_t*)container;
   }
-  a.rec_n = h.n_esc;
-  a.dense_min = kDenseMin;
-  if (h.flags & WC_FLAG_COMPACT) {
-    // no positions: every tile with escapes places its symbols by rank from
-    // its run, and the (never used) position prefetch reads the header
-    a.rec_n = 0;
+  const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
+  if (compact) {
+    // no positions: the (never used) position prefetch reads the header
     a.esc_last = 0;
     a.esc_pos = (const uint32_t*)container;
-    a.dense_min = 0;
-    a.compact = 1;
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;
@@ -326,10 +319,16 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb));
   a.dict = dict_of(&h);
   const dim3 blk(kBlockThreads);
-  if (h.layout == WC_LAYOUT_K15)
-    hipLaunchKernelGGL(k_decode<WC_LAYOUT_K15>, grid, blk, 0, s, a);
-  else
-    hipLaunchKernelGGL(k_decode<WC_LAYOUT_BYTESPLIT>, grid, blk, 0, s, a);
+  if (h.layout == WC_LAYOUT_K15) {
+    if (compact)
+      hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, true>), grid, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, false>), grid, blk, 0, s, a);
+  } else if (compact) {
+    hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, true>), grid, blk, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, false>), grid, blk, 0, s, a);
+  }
   return hipGetLastError();
 }
 
