@@ -141,3 +141,28 @@ def test_header_struct_layout(wc):
     assert list(h.dict)[:3] == [0x3F, 0x40, 0xBF]
     assert (h.off_codes, h.off_raw, h.off_esc_pos, h.total_bytes, h.off_esc_idx) == \
         (128, 144, 160, 160, 160)
+
+
+def test_compact_flag_in_header(wc):
+    """Headers of the oracle's compact containers validate on the host, with
+    the same accounting; an unknown flag, or the flag on the raw layout,
+    does not."""
+    w = synth.random_bits(30000, 9, "uniform")
+    for layout in (0, 1):
+        c = oracle.encode(layout, w, oracle.COMPACT)
+        h = wc.Header.from_bytes(c[:128].tobytes())
+        assert h.flags == wc.FLAG_COMPACT and h.off_esc_sym == h.off_esc_pos
+        assert wc.bits_per_weight(h) == pytest.approx(oracle.bits_per_weight(c), rel=1e-15)
+        bad = wc.Header.from_bytes(h.to_bytes())
+        bad.flags = 2
+        with pytest.raises(wc.WCError) as e:
+            wc.bits_per_weight(bad)
+        assert e.value.code == -3
+        bad = wc.Header.from_bytes(h.to_bytes())
+        bad.flags = 0  # the full form's offsets differ
+        with pytest.raises(wc.WCError):
+            wc.bits_per_weight(bad)
+    h = wc.Header.from_bytes(oracle.encode(2, w)[:128].tobytes())
+    h.flags = wc.FLAG_COMPACT
+    with pytest.raises(wc.WCError):
+        wc.bits_per_weight(h)
