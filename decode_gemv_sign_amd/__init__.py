@@ -134,15 +134,69 @@ def _stream(stream=None) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_device(t: torch.Tensor) -> bool:
+    """True for a tensor in GPU memory (the library takes device pointers only)."""
+    return t.device.type == "cuda"
+
+
 def _bits16(t: torch.Tensor, what: str) -> torch.Tensor:
-    """A contiguous 16-bit CUDA tensor viewed as raw BF16 bit patterns."""
-    if not t.is_cuda:
+    """A contiguous 16-bit device tensor viewed as raw BF16 bit patterns."""
+    if not _on_device(t):
         raise ValueError(f"{what} must be a device tensor")
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"{what} must hold BF16 bit patterns (bfloat16, int16 or uint16)")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     return t
+
+
+def _bytes(t: torch.Tensor, what: str, need: int) -> torch.Tensor:
+    """A contiguous uint8 device tensor of at least `need` bytes."""
+    if not _on_device(t):
+        raise ValueError(f"{what} must be a device tensor")
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{what} must be a uint8 tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() < need:
+        raise ValueError(f"{what} holds {t.numel()} bytes, {need} needed")
+    return t
+
+
+def _same_device(what: str, *ts: torch.Tensor):
+    devs = {t.device for t in ts}
+    if len(devs) > 1:
+        raise ValueError(f"{what}: tensors on different devices {sorted(map(str, devs))}")
+
+
+def _batch_of(x: torch.Tensor, cols: int, what: str = "x") -> int:
+    """Rows of x, which must be exactly [batch, cols] (or [cols] for batch 1):
+    the library reads batch * cols values and cannot check that itself."""
+    if x.dim() == 1:
+        batch = 1
+    elif x.dim() == 2:
+        batch = x.shape[0]
+    else:
+        raise ValueError(f"{what} must be [batch, cols] or [cols], got {tuple(x.shape)}")
+    if x.shape[-1] != cols or x.numel() != batch * cols:
+        raise ValueError(f"{what} has shape {tuple(x.shape)}, expected ({batch}, {cols})")
+    if not 1 <= batch <= MAX_BATCH:
+        raise ValueError(f"batch {batch} outside 1..{MAX_BATCH}")
+    return batch
+
+
+def _gemv_out(out: torch.Tensor, batch: int, rows: int, what: str = "out") -> torch.Tensor:
+    """y must be fp32 [batch, rows] (or [rows] for batch 1), contiguous, on the device."""
+    if not _on_device(out):
+        raise ValueError(f"{what} must be a device tensor")
+    if out.dtype != torch.float32:
+        raise TypeError(f"{what} must be float32")
+    if not out.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    ok = tuple(out.shape) == (batch, rows) or (batch == 1 and tuple(out.shape) == (rows,))
+    if not ok:
+        raise ValueError(f"{what} has shape {tuple(out.shape)}, expected ({batch}, {rows})")
+    return out
 
 
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
@@ -165,6 +219,8 @@ def build_dict(w: torch.Tensor, layout: int, work: torch.Tensor | None = None,
     n = w.numel()
     if work is None:
         work = _workspace(n, w.device)
+    _bytes(work, "work", workspace_bytes(n))
+    _same_device("build_dict", w, work)
     h = Header()
     _check(_lib.wc_build_dict(layout, _ptr(w), n, _ptr(work), work.numel(), _stream(stream),
                               ctypes.byref(h)), "wc_build_dict")
@@ -175,8 +231,13 @@ def encode_into(h: Header, w: torch.Tensor, container: torch.Tensor,
                 work: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """wc_encode into a caller-allocated uint8 container (asynchronous)."""
     w = _bits16(w, "w")
+    if w.numel() != h.n:
+        raise ValueError(f"w has {w.numel()} weights, the header {h.n}")
+    _bytes(container, "container", h.total_bytes)
     if work is None:
         work = _workspace(w.numel(), w.device)
+    _bytes(work, "work", workspace_bytes(w.numel()))
+    _same_device("encode_into", w, container, work)
     _check(_lib.wc_encode(ctypes.byref(h), _ptr(w), _ptr(container), container.numel(),
                           _ptr(work), work.numel(), _stream(stream)), "wc_encode")
     return container
@@ -200,9 +261,13 @@ def read_header(container: torch.Tensor) -> Header:
 def decode(h: Header, container: torch.Tensor, out: torch.Tensor | None = None,
            stream=None) -> torch.Tensor:
     """wc_decode: the n BF16 bit patterns (int16 tensor unless `out` is given)."""
+    _bytes(container, "container", h.total_bytes)
     if out is None:
         out = torch.empty(h.n, dtype=torch.int16, device=container.device)
     out = _bits16(out, "out")
+    if out.numel() < h.n:
+        raise ValueError(f"out holds {out.numel()} weights, {h.n} needed")
+    _same_device("decode", container, out)
     _check(_lib.wc_decode(ctypes.byref(h), _ptr(container), container.numel(), _ptr(out),
                           _stream(stream)), "wc_decode")
     return out
@@ -211,10 +276,15 @@ def decode(h: Header, container: torch.Tensor, out: torch.Tensor | None = None,
 def decode_gemv(h: Header, container: torch.Tensor, rows: int, cols: int, x: torch.Tensor,
                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """wc_decode_gemv: y [batch, rows] fp32 for x [batch, cols] BF16."""
+    _bytes(container, "container", h.total_bytes)
+    if rows * cols != h.n:
+        raise ValueError(f"rows * cols = {rows * cols}, the header holds {h.n} weights")
     x = _bits16(x, "x")
-    batch = 1 if x.dim() == 1 else x.shape[0]
+    batch = _batch_of(x, cols)
     if out is None:
         out = torch.empty((batch, rows), dtype=torch.float32, device=container.device)
+    _gemv_out(out, batch, rows)
+    _same_device("decode_gemv", container, x, out)
     _check(_lib.wc_decode_gemv(ctypes.byref(h), _ptr(container), container.numel(), rows, cols,
                                _ptr(x), batch, _ptr(out), _stream(stream)), "wc_decode_gemv")
     return out
@@ -224,11 +294,15 @@ def gemv_bf16(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:
     """wc_gemv_bf16: plain BF16 GEMV, W [rows, cols], x [batch, cols] -> [batch, rows]."""
     w = _bits16(w, "w")
+    if w.dim() != 2:
+        raise ValueError(f"w must be [rows, cols], got {tuple(w.shape)}")
     x = _bits16(x, "x")
     rows, cols = w.shape
-    batch = 1 if x.dim() == 1 else x.shape[0]
+    batch = _batch_of(x, cols)
     if out is None:
         out = torch.empty((batch, rows), dtype=torch.float32, device=w.device)
+    _gemv_out(out, batch, rows)
+    _same_device("gemv_bf16", w, x, out)
     _check(_lib.wc_gemv_bf16(_ptr(w), rows, cols, _ptr(x), batch, _ptr(out), _stream(stream)),
            "wc_gemv_bf16")
     return out

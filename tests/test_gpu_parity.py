@@ -412,28 +412,37 @@ def test_gemv_cols_zero_and_rows_zero():
 
 
 def test_error_codes():
+    """The library's own status codes, called through the C ABI directly (the
+    binding rejects these arguments itself before any library call)."""
+    import ctypes
     W = synth.random_bits(64 * 64, 1, "normal").reshape(64, 64)
     h, c = gpu_encode(0, W)
+    lib = wc._lib
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
     x = dev16(synth.vectors(1, 257, 64))
-    with pytest.raises(wc.WCError) as e:
-        wc.decode_gemv(h, c, 64, 64, x)
-    assert e.value.code == -5
-    with pytest.raises(wc.WCError) as e:
-        wc.decode_gemv(h, c, 32, 64, x[:1])
-    assert e.value.code == -1
+    y = torch.empty((257, 64), dtype=torch.float32, device=DEV)
+    assert lib.wc_decode_gemv(ctypes.byref(h), P(c.data_ptr()), c.numel(), 64, 64,
+                              P(x.data_ptr()), 257, P(y.data_ptr()), s) == -5
+    assert lib.wc_decode_gemv(ctypes.byref(h), P(c.data_ptr()), c.numel(), 32, 64,
+                              P(x.data_ptr()), 1, P(y.data_ptr()), s) == -1
     bad = wc.Header.from_bytes(h.to_bytes())
     bad.n_esc = bad.n + 1
-    with pytest.raises(wc.WCError) as e:
-        wc.decode(bad, c)
-    assert e.value.code == -3
-    with pytest.raises(wc.WCError) as e:
-        wc.decode(h, c[: h.total_bytes - 16])
-    assert e.value.code == -2
+    out = torch.empty(h.n, dtype=torch.int16, device=DEV)
+    assert lib.wc_decode(ctypes.byref(bad), P(c.data_ptr()), c.numel(), P(out.data_ptr()), s) == -3
+    assert lib.wc_decode(ctypes.byref(h), P(c.data_ptr()), h.total_bytes - 16,
+                         P(out.data_ptr()), s) == -2
     # misaligned output
     buf = torch.empty(h.n + 8, dtype=torch.int16, device=DEV)
     with pytest.raises(wc.WCError) as e:
         wc.decode(h, c, out=buf[1:1 + h.n])
     assert e.value.code == -1
+    # the binding's own checks come first
+    with pytest.raises(ValueError):
+        wc.decode_gemv(h, c, 64, 64, x)
+    with pytest.raises(ValueError):
+        wc.decode(h, c[: h.total_bytes - 16])
+    torch.cuda.synchronize()
 
 
 def test_determinism():
