@@ -35,6 +35,7 @@ AUTO = 3  # build_dict / encode only: the smallest of the three
 COMPACT = 0x10  # OR into a layout: escape symbols only (header flag FLAG_COMPACT)
 FLAG_COMPACT = 1
 MAX_BATCH = 256
+STAGE_SYMBOLS = 256  # WC_STAGE_SYMBOLS
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwc.so")
 
 _CODES = {0: "WC_OK", -1: "WC_E_ARG", -2: "WC_E_SIZE", -3: "WC_E_CORRUPT", -4: "WC_E_HIP",
@@ -205,7 +206,7 @@ def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
 
 def workspace_bytes(n: int) -> int:
     """WC_WORKSPACE_BYTES(n)."""
-    return 20480 + 8 * ((n + 8191) // 8192)
+    return 20512 + (8 + 2 * STAGE_SYMBOLS) * ((n + 8191) // 8192)
 
 
 def _workspace(n: int, device) -> torch.Tensor:

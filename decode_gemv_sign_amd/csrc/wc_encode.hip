@@ -13,13 +13,16 @@
 //               global copies; the byte-split histogram is the pair sum) ->
 //               k_top15 (sums the copies; rank by count desc, symbol asc) ->
 //               48-byte result copied to the host.
-//   encode:     k_pack (codes, raw stream, per-block escape counts, header and
-//               zero gaps) -> k_scan (exclusive scan of the block counts) ->
-//               k_emit (escape positions and symbols in weight order, and the
-//               escape index: the records before each 2048-weight tile).
+//   encode:     k_pack (codes, raw stream, header and zero gaps, each block's
+//               escape count, and the escape symbols of blocks with few
+//               escapes staged in the workspace) -> k_scan (exclusive scan of
+//               the block counts, one workgroup) -> k_emit (escape positions
+//               from the codes and symbols from the stage, in weight order,
+//               and the escape index).
 // Every output byte is a pure function of the input, so the container is
 // byte-identical from run to run.
 #include "wc_launch.h"
+#include "wc_tile.h"
 
 namespace wc {
 
@@ -183,84 +186,154 @@ hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t*
   return hipGetLastError();
 }
 
-// ---- pack ----------------------------------------------------------------
+// ---- pack, scan, escape records ---------------------------------------------
+//
+// Block b of k_pack and of k_emit covers weights [8192 b, 8192 b + 8192):
+// 1024 groups of 8, thread t taking groups t, t+256, t+512, t+768, so every
+// 16-byte load of a wave covers 1 KB of contiguous weights.  Group t + 256 j
+// lies in the block's 2048-weight tile j, so tile j's escapes are the
+// code-15 weights of the threads' j-th groups, in thread order.
+//
+// The escape records of the tensor are in weight order: block b's first
+// record is the number of escapes in blocks 0 .. b-1.  k_pack counts each
+// block's escapes; k_scan turns the counts into those prefix sums; k_emit
+// writes each block's records from there.  The records need the escaped
+// symbols, which the code stream does not hold: k_pack stages them (in
+// weight order, u16 each) for every block with at most `stage_cap` escapes,
+// so k_emit reads them back instead of the weights; only a block with more
+// escapes (a dense escape band) has its weights read again, in whole lines.
+
+constexpr uint32_t kDirectRecords = 256;  // blocks with more records write them through LDS
+
+// Per-tile exclusive scans of the threads' group escape counts over the
+// block (tile j = the threads' j-th groups, in thread order), two tiles per
+// 32-bit word: a tile holds at most 2048 escapes, so the halves never carry.
+// ex01/ex23: this thread's exclusive prefix in tiles 0/1 and 2/3; tot01 /
+// tot23: the tiles' totals.  Contains a block barrier.
+struct BlockEsc {
+  uint32_t ex01, ex23, tot01, tot23;
+  __device__ uint32_t ex(int j) const {
+    return (j < 2 ? (j == 0 ? ex01 : ex01 >> 16) : (j == 2 ? ex23 : ex23 >> 16)) & 0xFFFFu;
+  }
+  __device__ uint32_t tile(int j) const {
+    return (j < 2 ? (j == 0 ? tot01 : tot01 >> 16) : (j == 2 ? tot23 : tot23 >> 16)) & 0xFFFFu;
+  }
+  __device__ uint32_t total() const {
+    return (tot01 & 0xFFFFu) + (tot01 >> 16) + (tot23 & 0xFFFFu) + (tot23 >> 16);
+  }
+  // first escape of tile j relative to the block's first
+  __device__ uint32_t tile_base(int j) const {
+    uint32_t s = 0;
+    for (int q = 0; q < j; ++q) s += tile(q);
+    return s;
+  }
+};
+
+__device__ inline BlockEsc block_escape_scan(const uint32_t emask[4], uint32_t (*wtot)[kBlockThreads / kWave]) {
+  constexpr int kWpb = kBlockThreads / kWave;
+  const int lane = lane_id();
+  const int wib = wave_in_block();
+  const uint32_t p01 = (uint32_t)__popc(emask[0]) | ((uint32_t)__popc(emask[1]) << 16);
+  const uint32_t p23 = (uint32_t)__popc(emask[2]) | ((uint32_t)__popc(emask[3]) << 16);
+  const uint32_t i01 = wave_incl_scan_dpp(p01), i23 = wave_incl_scan_dpp(p23);
+  if (lane == kWave - 1) {
+    wtot[0][wib] = i01;
+    wtot[1][wib] = i23;
+  }
+  __syncthreads();
+  BlockEsc e{0, 0, 0, 0};
+  uint32_t b01 = 0, b23 = 0;
+#pragma unroll
+  for (int q = 0; q < kWpb; ++q) {
+    b01 += q < wib ? wtot[0][q] : 0u;
+    b23 += q < wib ? wtot[1][q] : 0u;
+    e.tot01 += wtot[0][q];
+    e.tot23 += wtot[1][q];
+  }
+  e.ex01 = b01 + i01 - p01;
+  e.ex23 = b23 + i23 - p23;
+  return e;
+}
 
 struct PackArgs {
   const uint16_t* w;
   uint8_t* container;
-  uint32_t* blk_cnt;
+  uint32_t* cnt;      // per-block escape counts
+  uint16_t* stage;    // stage_cap symbols per block
+  uint32_t stage_cap;
   uint64_t n;
   wc_header h;
 };
 
-// Block b encodes weights [8192 b, 8192 b + 8192): 1024 groups of 8, thread t
-// taking groups t, t+256, t+512, t+768, so every 16-byte input load of a wave
-// covers 1 KB of contiguous weights.  The block's code and raw bytes are
-// assembled in a zero-filled LDS image (K15 groups are 7 bytes, unaligned)
-// and written out with aligned 16-byte stores up to each stream's padded end,
-// which also writes the streams' zero padding.
 template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
   constexpr int kGroups = kPackBlock / 8;                                  // 1024
   constexpr int kRawBytes = LAYOUT == WC_LAYOUT_K15 ? 7 * kGroups : 8 * kGroups;
+  constexpr int kShift = LAYOUT == WC_LAYOUT_K15 ? 7 : 8;
   __shared__ uint8_t lut[512];
-  __shared__ uint32_t wsum[kBlockThreads / kWave];
+  __shared__ uint32_t wtot[2][kBlockThreads / kWave];
   __shared__ __attribute__((aligned(16))) uint32_t img_codes[kGroups];     // 4 KB
   __shared__ __attribute__((aligned(16))) uint32_t img_raw[kRawBytes / 4];  // 7 or 8 KB
   const int tid = threadIdx.x;
+  const wc_header& h = a.h;
+  const bool with_esc = h.n_esc != 0;
   for (int sidx = tid; sidx < 512; sidx += kBlockThreads) lut[sidx] = 15;
   for (int q = tid; q < kGroups; q += kBlockThreads) img_codes[q] = 0;
   for (int q = tid; q < kRawBytes / 4; q += kBlockThreads) img_raw[q] = 0;
   __syncthreads();
-  if (tid < (int)a.h.n_dict) lut[a.h.dict[tid]] = (uint8_t)tid;
+  if (tid < (int)h.n_dict) lut[h.dict[tid]] = (uint8_t)tid;
   __syncthreads();
 
-  const wc_header& h = a.h;
-  const uint64_t w0 = (uint64_t)blockIdx.x * kPackBlock;  // first weight of the block
-  uint32_t esc = 0;
+  const uint64_t blk = blockIdx.x;
+  const uint64_t w0 = blk * kPackBlock;  // first weight of the block
   uint8_t* rimg = (uint8_t*)img_raw;
   // a full block (every block but possibly the last) loads its four groups at once
   const bool full = w0 + kPackBlock <= a.n;
-  u32x4 pre[4];
+  uint32_t wd[4][4];  // per group: weights 2i (low half) and 2i+1 (high half)
   if (full) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pre[j] = __builtin_nontemporal_load((const u32x4*)(a.w + w0) + tid + kBlockThreads * j);
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + w0) + tid + kBlockThreads * j);
+      wd[j][0] = v[0]; wd[j][1] = v[1]; wd[j][2] = v[2]; wd[j][3] = v[3];
+    }
   }
+  uint32_t emask[4];  // per group: bit i set when weight i has code 15
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int g = tid + kBlockThreads * j;  // group within the block
     const uint64_t gw = w0 + 8u * (uint64_t)g;
-    if (gw >= a.n) continue;
-    const uint32_t valid = a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
-    uint32_t wd[4];  // weights 2i (low half) and 2i+1 (high half)
-    if (full) {
-      wd[0] = pre[j][0]; wd[1] = pre[j][1]; wd[2] = pre[j][2]; wd[3] = pre[j][3];
-    } else if (valid == 8) {
-      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + gw));
-      wd[0] = v[0]; wd[1] = v[1]; wd[2] = v[2]; wd[3] = v[3];
-    } else {
+    emask[j] = 0;
+    if (!full) {
+      wd[j][0] = wd[j][1] = wd[j][2] = wd[j][3] = 0;
+      if (gw >= a.n) continue;
+      const uint32_t valid = a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
+      if (valid == 8) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + gw));
+        wd[j][0] = v[0]; wd[j][1] = v[1]; wd[j][2] = v[2]; wd[j][3] = v[3];
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (uint32_t)(2 * i) < valid ? a.w[gw + 2 * i] : 0u;
-        const uint32_t hi = (uint32_t)(2 * i + 1) < valid ? a.w[gw + 2 * i + 1] : 0u;
-        wd[i] = lo | (hi << 16);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = (uint32_t)(2 * i) < valid ? a.w[gw + 2 * i] : 0u;
+          const uint32_t hi = (uint32_t)(2 * i + 1) < valid ? a.w[gw + 2 * i + 1] : 0u;
+          wd[j][i] = lo | (hi << 16);
+        }
       }
     }
+    const uint32_t valid = a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
     // codes: nibble i = code of weight i (even weight in the low nibble)
     uint32_t cd = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t b = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      const uint32_t code = (uint32_t)i < valid ? lut[b >> (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)] : 0u;
-      esc += code == 15u ? 1u : 0u;
+      const uint32_t b = (wd[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const uint32_t code = (uint32_t)i < valid ? lut[b >> kShift] : 0u;
+      emask[j] |= (code == 15u ? 1u : 0u) << i;
       cd |= code << (4 * i);
     }
     img_codes[g] = cd;
     if (LAYOUT == WC_LAYOUT_BYTESPLIT) {
       // low bytes of weights 0..3 and 4..7
-      uint32_t r0 = __builtin_amdgcn_perm(wd[1], wd[0], 0x06040200u);
-      uint32_t r1 = __builtin_amdgcn_perm(wd[3], wd[2], 0x06040200u);
+      uint32_t r0 = __builtin_amdgcn_perm(wd[j][1], wd[j][0], 0x06040200u);
+      uint32_t r1 = __builtin_amdgcn_perm(wd[j][3], wd[j][2], 0x06040200u);
       if (valid < 8) {
         const uint64_t keep = valid ? (~0ull >> (64 - 8 * valid)) : 0ull;
         r0 &= (uint32_t)keep;
@@ -273,39 +346,54 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
       uint64_t m = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint64_t mi = (uint32_t)i < valid ? (wd[i >> 1] >> (16 * (i & 1))) & 0x7Fu : 0u;
+        const uint64_t mi = (uint32_t)i < valid ? (wd[j][i >> 1] >> (16 * (i & 1))) & 0x7Fu : 0u;
         m |= mi << (7 * i);
       }
 #pragma unroll
       for (int k = 0; k < 7; ++k) rimg[7 * g + k] = (uint8_t)(m >> (8 * k));
     }
   }
-  // escape count of the block
-  const uint32_t ws = wave_sum_u32(esc);
-  if (lane_id() == 0) wsum[tid / kWave] = ws;
-  __syncthreads();
-  if (tid == 0 && w0 < a.n) {  // n == 0 has no blocks to count
-    uint32_t t = 0;
-    for (int q = 0; q < kBlockThreads / kWave; ++q) t += wsum[q];
-    a.blk_cnt[blockIdx.x] = t;
+
+  if (with_esc) {
+    // (the scan's barrier also orders the image writes above before the copies below)
+    const BlockEsc be = block_escape_scan(emask, wtot);
+    const uint32_t total = be.total();
+    if (tid == 0) a.cnt[blk] = total;
+    if (total != 0 && total <= a.stage_cap) {
+      // the block's escaped symbols, in weight order
+      uint16_t* st = a.stage + blk * a.stage_cap;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t m = emask[j];
+        uint32_t o = be.tile_base(j) + be.ex(j);
+        while (m) {
+          const int i = __builtin_ctz(m);
+          m &= m - 1u;
+          st[o++] = (uint16_t)(((wd[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) >> kShift);
+        }
+      }
+    }
+  } else {
+    __syncthreads();  // the images are complete before they are copied out
   }
+
   // the block's stream images, up to each stream's padded end
   {
     const uint64_t cpad = pad16((a.n + 1u) / 2u);
-    const uint64_t c0 = (uint64_t)blockIdx.x * (kGroups * 4u);
+    const uint64_t c0 = blk * (kGroups * 4u);
     const uint64_t cend = c0 + kGroups * 4u < cpad ? c0 + kGroups * 4u : cpad;
     u32x4* dst = (u32x4*)(a.container + h.off_codes + c0);
     const u32x4* srcv = (const u32x4*)img_codes;
     for (uint64_t q = tid; c0 + 16u * q < cend; q += kBlockThreads) dst[q] = srcv[q];
     const uint64_t rpad = pad16(raw_bytes(LAYOUT, a.n));
-    const uint64_t r0 = (uint64_t)blockIdx.x * kRawBytes;
+    const uint64_t r0 = blk * kRawBytes;
     const uint64_t rend = r0 + kRawBytes < rpad ? r0 + kRawBytes : rpad;
     u32x4* rdst = (u32x4*)(a.container + h.off_raw + r0);
     const u32x4* rsrc = (const u32x4*)img_raw;
     for (uint64_t q = tid; r0 + 16u * q < rend; q += kBlockThreads) rdst[q] = rsrc[q];
   }
   // header and the escape streams' zero gaps
-  if (blockIdx.x == 0) {
+  if (blk == 0) {
     if (tid < 32) ((uint32_t*)a.container)[tid] = ((const uint32_t*)&a.h)[tid];
     if (tid == 32) {
       const uint64_t pe = h.off_esc_pos + pos_bytes(h.flags, h.n_esc);
@@ -318,105 +406,216 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
   }
 }
 
-// ---- scan of block escape counts ----------------------------------------
+// ---- scan of block escape counts -------------------------------------------
+// One workgroup of 1024 threads: chunks of 16384 counts, thread t taking 16
+// consecutive counts of a chunk; a carry joins the chunks.  Also writes the
+// escape index's closing entry (the escape count).
 
-__global__ __launch_bounds__(1024) void k_scan(const uint32_t* __restrict__ cnt,
-                                               uint32_t* __restrict__ off, uint64_t nblk) {
-  __shared__ uint32_t wtot[1024 / kWave];
-  const uint64_t tid = threadIdx.x;
-  const uint64_t seg = (nblk + 1023) / 1024;
-  const uint64_t b0 = tid * seg;
-  const uint64_t b1 = b0 + seg < nblk ? b0 + seg : nblk;
-  uint32_t s = 0;
-  for (uint64_t i = b0; i < b1; ++i) s += cnt[i];
-  const uint32_t ex = wave_excl_scan_u32(s);
-  if (lane_id() == kWave - 1) wtot[tid / kWave] = ex + s;
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;
+
+__global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t* __restrict__ cnt,
+                                                       uint32_t* __restrict__ off, uint64_t nblk,
+                                                       uint32_t* __restrict__ close_entry,
+                                                       uint32_t n_esc) {
+  __shared__ uint32_t wtot[kScanThreads / kWave];
+  __shared__ uint32_t sh_carry;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wib = tid / kWave;
+  if (tid == 0) {
+    sh_carry = 0;
+    *close_entry = n_esc;
+  }
   __syncthreads();
-  uint32_t wbase = 0;
-  for (uint64_t q = 0; q < tid / kWave; ++q) wbase += wtot[q];
-  uint32_t run = wbase + ex;
-  for (uint64_t i = b0; i < b1; ++i) {
-    off[i] = run;
-    run += cnt[i];
+  for (uint64_t base = 0; base < nblk; base += (uint64_t)kScanThreads * kScanPer) {
+    const uint64_t i0 = base + (uint64_t)tid * kScanPer;
+    uint32_t v[kScanPer];
+    if (i0 + kScanPer <= nblk) {
+#pragma unroll
+      for (int k = 0; k < kScanPer; k += 4) {
+        const u32x4 q = *(const u32x4*)(cnt + i0 + k);
+        v[k] = q[0]; v[k + 1] = q[1]; v[k + 2] = q[2]; v[k + 3] = q[3];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kScanPer; ++k) v[k] = i0 + k < nblk ? cnt[i0 + k] : 0u;
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) s += v[k];
+    const uint32_t ex = wave_excl_scan_u32(s);
+    if (lane == kWave - 1) wtot[wib] = ex + s;
+    __syncthreads();
+    uint32_t before = 0, chunk = 0;
+    for (int q = 0; q < kScanThreads / kWave; ++q) {
+      before += q < wib ? wtot[q] : 0u;
+      chunk += wtot[q];
+    }
+    uint32_t run = sh_carry + before + ex;
+    if (i0 + kScanPer <= nblk) {
+#pragma unroll
+      for (int k = 0; k < kScanPer; k += 4) {
+        u32x4 q;
+        q[0] = run; run += v[k];
+        q[1] = run; run += v[k + 1];
+        q[2] = run; run += v[k + 2];
+        q[3] = run; run += v[k + 3];
+        *(u32x4*)(off + i0 + k) = q;
+      }
+    } else {
+      for (int k = 0; k < kScanPer; ++k) {
+        if (i0 + k < nblk) off[i0 + k] = run;
+        run += v[k];
+      }
+    }
+    __syncthreads();  // every thread has read sh_carry and wtot
+    if (tid == 0) sh_carry += chunk;
+    __syncthreads();
   }
 }
 
-// ---- escape records --------------------------------------------------------
+// ---- escape records ---------------------------------------------------------
 
 struct EmitArgs {
   const uint16_t* w;
   uint8_t* container;
-  const uint32_t* blk_cnt;
-  const uint32_t* blk_off;
+  const uint32_t* cnt;
+  const uint32_t* off;
+  const uint16_t* stage;
+  uint32_t stage_cap;
   uint64_t n;
   wc_header h;
 };
 
-// Block b covers weights [8192 b, 8192 b + 8192): wave q of it covers exactly
-// the 2048-weight tile 4 b + q, so the wave's first record number is that
-// tile's escape-index entry.
 template <int LAYOUT>
 __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
-  static_assert(kTile == (int)WC_INDEX_TILE && kPackBlock == 4 * kTile, "one index tile per wave");
-  __shared__ uint32_t wtot[kBlockThreads / kWave];
+  constexpr int kGroups = kPackBlock / 8;
+  constexpr int kShift = LAYOUT == WC_LAYOUT_K15 ? 7 : 8;
+  __shared__ uint32_t wtot[2][kBlockThreads / kWave];
+  // a dense tile's records: 8 KB of positions, 4 KB of symbols
+  __shared__ __attribute__((aligned(16))) uint32_t st_pos[2 * kGroups];
+  __shared__ __attribute__((aligned(16))) uint16_t st_sym[2 * kGroups];
   const int tid = threadIdx.x;
-  uint32_t* const index = (uint32_t*)(a.container + a.h.off_esc_idx);
+  const wc_header& h = a.h;
+  const uint64_t blk = blockIdx.x;
+  const uint64_t w0 = blk * kPackBlock;
   const uint64_t n_tiles = (a.n + kTile - 1) / kTile;
-  const uint64_t my_tile = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)(tid / kWave);
-  if (blockIdx.x == gridDim.x - 1 && tid == 0) index[n_tiles] = (uint32_t)a.h.n_esc;  // closing entry
-  if (a.blk_cnt[blockIdx.x] == 0) {  // whole block: no escapes
-    if ((tid & (kWave - 1)) == 0 && my_tile < n_tiles) index[my_tile] = a.blk_off[blockIdx.x];
+  uint32_t* const index = (uint32_t*)(a.container + h.off_esc_idx);
+  const uint32_t cntb = a.cnt[blk];
+  const uint32_t excl = a.off[blk];
+  if (cntb == 0) {  // block-uniform: index entries only
+    if (tid < 4 && 4u * blk + (uint64_t)tid < n_tiles) index[4u * blk + tid] = excl;
     return;
   }
-  const uint64_t chunk = (uint64_t)blockIdx.x * kBlockThreads + (uint64_t)tid;
-  const uint64_t base = chunk * kChunk;
-  uint32_t mask = 0;  // bit i: weight base+i escapes
-  if (base < a.n) {
-    const uint32_t valid = a.n - base >= kChunk ? kChunk : (uint32_t)(a.n - base);
-    const u32x4 c = *(const u32x4*)(a.container + a.h.off_codes + 16u * chunk);
+  // the block's codes, in k_pack's group mapping; codes past n are 0
+  const uint32_t* codes = (const uint32_t*)(a.container + h.off_codes) + w0 / 8;
+  uint32_t emask[4];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      const uint32_t code = (c[i >> 3] >> (4 * (i & 7))) & 15u;
-      if (code == 15u && (uint32_t)i < valid) mask |= 1u << i;
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t gw = w0 + 8u * (uint64_t)(tid + kBlockThreads * j);
+    const uint32_t c = gw < a.n ? codes[tid + kBlockThreads * j] : 0u;
+    emask[j] = group_esc_bits(c);
+  }
+  const BlockEsc be = block_escape_scan(emask, wtot);
+  if (tid < 4 && 4u * blk + (uint64_t)tid < n_tiles) index[4u * blk + tid] = excl + be.tile_base(tid);
+  // the escaped symbols: staged by k_pack, or from the weights again
+  const bool staged = cntb <= a.stage_cap;
+  const uint16_t* st = a.stage + blk * a.stage_cap;
+  uint32_t wd[4][4];
+  if (!staged) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wd[j][0] = wd[j][1] = wd[j][2] = wd[j][3] = 0;
+      if (!emask[j]) continue;
+      const uint64_t gw = w0 + 8u * (uint64_t)(tid + kBlockThreads * j);
+      if (gw + 8 <= a.n) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + gw));
+        wd[j][0] = v[0]; wd[j][1] = v[1]; wd[j][2] = v[2]; wd[j][3] = v[3];
+      } else {
+        for (int i = 0; gw + i < a.n; ++i) wd[j][i >> 1] |= (uint32_t)a.w[gw + i] << (16 * (i & 1));
+      }
     }
   }
-  const uint32_t cnt = __popc(mask);
-  const uint32_t ex = wave_excl_scan_u32(cnt);
-  if (lane_id() == kWave - 1) wtot[tid / kWave] = ex + cnt;
-  __syncthreads();
-  uint32_t wbase = 0;
-  for (int q = 0; q < tid / kWave; ++q) wbase += wtot[q];
-  uint64_t o = (uint64_t)a.blk_off[blockIdx.x] + wbase + ex;
-  if (lane_id() == 0 && my_tile < n_tiles) index[my_tile] = (uint32_t)o;  // ex == 0 in lane 0
-  uint32_t* pos = (uint32_t*)(a.container + a.h.off_esc_pos);
-  uint8_t* sym = a.container + a.h.off_esc_sym;
-  const bool compact = (a.h.flags & WC_FLAG_COMPACT) != 0;
-  while (mask) {
-    const int i = __builtin_ctz(mask);
-    mask &= mask - 1u;
-    if (o < a.h.n_esc) {
-      const uint64_t p = base + (uint64_t)i;
-      const uint32_t s = (uint32_t)a.w[p] >> (LAYOUT == WC_LAYOUT_K15 ? 7 : 8);
-      if (!compact) pos[o] = (uint32_t)p;  // the compact form keeps symbols only
-      if (LAYOUT == WC_LAYOUT_K15)
-        ((uint16_t*)sym)[o] = (uint16_t)s;
-      else
-        sym[o] = (uint8_t)s;
+  auto sym_at = [&](int j, int i, uint32_t rank) -> uint32_t {
+    return staged ? (uint32_t)st[rank] : ((wd[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) >> kShift;
+  };
+  uint32_t* pos = (uint32_t*)(a.container + h.off_esc_pos);
+  uint8_t* sym = a.container + h.off_esc_sym;
+  const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
+  if (cntb <= kDirectRecords) {
+    // few records: each thread stores its own
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t m = emask[j];
+      if (!m) continue;
+      uint32_t r = be.tile_base(j) + be.ex(j);  // rank in the block
+      const uint64_t gw = w0 + 8u * (uint64_t)(tid + kBlockThreads * j);
+      while (m) {
+        const int i = __builtin_ctz(m);
+        m &= m - 1u;
+        const uint64_t o = (uint64_t)excl + r;
+        if (o < h.n_esc) {
+          if (!compact) pos[o] = (uint32_t)(gw + (uint64_t)i);  // the compact form keeps symbols only
+          if (LAYOUT == WC_LAYOUT_K15)
+            ((uint16_t*)sym)[o] = (uint16_t)sym_at(j, i, r);
+          else
+            sym[o] = (uint8_t)sym_at(j, i, r);
+        }
+        ++r;
+      }
     }
-    ++o;
+  } else {
+    // many: each tile's records go through LDS in order and out with
+    // lane-contiguous stores
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t tc = be.tile(j);
+      if (tc == 0) continue;  // block-uniform
+      const uint32_t tb = be.tile_base(j);
+      uint32_t m = emask[j];
+      uint32_t o = be.ex(j);
+      const uint64_t gw = w0 + 8u * (uint64_t)(tid + kBlockThreads * j);
+      while (m) {
+        const int i = __builtin_ctz(m);
+        m &= m - 1u;
+        st_pos[o] = (uint32_t)(gw + (uint64_t)i);
+        st_sym[o] = (uint16_t)sym_at(j, i, tb + o);
+        ++o;
+      }
+      __syncthreads();
+      for (uint32_t q = (uint32_t)tid; q < tc; q += kBlockThreads) {
+        const uint64_t oo = (uint64_t)excl + tb + q;
+        if (oo < h.n_esc) {
+          if (!compact) pos[oo] = st_pos[q];
+          if (LAYOUT == WC_LAYOUT_K15)
+            ((uint16_t*)sym)[oo] = st_sym[q];
+          else
+            sym[oo] = (uint8_t)st_sym[q];
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
-hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
-                         hipStream_t s) {
+// Encode with the block state at `state` (16-byte aligned: counts, offsets,
+// then the symbol stage of `stage_cap` u16 per block, which may be 0).
+static hipError_t launch_encode_state(const wc_header& h, const uint16_t* w, uint8_t* container,
+                                      uint8_t* state, uint32_t stage_cap, hipStream_t s) {
   if (h.layout == WC_LAYOUT_RAW) return launch_encode_raw(h, w, container, s);
   const uint64_t nblk = (h.n + kPackBlock - 1) / kPackBlock;
-  uint32_t* blk_cnt = (uint32_t*)(work + kWorkBlocks);
-  uint32_t* blk_off = blk_cnt + nblk;
+  // counts and offsets each start 16-byte aligned (k_scan moves them 16 bytes at a time)
+  const uint64_t nblk4 = (nblk + 3) & ~(uint64_t)3;
+  uint32_t* cnt = (uint32_t*)state;
+  uint32_t* off = cnt + nblk4;
+  uint16_t* stage = (uint16_t*)(state + 8u * nblk4);
   PackArgs p;
   p.w = w;
   p.container = container;
-  p.blk_cnt = blk_cnt;
+  p.cnt = cnt;
+  p.stage = stage;
+  p.stage_cap = stage_cap;
   p.n = h.n;
   p.h = h;
   // n == 0 still runs one block: it writes the header
@@ -426,12 +625,16 @@ hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* contain
   else
     hipLaunchKernelGGL(k_pack<WC_LAYOUT_BYTESPLIT>, grid, dim3(kBlockThreads), 0, s, p);
   if (h.n_esc == 0 || nblk == 0) return hipGetLastError();
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, blk_cnt, blk_off, nblk);
+  const uint64_t n_tiles = (h.n + kTile - 1) / kTile;
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, (const uint32_t*)cnt, off, nblk,
+                     (uint32_t*)(container + h.off_esc_idx) + n_tiles, (uint32_t)h.n_esc);
   EmitArgs e;
   e.w = w;
   e.container = container;
-  e.blk_cnt = blk_cnt;
-  e.blk_off = blk_off;
+  e.cnt = cnt;
+  e.off = off;
+  e.stage = stage;
+  e.stage_cap = stage_cap;
   e.n = h.n;
   e.h = h;
   if (h.layout == WC_LAYOUT_K15)
@@ -439,6 +642,11 @@ hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* contain
   else
     hipLaunchKernelGGL(k_emit<WC_LAYOUT_BYTESPLIT>, dim3((unsigned)nblk), dim3(kBlockThreads), 0, s, e);
   return hipGetLastError();
+}
+
+hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
+                         hipStream_t s) {
+  return launch_encode_state(h, w, container, work + kWorkBlocks, WC_STAGE_SYMBOLS, s);
 }
 
 }  // namespace wc

@@ -11,7 +11,8 @@ constexpr int kHistGlobal = 8;          // copies of the global histogram (block
 constexpr size_t kWorkHist = 0;         // u32[kHistGlobal][512] symbol counts
 constexpr size_t kWorkResult = 16384;   // DictResult (of the layout asked for; byte-split's under AUTO)
 constexpr size_t kWorkResult2 = 16432;  // DictResult of K15 under AUTO
-constexpr size_t kWorkBlocks = 20480;   // u32[nblk] escape counts, then u32[nblk] offsets
+constexpr size_t kWorkBlocks = 20480;   // encode: u32[nblk] escape counts, u32[nblk] offsets, then
+                                        // the symbol stage (WC_STAGE_SYMBOLS u16 per block)
 static_assert(kWorkHist + 4u * 512u * kHistGlobal <= kWorkResult, "histogram copies fit");
 
 struct DictResult {

@@ -98,8 +98,13 @@ extern "C" {
 #define WC_FLAG_COMPACT 1u
 #define WC_COMPACT 0x10
 
-/* Scratch bytes wc_build_dict and wc_encode need for n weights. */
-#define WC_WORKSPACE_BYTES(n) ((size_t)20480 + (size_t)8 * (((uint64_t)(n) + 8191u) / 8192u))
+/* Scratch bytes wc_build_dict and wc_encode need for n weights: 20512, plus
+ * 8 per 8192-weight block for its escape count and first record, plus
+ * 2 * WC_STAGE_SYMBOLS per block, where encode stages the escaped symbols of
+ * blocks that have at most WC_STAGE_SYMBOLS of them (0.063 bytes/weight). */
+#define WC_STAGE_SYMBOLS 256u
+#define WC_WORKSPACE_BYTES(n) \
+  ((size_t)20512 + (size_t)(8u + 2u * WC_STAGE_SYMBOLS) * (((uint64_t)(n) + 8191u) / 8192u))
 
 /* The first 128 bytes of every container, byte for byte. */
 typedef struct wc_header {

@@ -184,3 +184,18 @@ def all_patterns(shuffle_seed: int | None = None) -> np.ndarray:
 def vectors(cfg_seed: int, batch: int, cols: int) -> np.ndarray:
     """x [batch, cols] ~ N(0, 1) rounded to BF16 (seeded by [cfg_seed, 1000])."""
     return _vectors(cfg_seed, batch, cols)
+
+
+def layerset_tensor_device(t: int, device):
+    """Tensor t of the layer set drawn on a GPU (torch's seeded device
+    generator, seed 4000 + t), as int16 BF16 bit patterns: the same shapes and
+    distributions as ``layerset_tensor``, without drawing 20 GiB on the host.
+    The values differ from the host draw; both stand in for the same recipe."""
+    import torch
+    name, shape, mean, sigma = layerset_spec(t)
+    n = int(np.prod(shape))
+    g = torch.Generator(device=device)
+    g.manual_seed(4000 + t)
+    z = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+    z.mul_(sigma).add_(mean)
+    return name, shape, z.to(torch.bfloat16).view(torch.int16)

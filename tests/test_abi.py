@@ -123,9 +123,21 @@ def test_argument_checks_before_device_work(wc):
                             None) == -5
 
 
-def test_workspace_formula(wc):
-    for n in (0, 1, 8191, 8192, 8193, 10 ** 9):
-        assert wc.workspace_bytes(n) == 20480 + 8 * ((n + 8191) // 8192)
+def test_workspace_formula(wc, tmp_path):
+    """The binding's workspace size equals the header's WC_WORKSPACE_BYTES(n),
+    evaluated by a C program compiled against include/wc.h."""
+    ns = (0, 1, 8191, 8192, 8193, 10 ** 9, (1 << 32) - 1)
+    src = tmp_path / "ws.c"
+    src.write_text('#include <stdio.h>\n#include "wc.h"\nint main(void){\n' +
+                   "".join(f'printf("%zu\\n", WC_WORKSPACE_BYTES({n}ull));\n' for n in ns) +
+                   "return 0;}\n")
+    exe = tmp_path / "ws"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src),
+                           "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)], text=True).split()]
+    assert got == [wc.workspace_bytes(n) for n in ns]
+    # counts and offsets (8 bytes) plus the symbol stage per 8192-weight block
+    assert wc.workspace_bytes(8192) - wc.workspace_bytes(0) == 8 + 2 * wc.STAGE_SYMBOLS
 
 
 def test_header_struct_layout(wc):
