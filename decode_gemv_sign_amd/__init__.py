@@ -22,7 +22,7 @@ import os
 import torch  # loaded first, so libwc binds to the HIP runtime torch already uses
 
 __all__ = [
-    "BYTESPLIT", "K15", "RAW", "AUTO", "COMPACT", "FLAG_COMPACT", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into",
+    "BYTESPLIT", "K15", "RAW", "AUTO", "COMPACT", "FLAG_COMPACT", "Header", "WCError", "workspace_bytes", "build_dict", "encode_into", "encode_into_noalloc",
     "encode", "decode", "decode_gemv", "gemv_bf16", "bits_per_weight", "read_header",
     "crc32", "container_crcs", "artifact_write", "artifact_entries", "artifact_read",
     "artifact_verify", "LIB_PATH",
@@ -93,6 +93,7 @@ def _load(path: str = LIB_PATH):
     HP = ctypes.POINTER(Header)
     lib.wc_build_dict.argtypes = [ctypes.c_int, P, U64, P, ctypes.c_size_t, P, HP]
     lib.wc_encode.argtypes = [HP, P, P, ctypes.c_size_t, P, ctypes.c_size_t, P]
+    lib.wc_encode_noalloc.argtypes = [HP, P, P, ctypes.c_size_t, P]
     lib.wc_decode.argtypes = [HP, P, ctypes.c_size_t, P, P]
     lib.wc_decode_gemv.argtypes = [HP, P, ctypes.c_size_t, U64, U64, P, ctypes.c_uint32, P, P]
     lib.wc_gemv_bf16.argtypes = [P, U64, U64, P, ctypes.c_uint32, P, P]
@@ -108,7 +109,7 @@ def _load(path: str = LIB_PATH):
     lib.wc_artifact_entry.argtypes = [ctypes.c_char_p, ctypes.c_uint32,
                                       ctypes.POINTER(ArtifactInfo)]
     lib.wc_artifact_read.argtypes = [ctypes.c_char_p, ctypes.c_uint32, P, ctypes.c_size_t]
-    for f in (lib.wc_build_dict, lib.wc_encode, lib.wc_decode, lib.wc_decode_gemv,
+    for f in (lib.wc_build_dict, lib.wc_encode, lib.wc_encode_noalloc, lib.wc_decode, lib.wc_decode_gemv,
               lib.wc_gemv_bf16, lib.wc_bits_per_weight, lib.wc_container_crcs,
               lib.wc_artifact_write, lib.wc_artifact_count, lib.wc_artifact_entry,
               lib.wc_artifact_read):
@@ -241,6 +242,21 @@ def encode_into(h: Header, w: torch.Tensor, container: torch.Tensor,
     _same_device("encode_into", w, container, work)
     _check(_lib.wc_encode(ctypes.byref(h), _ptr(w), _ptr(container), container.numel(),
                           _ptr(work), work.numel(), _stream(stream)), "wc_encode")
+    return container
+
+
+def encode_into_noalloc(h: Header, w: torch.Tensor, container: torch.Tensor,
+                        stream=None) -> torch.Tensor:
+    """wc_encode_noalloc: as encode_into, with the library's own per-GPU
+    scratch instead of a workspace (nothing is allocated; calls that overlap
+    on one GPU race)."""
+    w = _bits16(w, "w")
+    if w.numel() != h.n:
+        raise ValueError(f"w has {w.numel()} weights, the header {h.n}")
+    _bytes(container, "container", h.total_bytes)
+    _same_device("encode_into_noalloc", w, container)
+    _check(_lib.wc_encode_noalloc(ctypes.byref(h), _ptr(w), _ptr(container), container.numel(),
+                                  _stream(stream)), "wc_encode_noalloc")
     return container
 
 

@@ -3,7 +3,8 @@
 // Argument checks happen here, before anything is enqueued; kernels and
 // launch geometry live in wc_encode.hip, wc_decode.hip and wc_gemv.hip.
 // The library allocates no device or host memory: every buffer is the
-// caller's.
+// caller's (wc_encode_noalloc's fixed scratch array is part of the loaded
+// code object, see wc_encode.hip).
 #include <string.h>
 
 #include "wc_launch.h"
@@ -99,6 +100,17 @@ extern "C" int wc_encode(const wc_header* h, const uint16_t* d_w, uint8_t* d_con
   if (!d_work || !wc::aligned16(d_work)) return WC_E_ARG;
   if (work_bytes < WC_WORKSPACE_BYTES(h->n) || container_bytes < h->total_bytes) return WC_E_SIZE;
   return hip_status(wc::launch_encode(*h, d_w, d_container, (uint8_t*)d_work, (hipStream_t)stream));
+}
+
+extern "C" int wc_encode_noalloc(const wc_header* h, const uint16_t* d_w, uint8_t* d_container,
+                                 size_t container_bytes, void* stream) {
+  if (!h || !d_container || !wc::aligned16(d_container)) return WC_E_ARG;
+  const int v = wc::validate_header(h);
+  if (v != WC_OK) return v;
+  if (h->n > WC_NOALLOC_MAX_N) return WC_E_SIZE;
+  if (h->n && (!d_w || !wc::aligned16(d_w))) return WC_E_ARG;
+  if (container_bytes < h->total_bytes) return WC_E_SIZE;
+  return hip_status(wc::launch_encode_noalloc(*h, d_w, d_container, (hipStream_t)stream));
 }
 
 extern "C" int wc_decode(const wc_header* h, const uint8_t* d_container, size_t container_bytes,

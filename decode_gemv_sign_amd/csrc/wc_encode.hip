@@ -21,6 +21,8 @@
 //               and the escape index).
 // Every output byte is a pure function of the input, so the container is
 // byte-identical from run to run.
+#include <mutex>
+
 #include "wc_launch.h"
 #include "wc_tile.h"
 
@@ -647,6 +649,48 @@ static hipError_t launch_encode_state(const wc_header& h, const uint16_t* w, uin
 hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
                          hipStream_t s) {
   return launch_encode_state(h, w, container, work + kWorkBlocks, WC_STAGE_SYMBOLS, s);
+}
+
+// ---- encode without a workspace --------------------------------------------
+// For callers that cannot allocate: the block counts and offsets live in a
+// fixed device array of the library, one per GPU, held until the process
+// ends, sized for the largest tensor taken (WC_NOALLOC_MAX_N weights, 8
+// bytes per 8192-weight block).  Nothing is staged there, so k_emit reads
+// the weights of every block with escapes again; the container is the same.
+// In host code the array's name stands for a host-side symbol, not a device
+// address: its device address is looked up once per device and only that
+// address reaches the kernels.  Every call rewrites the counts and offsets
+// of its blocks before reading them, so nothing needs clearing.  Calls that
+// overlap on one GPU share the array and race.
+constexpr size_t kScratchBytes = 8u * (WC_NOALLOC_MAX_N / kPackBlock) + 32u;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[64];
+
+static hipError_t scratch_address(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = (uint8_t*)g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_encode_noalloc(const wc_header& h, const uint16_t* w, uint8_t* container,
+                                 hipStream_t s) {
+  uint8_t* sp = nullptr;
+  const hipError_t e = scratch_address(&sp);
+  if (e != hipSuccess) return e;
+  return launch_encode_state(h, w, container, sp, 0, s);
 }
 
 }  // namespace wc

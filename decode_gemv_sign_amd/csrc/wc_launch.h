@@ -47,6 +47,10 @@ hipError_t launch_decode_raw(const wc_header& h, const uint8_t* container, uint1
                              hipStream_t s);
 hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* container, uint8_t* work,
                          hipStream_t s);
+// The same with the library's own per-GPU scratch (no workspace argument);
+// h.n <= WC_NOALLOC_MAX_N.
+hipError_t launch_encode_noalloc(const wc_header& h, const uint16_t* w, uint8_t* container,
+                                 hipStream_t s);
 hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t* out,
                          hipStream_t s);
 hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint64_t rows,

@@ -159,6 +159,27 @@ int wc_encode(const wc_header *h, const uint16_t *d_w, uint8_t *d_container,
               void *stream);
 
 /*
+ * wc_encode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same container as wc_encode for the same header and
+ * weights.  Its scratch (each 8192-weight block's escape count and first
+ * record) is a fixed device array of the library, 8 * 2^18 + 32 bytes
+ * (2 MiB) on each GPU it runs on, held until the process ends; every call
+ * writes what it reads there first.  It stages no escape symbols, so the
+ * weights of blocks with escapes are read twice (wc_encode reads them once
+ * when a block has at most WC_STAGE_SYMBOLS escapes).  h->n >
+ * WC_NOALLOC_MAX_N -> WC_E_SIZE.
+ * All calls on one GPU share that array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must not be issued; calls in
+ * one stream's order are safe.  Allocates nothing (no hipMalloc, hipFree or
+ * allocating library call); the first call on a device looks up the
+ * array's device address.
+ */
+#define WC_NOALLOC_MAX_N (1ull << 31)
+int wc_encode_noalloc(const wc_header *h, const uint16_t *d_w, uint8_t *d_container,
+                      size_t container_bytes, void *stream);
+
+/*
  * Exact decode [P3 "Cómo funciona la compresión"; P2 "¿Qué significa “sin
  * pérdida”…"]: rebuilds the n BF16 bit patterns into d_out[0..n).  *h is the
  * host copy of the container's header (validated: WC_E_CORRUPT).  Escape

@@ -29,7 +29,8 @@ def wc():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "wc_build_dict", "wc_encode", "wc_decode", "wc_decode_gemv", "wc_gemv_bf16",
+        "wc_build_dict", "wc_encode", "wc_encode_noalloc", "wc_decode", "wc_decode_gemv",
+        "wc_gemv_bf16",
         "wc_bits_per_weight", "wc_crc32", "wc_container_crcs", "wc_artifact_write",
         "wc_artifact_count", "wc_artifact_entry", "wc_artifact_read"])
 
