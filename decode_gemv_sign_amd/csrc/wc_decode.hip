@@ -19,10 +19,15 @@
 
 namespace wc {
 
-#ifndef WC_DECODE_TILES_PER_WAVE
-#define WC_DECODE_TILES_PER_WAVE 4
-#endif
-constexpr uint64_t kDecodeTilesPerWave = WC_DECODE_TILES_PER_WAVE;
+// Tiles per wave on tensors larger than one round of waves (measured on the
+// layer set's 6144 x 24576 tensors, fraction of the 8 TB/s peak by tiles per
+// wave 1 / 2 / 3 / 4 / 6: byte-split 0.76 / 0.70 / 0.70 / 0.69 / 0.67, K15
+// 0.70 / 0.74 / 0.71 / 0.70 / 0.67).  Byte-split tiles carry almost no
+// escapes, and a wave per tile spreads the loads widest; K15 tiles patch
+// about 40 escapes each, whose record loads a two-tile run issues one tile
+// ahead.
+constexpr uint64_t kDecodeTilesBS = 1;
+constexpr uint64_t kDecodeTilesK15 = 2;
 
 
 struct DecodeArgs {
@@ -45,7 +50,10 @@ struct DecodeArgs {
 // CMP: the compact escape form (symbols only; every tile with escapes takes
 // its symbols by rank from its run), a template argument so that the full
 // form's kernel carries none of its branches.
-template <int LAYOUT, bool CMP>
+// SLOTS: 2 for runs of several tiles; 1 when every wave takes one tile (the
+// second slot would never be filled, and half the LDS lets twice the blocks
+// share a compute unit).
+template <int LAYOUT, bool CMP, int SLOTS>
 __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   __shared__ uint32_t T2[256];
   // per wave: a ring of tile buffers filled by global->LDS loads, 4 KB per
@@ -53,7 +61,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
   // doubles as the escape stage of the tile just read from it
   constexpr int kWpb = kBlockThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint32_t ring0[kWpb][kRingSlotDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t ring1[kWpb][kRingSlotDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring1[kWpb][SLOTS == 2 ? kRingSlotDwords : 4];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
       return ring_read_esc<LAYOUT>(buf, e0, (CMP ? 0ull : a.n_esc), a.esc_last);
     };
     uint32_t* const s0 = ring0[wib];
-    uint32_t* const s1 = ring1[wib];
+    uint32_t* const s1 = SLOTS == 2 ? ring1[wib] : ring0[wib];  // one slot: never refilled
     {
       // Two slots, one tile ahead.
       auto slot_buf = [&](auto slc) -> uint32_t* {
@@ -161,7 +169,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         read_tile(buf, l);
         const EscBatch eb = read_eb(buf, e);
         uint32_t* nbuf = slot_buf(std::integral_constant<int, sl + 1>{});
-        rebuild(t, l, eb, [&](uint64_t en) { dma_eb(en, nbuf); }, out, buf, CMP);
+        // (the next tile's records: with one slot there is never a next tile,
+        // and the slot is this tile's escape stage, so nothing is loaded)
+        rebuild(t, l, eb, [&](uint64_t en) { if (SLOTS == 2) dma_eb(en, nbuf); }, out, buf, CMP);
         ++t;
       };
       while (t + 2 <= f1) {
@@ -306,28 +316,35 @@ hipError_t launch_decode(const wc_header& h, const uint8_t* container, uint16_t*
   }
   a.raw_last = pad16(raw_bytes(h.layout, h.n)) / 4 - 1;
   a.n_tiles = (h.n + kTile - 1) / kTile;
-  // Runs of 4 tiles per wave: short runs keep the waves that run at the same
-  // time on neighbouring memory (whole-tensor runs per resident wave measured
-  // 12% slower).  A tensor that fits in one round of 3-tile runs of the
-  // waves the chip holds at once (4 per SIMD, LDS-bound) takes runs that
-  // fill exactly one round instead.
+  // Short runs of tiles per wave keep the waves that run at the same time on
+  // neighbouring memory (whole-tensor runs per resident wave measured 12%
+  // slower than 4-tile runs, and shorter runs faster still, see above).  A
+  // tensor that fits in one round of 3-tile runs of the waves the chip holds
+  // at once (4 per SIMD, LDS-bound) takes runs that fill exactly one round.
   const uint64_t slots = (uint64_t)cu_count() * 4u * 4u;
   const bool one_round = a.n_tiles <= 3 * slots;
-  a.tiles_per_wave = one_round ? (a.n_tiles + slots - 1) / slots : kDecodeTilesPerWave;
+  a.tiles_per_wave = one_round ? (a.n_tiles + slots - 1) / slots
+                               : (h.layout == WC_LAYOUT_K15 ? kDecodeTilesK15 : kDecodeTilesBS);
   const uint64_t waves = (a.n_tiles + a.tiles_per_wave - 1) / a.tiles_per_wave;
   const uint64_t wpb = kBlockThreads / kWave;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb));
   a.dict = dict_of(&h);
   const dim3 blk(kBlockThreads);
+  const bool one = a.tiles_per_wave == 1;
   if (h.layout == WC_LAYOUT_K15) {
-    if (compact)
-      hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, true>), grid, blk, 0, s, a);
-    else
-      hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, false>), grid, blk, 0, s, a);
+    if (compact) {
+      if (one) hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, true, 1>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, true, 2>), grid, blk, 0, s, a);
+    } else {
+      if (one) hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, false, 1>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_decode<WC_LAYOUT_K15, false, 2>), grid, blk, 0, s, a);
+    }
   } else if (compact) {
-    hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, true>), grid, blk, 0, s, a);
+    if (one) hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, true, 1>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, true, 2>), grid, blk, 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, false>), grid, blk, 0, s, a);
+    if (one) hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, false, 1>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_decode<WC_LAYOUT_BYTESPLIT, false, 2>), grid, blk, 0, s, a);
   }
   return hipGetLastError();
 }
