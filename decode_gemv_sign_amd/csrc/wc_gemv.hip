@@ -48,6 +48,8 @@ struct GemvArgs {
   uint64_t sym_last;  // last dword of the symbol stream's padded extent
   uint32_t compact;    // escape symbols only (no position stream)
   uint32_t batch;
+  uint32_t wpr;        // ring kernel, split rows: parts per row (rows, cols are the parts')
+  uint64_t x_cols;     // ring kernel, split rows: length of an x row (the real cols)
   Dict dict;
 };
 
@@ -272,11 +274,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
 // of the register ring.  At batch 1, x for the next tile rides in
 // registers; larger batches read x when the tile is used.  Each step issues
 // the next tile's loads first and waits for them before its dot product.
-template <int LAYOUT, int B, bool CMP>
+//
+// SPLIT: a row of W[R][C] is split into a.wpr parts of whole tiles, each a
+// row of the same bytes viewed as W[R * wpr][C / wpr] (row-major order and
+// tile numbering are unchanged, so the escape index serves as it is).  The
+// kernel runs on that view, one part per wave (a.rows, a.cols are the
+// parts'; a.rows_per_wave is 1); part p of a row reads x from column
+// p * a.cols on, and the waves of the block that hold one row's parts add
+// their sums in LDS in column order, so the result does not depend on which
+// wave ends first.  Measured at batch 4 on 6144 x 24576 (4 parts of 3
+// tiles): 82 against 87 us byte-split, 89 against 91 K15; at batch 1 it was
+// slower (57 against 50), so batch 1 keeps whole rows.
+template <int LAYOUT, int B, bool CMP, bool SPLIT>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) {
   __shared__ uint32_t T2[256];
   __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][kRingSlotDwords];
   __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][kRingSlotDwords];
+  __shared__ float part_sum[kBlockThreads / kWave][SPLIT ? B : 1];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
 
@@ -284,7 +298,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   const int wib = wave_in_block();
   const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wib;
   const uint64_t r0 = wave * a.rows_per_wave;
-  if (r0 >= a.rows) return;
+  if (!SPLIT && r0 >= a.rows) return;
+  // split rows: every wave of the block reaches the combine below
+  if (!SPLIT || r0 < a.rows) {
   const uint64_t r1 = r0 + a.rows_per_wave < a.rows ? r0 + a.rows_per_wave : a.rows;
   const uint64_t gpr = a.cols / kGroup;
   const uint64_t tpr = a.cols / kTile;  // whole tiles
@@ -299,9 +315,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   // tile q of the wave: row r0 + q / tpr, tile q % tpr of the row (loaded
   // for q < nq only)
   TileCursor lc{r0, 0};
+  // x of a row's part p starts at column p * a.cols
+  auto xrow = [&](uint64_t r) -> const uint16_t* {
+    return SPLIT ? a.x + (r % a.wpr) * a.cols : a.x;
+  };
   auto load_next = [&](uint32_t* buf, uint32_t xv[16]) {
     ring_load_tile<LAYOUT>(a.codes, a.raw, lc.r * gpr + lc.ct * (kTile / kGroup), buf);
-    if (kXpf) load_x_lane(a.x + lc.ct * kTile, lg, xv);
+    if (kXpf) load_x_lane(xrow(lc.r) + lc.ct * kTile, lg, xv);
     lc.next(tpr);
   };
 
@@ -397,12 +417,20 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         uint32_t xb[16];
-        load_x_lane(a.x + (uint64_t)b * a.cols + pc.ct * kTile, lg, xb);
+        load_x_lane(xrow(pc.r) + (uint64_t)b * (SPLIT ? a.x_cols : a.cols) + pc.ct * kTile, lg, xb);
         acc[b] = dot_lane(w, xb, acc[b]);
       }
     }
     if (pc.ct + 1 == tpr) {
-      store_row<B>(acc, a.y, a.rows, pc.r);
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float t = wave_sum_f32(acc[b]);
+          if (lane == 0) part_sum[wib][b] = t;
+        }
+      } else {
+        store_row<B>(acc, a.y, a.rows, pc.r);
+      }
 #pragma unroll
       for (int b = 0; b < B; ++b) acc[b] = 0.0f;
     }
@@ -415,6 +443,19 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   }
   if (q < nq) step(q, s0, s1, x0, x1);
   wait_vm<0>();  // the last tile's (unused) record loads land before the wave ends
+  }
+  if constexpr (SPLIT) {
+    __syncthreads();
+    if (r0 < a.rows && r0 % a.wpr == 0 && lane == 0) {
+      const uint64_t rows_real = a.rows / a.wpr;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float t = part_sum[wib][b];
+        for (uint32_t k = 1; k < a.wpr; ++k) t += part_sum[wib + k][b];
+        a.y[(uint64_t)b * rows_real + r0 / a.wpr] = t;
+      }
+    }
+  }
 }
 
 // The same wave/tile schedule as k_decode_gemv with W read as plain BF16
@@ -587,6 +628,10 @@ constexpr uint32_t kMfmaMinBatch = WC_MFMA_MIN_BATCH;
 #define WC_GEMV_RING 1
 #endif
 constexpr bool kGemvRing = WC_GEMV_RING;
+#ifndef WC_SPLIT_MIN_TILES
+#define WC_SPLIT_MIN_TILES 4
+#endif
+constexpr uint64_t kSplitMinTiles = WC_SPLIT_MIN_TILES;  // rows of more tiles are split at batch 4
 
 static dim3 row_grid(uint64_t rows) {
   const uint64_t wpb = kBlockThreads / kWave;
@@ -632,10 +677,24 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
     const dim3 g = wave_grid(a.rows, a.rows_per_wave), t(kBlockThreads);
     // (batches of 8 and 16 with whole-tile rows take the matrix-core kernel)
     if (kGemvRing && a.cols % kTile == 0 && b <= 4) {
-      switch (b) {
-        case 4: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP>), g, t, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2, CMP>), g, t, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP>), g, t, 0, s, p); break;
+      // Batch 4 on rows of more than kSplitMinTiles tiles: each row split into
+      // 4 (or 2) parts of whole tiles, one wave each (see the kernel).
+      const uint64_t tpr = a.cols / kTile;
+      const uint32_t wpr = b == 4 && tpr > kSplitMinTiles ? (tpr % 4 == 0 ? 4u : tpr % 2 == 0 ? 2u : 1u) : 1u;
+      if (wpr > 1) {
+        GemvArgs v = p;
+        v.wpr = wpr;
+        v.x_cols = a.cols;
+        v.rows = a.rows * wpr;
+        v.cols = a.cols / wpr;
+        v.rows_per_wave = 1;
+        hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
+      } else {
+        switch (b) {
+          case 4: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, false>), g, t, 0, s, p); break;
+          case 2: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2, CMP, false>), g, t, 0, s, p); break;
+          default: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, false>), g, t, 0, s, p); break;
+        }
       }
     } else {
       switch (b) {
