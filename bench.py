@@ -1087,7 +1087,45 @@ def summarize_counters(fetch_dir, write_dir, workload, md_out=None, command=""):
     print(json.dumps({"workload": workload, "fetch_scale": fs, "write_scale": ws, "decode": entry}))
 
 
+def summarize_trace(stats_csv, md_out, command, bench_json=None):
+    """Markdown table of a `rocprofv3 --kernel-trace --stats` run's per-kernel
+    statistics; with the profiled run's bench line, the decode kernel's mean
+    launch time over the trace beside the one the bench line reports."""
+    import csv
+    with open(stats_csv, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1]) if bench_json else None
+    lines = [f"Command: {command}", ""]
+    if line:
+        lines += [f"Workload: {line['config']['workload']}", ""]
+    lines += ["| kernel | calls | avg µs | min µs | max µs | % GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    if line:
+        by = (line.get("roofline") or {}).get("by_layout") or {}
+        lines += ["", "Decode launch time, the trace against the bench line of the same run:", ""]
+        for lay, tag in ((0, "byte-split"), (1, "K15")):
+            ks = [r for r in rows if r["Name"].startswith(f"void wc::k_decode<{lay},")]
+            calls = sum(int(r["Calls"]) for r in ks)
+            if not calls or tag not in by:
+                continue
+            avg = sum(float(r["TotalDurationNs"]) for r in ks) / calls / 1e3
+            lines.append(f"* {tag}: trace mean {avg:.2f} µs over {calls} launches "
+                         f"({', '.join(r['Name'].split('(')[0] for r in ks)}); bench "
+                         f"launch_us {by[tag]['launch_us']} (ratio {by[tag]['launch_us'] / avg:.3f})")
+    with open(md_out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        # bench.py --summarize-trace STATS_CSV MD_OUT COMMAND [BENCH_JSON]
+        a = sys.argv[2:]
+        summarize_trace(a[0], a[1], a[2], a[3] if len(a) > 3 else None)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
         # bench.py --summarize-counters FETCH_DIR WRITE_DIR WORKLOAD [MD_OUT] [COMMAND]
         a = sys.argv[2:]

@@ -7,9 +7,10 @@
 // (page "Compresión de pesos LLM sin pérdida vs 8-bit GGUF: ¿qué está listo
 // para producción?", sections "¿Está listo para producción el resultado de
 // GLM-5.2?" and "Preguntas para un vendor o equipo de investigación").  Here
-// every byte of the file is under a CRC-32: the file header, each table
-// entry and each of a container's six regions; a reader reports any
-// mismatch as WC_E_CORRUPT before a container reaches the GPU.
+// every byte of the file is either under a CRC-32 (the file header, each
+// table entry and each of a container's six regions) or a gap byte that must
+// be zero where the writer puts it; a reader reports any mismatch as
+// WC_E_CORRUPT before a container reaches the GPU.
 #include <stdio.h>
 #include <string.h>
 #include <sys/stat.h>
@@ -269,10 +270,29 @@ extern "C" int wc_artifact_count(const char* path, uint32_t* count) {
   uint64_t doff, fsize;
   int st = read_file_header(file, &n, &doff, &fsize);
   if (st != WC_OK) return st;
+  // every container where the writer places it, and every byte between the
+  // table and the data and between containers zero: with the CRCs, a change
+  // to any byte of the file is then reported
   wc_artifact_info info;
-  for (uint32_t i = 0; i < n; ++i) {
-    st = read_entry(file, i, &info);
-    if (st != WC_OK) return st;
+  uint64_t gap_lo = kFileHeader + (uint64_t)kEntry * n, at = doff;
+  uint8_t chunk[WC_ARTIFACT_ALIGN];
+  for (uint32_t i = 0; i <= n; ++i) {
+    uint64_t gap_hi = fsize;
+    if (i < n) {
+      st = read_entry(file, i, &info);
+      if (st != WC_OK) return st;
+      if (info.offset != at) return WC_E_CORRUPT;
+      gap_hi = info.offset;
+    }
+    if (gap_hi < gap_lo || gap_hi - gap_lo >= WC_ARTIFACT_ALIGN) return WC_E_CORRUPT;
+    const size_t len = (size_t)(gap_hi - gap_lo);
+    if (len && !file.read_at(gap_lo, chunk, len)) return WC_E_CORRUPT;
+    for (size_t k = 0; k < len; ++k)
+      if (chunk[k]) return WC_E_CORRUPT;
+    if (i < n) {
+      gap_lo = info.offset + info.bytes;
+      at = align_up(gap_lo);
+    }
   }
   *count = n;
   return WC_OK;

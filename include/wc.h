@@ -287,7 +287,11 @@ int wc_artifact_write(const char *path, uint32_t count, const char *const *names
                       const uint8_t *const *h_containers, const uint64_t *container_bytes,
                       const uint32_t *src_crcs);
 
-/* Number of entries, after checking the file header and every entry's CRC. */
+/* Number of entries, after checking the file header, every entry's CRC, that
+ * each container sits where the writer places it (the data offset, then the
+ * next 4096-byte boundary after the previous one; the file ends with the last)
+ * and that every gap byte is zero: with the CRCs, any changed byte of the file
+ * is reported as WC_E_CORRUPT. */
 int wc_artifact_count(const char *path, uint32_t *count);
 
 /* Entry i's metadata (file header and entry checked). */

@@ -108,6 +108,11 @@ def test_corruption_is_detected(wc, tmp_path):
         base = 64 + 256 * i
         spots += [(f"entry {i} name", base + 1), (f"entry {i} shape", base + 104),
                   (f"entry {i} offset", base + 137), (f"entry {i} crc", base + 253)]
+    # the zero gaps: after the table, and after each container but the last
+    spots.append(("gap after the table", 64 + 256 * len(items)))
+    for e in ents[:-1]:
+        if (e["offset"] + e["bytes"]) % 4096:
+            spots.append((f"gap after {e['name']}", e["offset"] + e["bytes"]))
     for i, e in enumerate(ents):
         c = items[i][3]
         info = oracle.header_info(c)
