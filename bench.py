@@ -1105,8 +1105,12 @@ def summarize_trace(stats_csv, md_out, command, bench_json=None):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
     if line:
-        by = (line.get("roofline") or {}).get("by_layout") or {}
-        lines += ["", "Decode launch time, the trace against the bench line of the same run:", ""]
+        roof = line.get("roofline") or {}
+        by = roof.get("by_layout") or {}
+        if not by and roof.get("kernel"):  # one tensor: the slower layout only
+            by = {roof["kernel"].split("(")[1].rstrip(")"): {"launch_us": roof["launch_us"]}}
+        lines += ["", "Decode launch time, the trace against the bench line of the same run "
+                  "(the trace's mean covers every decode launch of the run):", ""]
         for lay, tag in ((0, "byte-split"), (1, "K15")):
             ks = [r for r in rows if r["Name"].startswith(f"void wc::k_decode<{lay},")]
             calls = sum(int(r["Calls"]) for r in ks)
