@@ -99,8 +99,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode(DecodeArgs a) {
         dense && !ahead ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, stg) : 0u;
     rebuild_lane<LAYOUT>(T2, l, out);
     if (dense && ahead) {
-      patch_tile_symrun<LAYOUT>(l, out, stg + 768,
-                                (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u));
+      const uint32_t off = (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u);
+      // K15 tiles with few escapes per lane: by rank gather (wc_tile.h)
+      uint32_t gm[kLaneGroups], gc[kLaneGroups], gf[kLaneGroups];
+      bool few = false;
+      if (LAYOUT == WC_LAYOUT_K15) {
+        group_records(l, gm, gc, gf);
+        few = !__ballot((gc[0] + gc[1] + gc[2] + gc[3]) > (uint32_t)kGatherMax);
+      }
+      if (few)
+        patch_tile_gather<LAYOUT>(stg, out, gm, gf, lds_addr(stg + 768) + off);
+      else
+        patch_tile_symrun<LAYOUT>(l, out, stg + 768, off);
     } else if (dense) {
       wait_vm<0>();  // the symbol run is complete
       patch_tile_symrun<LAYOUT>(l, out, stg, off0);

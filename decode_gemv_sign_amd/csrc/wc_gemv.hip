@@ -90,6 +90,13 @@ __device__ inline void store_row(float acc[B], float* __restrict__ y, uint64_t r
 #ifndef WC_GEMV_PREFETCH_X
 #define WC_GEMV_PREFETCH_X 1
 #endif
+#ifndef WC_GATHER
+#define WC_GATHER 1
+#endif
+// K15 tiles with few escapes per lane are patched by rank gather at batch 1
+// (measured on 6144 x 24576 N(0, 0.015), compact form: 80 -> 67 us); the
+// window path stays faster for byte-split, whose windows are cheap
+constexpr bool kGatherOn = WC_GATHER;
 constexpr int kGemvDepth = WC_GEMV_DEPTH;            // tiles in the prefetch ring
 constexpr bool kGemvPrefetchX = WC_GEMV_PREFETCH_X;  // x rides in the ring at batch 1
 
@@ -309,6 +316,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   uint32_t* const s1 = ring1[wib];
 
   constexpr bool kXpf = B == 1;
+  // K15 symbol windows per LDS round trip: one at batch 4, where the
+  // batch's accumulators leave no registers for two
+  constexpr int kSymPass = B == 1 ? 2 : 1;
   uint32_t lg[kLaneGroups];
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) lg[k] = (uint32_t)lane + kWave * k;
@@ -344,39 +354,50 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
       iv = v < a.n_esc ? v : (uint32_t)a.n_esc;
     }
   };
-  // first record of tile q; called with q non-decreasing
-  auto cursor = [&](uint64_t q) -> uint64_t {
-    if (q - qb >= (uint64_t)kWave) {
+  // Entries of tiles q .. q + 2 in the lanes (a tile's first record, and its
+  // escape count as the next tile's first record minus its own); called
+  // with q non-decreasing.
+  auto window = [&](uint64_t q) {
+    if (q + 2 - qb >= (uint64_t)kWave) {
       qb = q;
       load_iv();
     }
+  };
+  auto entry = [&](uint64_t q) -> uint64_t {
     return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)iv, (int)(q - qb));
   };
 
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
   load_next(s0, x0);  // in flight while the escape index is read
   load_iv();
-  // a tile's first records go out with its ring loads; in the compact form,
-  // the start of its symbol run instead (the same number of loads)
-  auto load_records = [&](uint64_t e0, uint32_t* buf) {
+  // With a tile's ring loads go its first records; in the compact form,
+  // which has none, the start of its symbol run instead, as much of it as
+  // the index says the tile holds (the same number of loads either way).
+  // (Taking the run instead of the records also for full-form tiles with
+  // many escapes measured slower: 6144 x 24576 banded, 57.6 against 55.6 us.)
+  auto load_records = [&](uint64_t e0, uint64_t cnt, uint32_t* buf) {
     if constexpr (CMP)
-      ring_load_symrun_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, buf);
+      ring_load_run_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, cnt, buf);
     else
       ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, (CMP ? 0ull : a.n_esc), a.esc_last, e0, buf);
   };
-  load_records(cursor(0), s0);
+  window(0);
+  load_records(entry(0), entry(1) - entry(0), s0);
   TileCursor pc{r0, 0};
 
   auto step = [&](uint64_t q, uint32_t* buf, uint32_t* nbuf, uint32_t xv[16], uint32_t xn[16]) {
     wait_lgkm0();  // the previous tile's LDS reads and stage writes are done
-    const uint64_t e = cursor(q);
-    // The next tile's ring loads and its first records go out together.  The
-    // first tile's ring and record loads are complete once at most those 3 +
-    // 2 loads are outstanding, or none when there is no next tile; later
-    // tiles' loads were issued before the previous tile's full wait.
+    window(q);
+    const uint64_t e = entry(q);
+    // The next tile's ring loads and its first records (or run) go out
+    // together.  The first tile's ring and record loads are complete once at
+    // most those 3 + 2 loads are outstanding, or none when there is no next
+    // tile; later tiles' loads were issued before the previous tile's full
+    // wait.
     if (q + 1 < nq) {
       load_next(nbuf, xn);
-      load_records(cursor(q + 1), nbuf);
+      const uint64_t e1 = entry(q + 1);
+      load_records(e1, entry(q + 2) - e1, nbuf);
       if (q == 0) wait_vm<kRingAheadEsc>();
     } else if (q == 0) {
       wait_vm<0>();
@@ -389,20 +410,30 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
-    // a dense tile's symbol run goes into its own slot (free: the tile is in
-    // registers)
+    // A dense tile is patched from its symbol run: the one that came with
+    // the tile when it fits, else one loaded into the slot now (free: the
+    // tile is in registers).
     const bool dense = cnt_wave > (CMP ? 0u : kDenseMin);
-    const bool ahead = CMP && cnt_wave <= AheadSyms<LAYOUT>::value;
+    const bool ahead = CMP && cnt_wave <= RunAheadSyms<LAYOUT>::value;
     const uint32_t off0 =
         dense && !ahead ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, l, w);
     if (dense && ahead) {
-      patch_tile_symrun<LAYOUT>(l, w, buf + 768,
-                                (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u));
+      const uint32_t off = (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u);
+      uint32_t gm[kLaneGroups], gc[kLaneGroups], gf[kLaneGroups];
+      bool few = false;
+      if (kGatherOn && B == 1 && LAYOUT == WC_LAYOUT_K15) {
+        group_records(l, gm, gc, gf);
+        few = !__ballot((gc[0] + gc[1] + gc[2] + gc[3]) > (uint32_t)kGatherMax);
+      }
+      if (few)
+        patch_tile_gather<LAYOUT>(buf, w, gm, gf, lds_addr(buf + 768) + off);
+      else
+        patch_tile_symrun<LAYOUT, kSymPass>(l, w, buf + 768, off);
     } else if (dense) {
       wait_vm<0>();
-      patch_tile_symrun<LAYOUT>(l, w, buf, off0);
+      patch_tile_symrun<LAYOUT, kSymPass>(l, w, buf, off0);
     } else if (cnt_wave) {
       patch_tile<LAYOUT>(buf, w, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
                          cnt_wave, pc.r * a.cols + pc.ct * kTile, kTile, eb);

@@ -567,25 +567,28 @@ __device__ inline void expand_window(uint32_t m, const uint32_t (&w)[WinDwords<L
     out[2] |= __builtin_amdgcn_perm(0u, hh, 0x010C000Cu);
     out[3] |= __builtin_amdgcn_perm(0u, hh, 0x030C020Cu);
   } else {
+    // symbols 0..7 of the window as little-endian u16 in a[0..3]; their low
+    // bytes gathered into lo[0..1] and their high bytes (the symbol's ninth
+    // bit) into hi[0..1], so that one byte permute by rank reaches any of
+    // the eight, as in the byte-split case
     uint32_t a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // weights 2j, 2j+1: their ranks and marks, each byte doubled
-      const uint32_t R = j < 2 ? rl : rh, Mk = j < 2 ? ml : mh;
-      const uint32_t ps = (j & 1) ? 0x03030202u : 0x01010000u;
-      const uint32_t rb = __builtin_amdgcn_perm(0u, R, ps);
-      const uint32_t mb = __builtin_amdgcn_perm(0u, Mk, ps);
-      // byte selectors of symbol halfword (rank mod 4) in a 2-dword half
-      const uint32_t hs = ((rb & 0x03030303u) << 1) | 0x01000100u;
-      const uint32_t sel = (hs & mb) | (0x0C0C0C0Cu & ~mb);
-      const uint32_t lo = __builtin_amdgcn_perm(a[1], a[0], sel);  // symbols 0..3
-      const uint32_t hi = __builtin_amdgcn_perm(a[3], a[2], sel);  // symbols 4..7
-      const uint32_t hm = ((rb >> 2) & 0x01010101u) * 0xFFu;        // rank >= 4
-      const uint32_t v = (hi & hm) | (lo & ~hm);
-      out[j] |= (v & 0x01FF01FFu) << 7;
-    }
+    const uint32_t lo0 = __builtin_amdgcn_perm(a[1], a[0], 0x06040200u);
+    const uint32_t lo1 = __builtin_amdgcn_perm(a[3], a[2], 0x06040200u);
+    const uint32_t hi0 = __builtin_amdgcn_perm(a[1], a[0], 0x07050301u) & 0x01010101u;
+    const uint32_t hi1 = __builtin_amdgcn_perm(a[3], a[2], 0x07050301u) & 0x01010101u;
+    // byte j of the selectors = rank of weight j (4 + j), or a zero byte
+    const uint32_t sl = (rl & ml) | (0x0C0C0C0Cu & ~ml);
+    const uint32_t sh2 = (rh & mh) | (0x0C0C0C0Cu & ~mh);
+    const uint32_t l4 = __builtin_amdgcn_perm(lo1, lo0, sl), h4 = __builtin_amdgcn_perm(hi1, hi0, sl);
+    const uint32_t l8 = __builtin_amdgcn_perm(lo1, lo0, sh2), h8 = __builtin_amdgcn_perm(hi1, hi0, sh2);
+    // weights 2j, 2j+1: their symbols as the two halves of a dword, moved
+    // above the 7 mantissa bits
+    out[0] |= __builtin_amdgcn_perm(h4, l4, 0x05010400u) << 7;
+    out[1] |= __builtin_amdgcn_perm(h4, l4, 0x07030602u) << 7;
+    out[2] |= __builtin_amdgcn_perm(h8, l8, 0x05010400u) << 7;
+    out[3] |= __builtin_amdgcn_perm(h8, l8, 0x07030602u) << 7;
   }
 }
 
@@ -667,32 +670,201 @@ struct AheadSyms {  // records a prefetched run holds whatever its alignment
   static constexpr uint32_t value = (kAheadRunBytes - 16) / (LAYOUT == WC_LAYOUT_K15 ? 2 : 1);
 };
 
+// The windows of four groups (W dwords each, from LDS byte addresses ad[k],
+// dword-aligned) behind one wait: one LDS round trip instead of four.
+template <int W>
+__device__ inline void lds_read_windows4(const uint32_t ad[4], uint32_t (&w)[4][W]) {
+  static_assert(W == 3 || W == 5, "window sizes of the two layouts");
+  if constexpr (W == 3) {
+    asm volatile(
+        "ds_read_b32 %0, %12\n\tds_read_b32 %1, %12 offset:4\n\tds_read_b32 %2, %12 offset:8\n\t"
+        "ds_read_b32 %3, %13\n\tds_read_b32 %4, %13 offset:4\n\tds_read_b32 %5, %13 offset:8\n\t"
+        "ds_read_b32 %6, %14\n\tds_read_b32 %7, %14 offset:4\n\tds_read_b32 %8, %14 offset:8\n\t"
+        "ds_read_b32 %9, %15\n\tds_read_b32 %10, %15 offset:4\n\tds_read_b32 %11, %15 offset:8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][2]), "=&v"(w[1][0]), "=&v"(w[1][1]),
+          "=&v"(w[1][2]), "=&v"(w[2][0]), "=&v"(w[2][1]), "=&v"(w[2][2]), "=&v"(w[3][0]),
+          "=&v"(w[3][1]), "=&v"(w[3][2])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %20\n\tds_read_b32 %1, %20 offset:4\n\tds_read_b32 %2, %20 offset:8\n\t"
+        "ds_read_b32 %3, %20 offset:12\n\tds_read_b32 %4, %20 offset:16\n\t"
+        "ds_read_b32 %5, %21\n\tds_read_b32 %6, %21 offset:4\n\tds_read_b32 %7, %21 offset:8\n\t"
+        "ds_read_b32 %8, %21 offset:12\n\tds_read_b32 %9, %21 offset:16\n\t"
+        "ds_read_b32 %10, %22\n\tds_read_b32 %11, %22 offset:4\n\tds_read_b32 %12, %22 offset:8\n\t"
+        "ds_read_b32 %13, %22 offset:12\n\tds_read_b32 %14, %22 offset:16\n\t"
+        "ds_read_b32 %15, %23\n\tds_read_b32 %16, %23 offset:4\n\tds_read_b32 %17, %23 offset:8\n\t"
+        "ds_read_b32 %18, %23 offset:12\n\tds_read_b32 %19, %23 offset:16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][2]), "=&v"(w[0][3]), "=&v"(w[0][4]),
+          "=&v"(w[1][0]), "=&v"(w[1][1]), "=&v"(w[1][2]), "=&v"(w[1][3]), "=&v"(w[1][4]),
+          "=&v"(w[2][0]), "=&v"(w[2][1]), "=&v"(w[2][2]), "=&v"(w[2][3]), "=&v"(w[2][4]),
+          "=&v"(w[3][0]), "=&v"(w[3][1]), "=&v"(w[3][2]), "=&v"(w[3][3]), "=&v"(w[3][4])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  }
+}
+
+// Two groups' windows of 5 dwords behind one wait.
+__device__ inline void lds_read_windows2(const uint32_t ad[2], uint32_t (&w)[2][5]) {
+  asm volatile(
+      "ds_read_b32 %0, %10\n\tds_read_b32 %1, %10 offset:4\n\tds_read_b32 %2, %10 offset:8\n\t"
+      "ds_read_b32 %3, %10 offset:12\n\tds_read_b32 %4, %10 offset:16\n\t"
+      "ds_read_b32 %5, %11\n\tds_read_b32 %6, %11 offset:4\n\tds_read_b32 %7, %11 offset:8\n\t"
+      "ds_read_b32 %8, %11 offset:12\n\tds_read_b32 %9, %11 offset:16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][2]), "=&v"(w[0][3]), "=&v"(w[0][4]),
+        "=&v"(w[1][0]), "=&v"(w[1][1]), "=&v"(w[1][2]), "=&v"(w[1][3]), "=&v"(w[1][4])
+      : "v"(ad[0]), "v"(ad[1])
+      : "memory");
+}
+
+// A tile's symbol run ahead of its use, in place of its first records:
+// the 16-byte chunks from the one holding record e0, as many as `cnt`
+// symbols need (the count the escape index gives), at most 66, into
+// buf[768 .. 1032) with the tile's ring loads.  Two global->LDS loads, as
+// many as ring_load_esc issues (each with at least one lane), so the ring's
+// waits stay the same.  Chunks past the stream's padded end re-read its last.
+constexpr uint32_t kRunAheadBytes = 66 * 16;
+template <int LAYOUT>
+struct RunAheadSyms {  // records a run ahead holds whatever its alignment
+  static constexpr uint32_t value = (kRunAheadBytes - 16) / (LAYOUT == WC_LAYOUT_K15 ? 2 : 1);
+};
+template <int LAYOUT>
+__device__ inline void ring_load_run_ahead(const uint8_t* esc_sym, uint64_t sym_last, uint64_t n_esc,
+                                           uint64_t e0, uint64_t cnt, uint32_t* buf) {
+  constexpr uint64_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  const uint32_t lane = (uint32_t)lane_id();
+  uint64_t base = 0, last_chunk = 0;
+  uint32_t nch = 1;
+  if (n_esc) {
+    last_chunk = (4 * (sym_last + 1) - 16) >> 4;  // the padded extent is 16-byte whole
+    const uint64_t b0 = e0 * kSymBytes;
+    base = b0 >> 4;
+    const uint64_t need = ((b0 & 15u) + (cnt < 4096 ? cnt : 4096) * kSymBytes + 15) >> 4;
+    nch = need < kRunAheadBytes / 16 ? (uint32_t)need : kRunAheadBytes / 16;
+    nch = nch ? nch : 1u;
+  }
+  uint64_t c0 = base + lane, c1 = base + kWave + lane;
+  c0 = c0 < last_chunk ? c0 : last_chunk;
+  c1 = c1 < last_chunk ? c1 : last_chunk;
+  if (lane < nch || lane == 0) lds_dma16(esc_sym + 16 * c0, buf + 768);
+  if (lane + kWave < nch || lane == 0) lds_dma16(esc_sym + 16 * c1, buf + 1024);
+}
+
 // Patch a dense tile from its symbol run in LDS (ring_load_symrun, run byte
 // offset off0): each group reads the window that starts at its first record
-// and writes the symbols into its code-15 weights.
-template <int LAYOUT>
+// (byte-split: the four windows in one LDS round trip; K15, whose windows
+// are larger: K15_PASS at a time, fewer where registers are short) and
+// writes the symbols into its code-15 weights.
+template <int LAYOUT, int K15_PASS = 2>
 __device__ inline void patch_tile_symrun(const Lane4& l, uint32_t out[16], const uint32_t* buf,
                                          uint32_t off0) {
+  static_assert(K15_PASS == 1 || K15_PASS == 2, "K15 windows per LDS round trip");
   constexpr int W = WinDwords<LAYOUT>::value;
   constexpr uint32_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  static_assert(kLaneGroups == 4, "four groups per lane");
   uint32_t m[kLaneGroups], c[kLaneGroups], first[kLaneGroups];
   group_records(l, m, c, first);
+  uint32_t o[kLaneGroups], ad[kLaneGroups];
 #pragma unroll
   for (int k = 0; k < kLaneGroups; ++k) {
-    const uint32_t o = off0 + first[k] * kSymBytes;  // < 16 + 4096: the window stays in the slot
-    const uint32_t ad = lds_addr(buf) + (o & ~3u);
-    uint32_t w[W];
-    if constexpr (W == 3) {
-      asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %3 offset:4\n\tds_read_b32 %2, %3 offset:8\n\t"
-                   "s_waitcnt lgkmcnt(0)"
-                   : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]) : "v"(ad) : "memory");
-    } else {
+    o[k] = off0 + first[k] * kSymBytes;  // < 16 + 4096: the window stays in the slot
+    ad[k] = lds_addr(buf) + (o[k] & ~3u);
+  }
+  if constexpr (LAYOUT == WC_LAYOUT_BYTESPLIT) {
+    uint32_t w[kLaneGroups][W];
+    lds_read_windows4<W>(ad, w);
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k)
+      if (c[k]) expand_window<LAYOUT>(m[k], w[k], o[k] & 3u, out + 4 * k);
+  } else if constexpr (K15_PASS == 2) {
+#pragma unroll
+    for (int k0 = 0; k0 < kLaneGroups; k0 += 2) {
+      uint32_t w[2][W];
+      lds_read_windows2(ad + k0, w);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (c[k0 + u]) expand_window<LAYOUT>(m[k0 + u], w[u], o[k0 + u] & 3u, out + 4 * (k0 + u));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kLaneGroups; ++k) {
+      uint32_t w[W];
       asm volatile("ds_read_b32 %0, %5\n\tds_read_b32 %1, %5 offset:4\n\tds_read_b32 %2, %5 offset:8\n\t"
                    "ds_read_b32 %3, %5 offset:12\n\tds_read_b32 %4, %5 offset:16\n\ts_waitcnt lgkmcnt(0)"
-                   : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]) : "v"(ad) : "memory");
+                   : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]) : "v"(ad[k]) : "memory");
+      if (c[k]) expand_window<LAYOUT>(m[k], w, o[k] & 3u, out + 4 * k);
     }
-    if (c[k]) expand_window<LAYOUT>(m[k], w, o & 3u, out + 4 * k);
   }
+}
+
+// A tile with at most kGatherMax escapes in every lane, patched from its
+// symbol run in LDS by rank: the tile's r-th record belongs to its r-th
+// code-15 weight in tile order, so a weight's record is its group's first
+// record (group_records) plus the code-15 weights before it in the group.
+// Each lane reads the symbols of its (at most kGatherMax) escapes from the
+// run, byte address `run` of the tile's first symbol, in one LDS round
+// trip, then ORs them into its staged groups; the stage is written only
+// after the reads have returned, so it may overlap the run.  Per escape this
+// is a few instructions where the window path spends about 80 per group of
+// a K15 tile whatever its marks.
+constexpr int kGatherMax = 4;
+template <int LAYOUT>
+__device__ inline void patch_tile_gather(uint32_t* __restrict__ stage, uint32_t out[16],
+                                         const uint32_t m[kLaneGroups],
+                                         const uint32_t first[kLaneGroups], uint32_t run) {
+  constexpr uint32_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
+  constexpr uint32_t kShift = LAYOUT == WC_LAYOUT_K15 ? 7 : 8;
+  constexpr uint32_t kSymMask = LAYOUT == WC_LAYOUT_K15 ? 0x1FFu : 0xFFu;
+  const uint32_t lane = (uint32_t)lane_id();
+  const uint32_t all = m[0] | (m[1] << 8) | (m[2] << 16) | (m[3] << 24);
+  uint32_t left = all;
+  uint32_t ad[kGatherMax], dst[kGatherMax], sh[kGatherMax];
+  bool ok[kGatherMax];
+#pragma unroll
+  for (int u = 0; u < kGatherMax; ++u) {
+    ok[u] = left != 0;
+    const uint32_t b = ok[u] ? (uint32_t)__builtin_ctz(left) : 0u;  // bit 8k + j: weight j of group k
+    left &= left - 1u;
+    const uint32_t k = b >> 3, j = b & 7u;
+    const uint32_t f = k == 0 ? first[0] : k == 1 ? first[1] : k == 2 ? first[2] : first[3];
+    const uint32_t below = (all >> (b & ~7u)) & ((1u << j) - 1u);  // code-15 weights before j in k
+    ad[u] = run + (f + (uint32_t)__popc(below)) * kSymBytes;
+    const uint32_t p = 8u * (lane + (uint32_t)kWave * k) + j;  // weight in the tile
+    dst[u] = lds_addr(stage) + 4u * (p >> 1);
+    sh[u] = kShift + 16u * (p & 1u);
+  }
+  uint32_t v[kGatherMax];
+  if constexpr (LAYOUT == WC_LAYOUT_K15) {
+    asm volatile("ds_read_u16 %0, %4\n\tds_read_u16 %1, %5\n\tds_read_u16 %2, %6\n\t"
+                 "ds_read_u16 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                 : "memory");
+  } else {
+    asm volatile("ds_read_u8 %0, %4\n\tds_read_u8 %1, %5\n\tds_read_u8 %2, %6\n\t"
+                 "ds_read_u8 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                 : "memory");
+  }
+  uint32_t gmask = 0;
+#pragma unroll
+  for (int k = 0; k < kLaneGroups; ++k) gmask |= (m[k] != 0 ? 1u : 0u) << k;
+  stage_store(stage, out, gmask);
+  wave_lds_sync();
+#pragma unroll
+  for (int u = 0; u < kGatherMax; ++u)
+    if (ok[u]) {
+      const uint32_t w = (v[u] & kSymMask) << sh[u];
+      asm volatile("ds_or_b32 %0, %1" : : "v"(dst[u]), "v"(w) : "memory");
+    }
+  wave_lds_sync();
+  stage_load(stage, out, gmask);
+  wave_lds_sync();  // the stage is reused by this wave's next tile
 }
 
 // Patch a tile from per-group windows.  `e` = index of the tile's first
