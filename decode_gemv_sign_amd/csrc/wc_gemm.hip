@@ -807,31 +807,54 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
 // ---- launchers -----------------------------------------------------------
 
 #ifndef WC_GEMM_SLICES
-#define WC_GEMM_SLICES 8
+#define WC_GEMM_SLICES 0  // waves per block of the fused kernel: 0 = chosen by grid size
+#endif
+
+#ifndef WC_GEMM_PLAIN_SLICES
+#define WC_GEMM_PLAIN_SLICES 4
 #endif
 
 #ifndef WC_GEMM_CONTIG_SLICES
 #define WC_GEMM_CONTIG_SLICES 12
 #endif
 
+// Waves per 16-row block: enough to fill the chip about once, 12 for up to
+// 256 blocks, 8 up to 512, else 4.  Measured at batches 8 and 16 (us, batch
+// 16, against the fixed 8 waves): 4096 x 4096 14.8 against 15.6 (12 waves),
+// 14336 x 4096 43.8 against 48.5 (4 waves); 6144 x 24576 best with 8.
+// The plain kernel takes 4 waves everywhere (5-10% faster than 8 on all
+// four shapes).
+static int mfma_slices(uint64_t rows) {
+  if (WC_GEMM_SLICES) return WC_GEMM_SLICES;
+  const uint64_t blocks = (rows + kMRows - 1) / kMRows;
+  return blocks <= 256 ? 12 : blocks <= 512 ? 8 : 4;
+}
+
 template <int LAYOUT, bool PLAIN>
 static void launch_mfma(const GemmArgs& a, hipStream_t s) {
   const dim3 g((unsigned)((a.rows + kMRows - 1) / kMRows));
-  constexpr int S = WC_GEMM_SLICES;
   constexpr int SC = WC_GEMM_CONTIG_SLICES;
-  // Fused kernel on escape-heavy tensors (more than one weight in 32) whose
-  // rows of whole tiles split evenly over SC waves: contiguous per-wave
-  // ranges with cursors from the escape index, no count exchange.  Measured
-  // on 6144 x 24576 at batches 8 and 16: 6-9% faster on the banded tensor
-  // (5% escapes), 5% slower with 2% escapes, where the exchange costs less
-  // than the smaller grid.
-  if constexpr (!PLAIN) {
-    if (a.cols % ((uint64_t)WC_INDEX_TILE * SC) == 0 && a.n_esc * 32 > a.rows * a.cols) {
+  if constexpr (PLAIN) {
+    constexpr int SP = WC_GEMM_PLAIN_SLICES;
+    hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, true, SP, false>), g, dim3(kWave * SP), 0, s, a);
+  } else {
+    // K15 on escape-heavy tensors (more than one weight in 32) whose rows of
+    // whole tiles split evenly over SC waves: contiguous per-wave ranges
+    // with cursors from the escape index, no count exchange.  Measured on
+    // the 6144 x 24576 banded tensor (5% escapes) at batch 16: 161 against
+    // 194 us interleaved; byte-split there is faster interleaved (118
+    // against 128 us), so it always takes the interleaved ranges.
+    if (LAYOUT == WC_LAYOUT_K15 && a.cols % ((uint64_t)WC_INDEX_TILE * SC) == 0 &&
+        a.n_esc * 32 > a.rows * a.cols) {
       hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, SC, true>), g, dim3(kWave * SC), 0, s, a);
       return;
     }
+    switch (mfma_slices(a.rows)) {
+      case 12: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 12, false>), g, dim3(kWave * 12), 0, s, a); break;
+      case 8: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 8, false>), g, dim3(kWave * 8), 0, s, a); break;
+      default: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 4, false>), g, dim3(kWave * 4), 0, s, a); break;
+    }
   }
-  hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, PLAIN, S, false>), g, dim3(kWave * S), 0, s, a);
 }
 
 static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint32_t batch,
