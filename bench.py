@@ -82,6 +82,8 @@ def parse(argv=None):
                    help="run one 256 MiB device copy first (a known-size kernel for HBM counters)")
     p.add_argument("--bursts", action="store_true",
                    help="print burst timings (decode, fused/plain GEMV, both escape forms)")
+    p.add_argument("--once", action="store_true",
+                   help="with --bursts: launch each kernel once instead (for counter runs)")
     return p.parse_args(argv)
 
 
@@ -928,6 +930,10 @@ def run_bursts(args):
     work = torch.empty(wc.workspace_bytes(max(W.size for W in mats)), dtype=torch.uint8, device=dev)
 
     def burst(fn):
+        if args.once:  # one launch of each kernel, for counter runs
+            fn(0)
+            torch.cuda.synchronize()
+            return float("nan")
         for i in range(3):
             fn(i % copies)
         ts = []
@@ -1124,7 +1130,43 @@ def summarize_trace(stats_csv, md_out, command, bench_json=None):
         fh.write("\n".join(lines) + "\n")
 
 
+def summarize_instructions(pmc_dir, md_out, tiles, command):
+    """Per-kernel instruction counts of a `rocprofv3 --pmc SQ_...` run of
+    `bench.py --bursts --once` (one launch of each kernel per layout and
+    form, in that order): counts per 2048-weight tile of the tensor."""
+    import csv
+    files = [os.path.join(pmc_dir, f) for f in sorted(os.listdir(pmc_dir))
+             if f.endswith("counter_collection.csv")]
+    disp = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+    names = sorted({c for d in disp.values() for c in d if c != "name"})
+    lines = [f"Command: {command}", "",
+             f"Counts per dispatch divided by the tensor's {tiles} tiles of 2048 weights "
+             "(dispatches in launch order: per layout, full then compact form: encode kernels, "
+             "decode, fused GEMV; the plain kernels once per layout).", "",
+             "| dispatch | kernel | " + " | ".join(n + " / tile" for n in names) + " |",
+             "|---|---|" + "---|" * len(names)]
+    for k in sorted(disp):
+        d = disp[k]
+        if not d["name"].startswith(("void wc::k_decode", "wc::k_decode", "void wc::k_gemv",
+                                     "void wc::k_gemm")):
+            continue
+        lines.append(f"| {k} | `{d['name'].split('(')[0]}` | " +
+                     " | ".join(f"{d.get(n, float('nan')) / tiles:.1f}" for n in names) + " |")
+    with open(md_out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-instructions":
+        # bench.py --summarize-instructions PMC_DIR MD_OUT TILES COMMAND
+        a = sys.argv[2:]
+        summarize_instructions(a[0], a[1], int(a[2]), a[3])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         # bench.py --summarize-trace STATS_CSV MD_OUT COMMAND [BENCH_JSON]
         a = sys.argv[2:]
