@@ -135,15 +135,15 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   constexpr int kWinDwords = kK15 ? 17 : 9;  // a lane's symbol window: 32 symbols + alignment
   constexpr int kSymBytes = kK15 ? 2 : 1;
   constexpr int kGroupWin = WinDwords<LAYOUT>::value;  // dwords read per group (8 symbols + alignment)
-  constexpr bool kExpand = !kK15 || CONTIG;  // symbols placed by rank (see the stage below)
   // a lane's window in LDS, with room for a group's read to run past its end
-  constexpr int kWinStride = kExpand ? kWinDwords + kGroupWin - 1 : kWinDwords;
+  constexpr int kWinStride = kWinDwords + kGroupWin - 1;
   __shared__ uint32_t T2[PLAIN ? 1 : 256];
-  // Symbols go in by rank from each group's window (byte-split, and K15 on
-  // escape-heavy tensors), or one record at a time through an LDS stage of
-  // the rebuilt weights (K15 with sparse escapes, where that measured
-  // faster).  The stage also holds the final sums of the S waves.
-  __shared__ __attribute__((aligned(16))) uint32_t stage[S][kWave * (PLAIN || kExpand ? 4 : 16)];
+  // Symbols go in by rank from each group's window.  (K15 once inserted
+  // sparse escapes one record at a time through an LDS stage instead; with
+  // the K15 window placement of wc_tile.h the rank path measured faster:
+  // 14336 x 4096 at batch 16, 66.5 -> 53.9 us.)  The stage holds the final
+  // sums of the S waves.
+  __shared__ __attribute__((aligned(16))) uint32_t stage[S][kWave * 4];
   __shared__ uint32_t win[PLAIN ? 1 : S][PLAIN ? 1 : kWave * kWinStride];
   // escapes per row in each wave's chunk
   __shared__ __attribute__((aligned(16))) uint32_t xcnt[2][kMRows][S];
@@ -306,73 +306,34 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
             for (int u = 0; u < kWinDwords; ++u) wl[u] = wd[u];
           }
-          if constexpr (kExpand) {
-            wave_lds_sync();
-            // Group m's records start fm records into the lane's window (fm =
-            // the escapes of groups 0 .. m-1): read the dwords from the one
-            // holding its first symbol, and place its symbols by rank into
-            // the zero placeholders (as the 1D kernels' dense tiles do).
-            uint32_t fm = 0;
+          wave_lds_sync();
+          // Group m's records start fm records into the lane's window (fm =
+          // the escapes of groups 0 .. m-1): read the dwords from the one
+          // holding its first symbol, and place its symbols by rank into
+          // the zero placeholders (as the 1D kernels' dense tiles do).
+          uint32_t fm = 0;
 #pragma unroll
-            for (int m = 0; m < kLaneGroups; ++m) {
-              const uint32_t gm = (M >> (8 * m)) & 0xFFu;
-              if (__ballot(gm != 0)) {
-                const uint32_t o = off + fm * kSymBytes;  // inside the lane's window
-                const uint32_t ad = lds_addr(wl) + (o & ~3u);
-                uint32_t w[kGroupWin];
-                if constexpr (kGroupWin == 3) {
-                  asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %3 offset:4\n\tds_read_b32 %2, %3 offset:8\n\t"
-                               "s_waitcnt lgkmcnt(0)"
-                               : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]) : "v"(ad) : "memory");
-                } else {
-                  asm volatile("ds_read_b32 %0, %5\n\tds_read_b32 %1, %5 offset:4\n\tds_read_b32 %2, %5 offset:8\n\t"
-                               "ds_read_b32 %3, %5 offset:12\n\tds_read_b32 %4, %5 offset:16\n\ts_waitcnt lgkmcnt(0)"
-                               : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4])
-                               : "v"(ad) : "memory");
-                }
-                if (gm) expand_window<LAYOUT>(gm, w, o & 3u, wv + 4 * m);
+          for (int m = 0; m < kLaneGroups; ++m) {
+            const uint32_t gm = (M >> (8 * m)) & 0xFFu;
+            if (__ballot(gm != 0)) {
+              const uint32_t o = off + fm * kSymBytes;  // inside the lane's window
+              const uint32_t ad = lds_addr(wl) + (o & ~3u);
+              uint32_t w[kGroupWin];
+              if constexpr (kGroupWin == 3) {
+                asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %3 offset:4\n\tds_read_b32 %2, %3 offset:8\n\t"
+                             "s_waitcnt lgkmcnt(0)"
+                             : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]) : "v"(ad) : "memory");
+              } else {
+                asm volatile("ds_read_b32 %0, %5\n\tds_read_b32 %1, %5 offset:4\n\tds_read_b32 %2, %5 offset:8\n\t"
+                             "ds_read_b32 %3, %5 offset:12\n\tds_read_b32 %4, %5 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4])
+                             : "v"(ad) : "memory");
               }
-              fm += (uint32_t)__popc(gm);
+              if (gm) expand_window<LAYOUT>(gm, w, o & 3u, wv + 4 * m);
             }
-            wave_lds_sync();  // the window is rewritten at the next step
-          } else {
-            // one record at a time: the k-th record of the lane goes to its
-            // k-th marked weight, through the LDS stage
-            uint32_t* st = stage[s];
-            const uint32_t gmask = group_mask(marks);
-            stage_store(st, wv, gmask);
-            wave_lds_sync();
-            const uint8_t* wb = (const uint8_t*)wl;
-            for (uint32_t k0 = 0; __ballot(M != 0); k0 += 8) {
-              uint32_t sym[8], wi[8];
-              uint32_t mm = M;
-#pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                wi[u] = mm ? (uint32_t)__builtin_ctz(mm) : 32u;
-                mm &= mm - 1u;
-                const uint32_t p = off + (k0 + u) * kSymBytes;
-                sym[u] = 0;
-                if (wi[u] < 32u)
-                  sym[u] = kK15 ? (uint32_t)(*(const uint16_t*)(wb + p) & 0x1FFu) : (uint32_t)wb[p];
-              }
-              M = mm;
-#pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                if (wi[u] < 32u) {
-                  // weight i = 8 g + e of the lane: stage dword 4 (lane + 64 g) + e / 2
-                  const uint32_t g = wi[u] >> 3, e = wi[u] & 7u;
-                  const uint32_t dw = 4u * ((uint32_t)lane + (uint32_t)kWave * g) + (e >> 1);
-                  if (kK15)
-                    atomicOr(st + dw, (sym[u] << 7) << (16u * (e & 1u)));
-                  else
-                    ((uint8_t*)st)[4u * dw + 2u * (e & 1u) + 1u] = (uint8_t)sym[u];
-                }
-              }
-            }
-            wave_lds_sync();
-            stage_load(st, wv, gmask);
-            wave_lds_sync();
+            fm += (uint32_t)__popc(gm);
           }
+          wave_lds_sync();  // the window is rewritten at the next step
           rebuilt = true;
         }
       }
