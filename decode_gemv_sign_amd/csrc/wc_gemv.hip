@@ -292,11 +292,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
 // wave ends first.  Measured at batch 4 on 6144 x 24576 (4 parts of 3
 // tiles): 82 against 87 us byte-split, 89 against 91 K15; at batch 1 it was
 // slower (57 against 50), so batch 1 keeps whole rows.
-template <int LAYOUT, int B, bool CMP, bool SPLIT>
+template <int LAYOUT, int B, bool CMP, bool SPLIT, uint32_t SLOT = kRingSlotDwords>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) {
+  // 16-byte chunks of symbol run a slot takes ahead (wc_tile.h run_ahead)
+  constexpr uint32_t kAheadChunks = (4 * SLOT - 3104) / 16;
+  static_assert(kAheadChunks >= 66 && kAheadChunks <= 128, "slot sizes of the ring");
+  // symbols such a run holds (the rest of a longer run is loaded once the
+  // tile is in registers)
+  constexpr uint32_t kAheadCap = run_ahead_syms(kAheadChunks, LAYOUT);
   __shared__ uint32_t T2[256];
-  __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][kRingSlotDwords];
-  __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][kRingSlotDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][SLOT];
   __shared__ float part_sum[kBlockThreads / kWave][SPLIT ? B : 1];
   build_pair_table<LAYOUT>(T2, a.dict);
   __syncthreads();
@@ -370,14 +376,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
   load_next(s0, x0);  // in flight while the escape index is read
   load_iv();
-  // With a tile's ring loads go its first records; in the compact form,
-  // which has none, the start of its symbol run instead, as much of it as
-  // the index says the tile holds (the same number of loads either way).
-  // (Taking the run instead of the records also for full-form tiles with
-  // many escapes measured slower: 6144 x 24576 banded, 57.6 against 55.6 us.)
+  // With a tile's ring loads go its first records, or the start of its
+  // symbol run, as much of it as the index says the tile holds (the same
+  // number of loads either way): always in the compact form, which has no
+  // records, and in the byte-split full form for tiles that the index shows
+  // dense and whose run the slot holds whole (a dense tile is patched from
+  // its run, so its records are of no use).  Measured at batch 4: 14336 x
+  // 4096, 37.7 -> 35.7 us; 4096 x 14336, 37.2 -> 33.0.  K15 full-form tiles
+  // measured slower that way (4096 x 4096, batch 1: 10.1 -> 12.7 us).
+  constexpr bool kFullAhead = LAYOUT == WC_LAYOUT_BYTESPLIT;
+  auto run_taken = [&](uint64_t cnt) -> bool {
+    return CMP || (kFullAhead && cnt > kDenseMin && cnt <= kAheadCap);
+  };
   auto load_records = [&](uint64_t e0, uint64_t cnt, uint32_t* buf) {
-    if constexpr (CMP)
-      ring_load_run_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, cnt, buf);
+    if (run_taken(cnt))
+      ring_load_run_ahead<LAYOUT>(a.esc_sym, a.sym_last, a.n_esc, e0, cnt, kAheadChunks, buf);
     else
       ring_load_esc<LAYOUT>(a.esc_pos, a.esc_sym, (CMP ? 0ull : a.n_esc), a.esc_last, e0, buf);
   };
@@ -410,30 +423,39 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
-    // A dense tile is patched from its symbol run: the one that came with
-    // the tile when it fits, else one loaded into the slot now (free: the
-    // tile is in registers).
+    // A tile whose run came with it is patched from there when the run
+    // holds all its escapes (always, unless the container's index and codes
+    // disagree); other dense tiles load their run into the slot now (free:
+    // the tile is in registers); sparse ones use their records.
+    const bool taken = run_taken(entry(q + 1) - e);
     const bool dense = cnt_wave > (CMP ? 0u : kDenseMin);
-    const bool ahead = CMP && cnt_wave <= RunAheadSyms<LAYOUT>::value;
+    const bool ahead = taken && cnt_wave <= kAheadCap;
+    const bool by_run = cnt_wave && (ahead || dense);  // patched from a symbol run
     const uint32_t off0 =
-        dense && !ahead ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
+        by_run && !ahead ? ring_load_symrun<LAYOUT>(a.esc_sym, a.sym_last, e, cnt_wave, buf) : 0u;
     uint32_t w[16];
     rebuild_lane<LAYOUT>(T2, l, w);
-    if (dense && ahead) {
-      const uint32_t off = (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u);
+    if (by_run) {
+      // the run that came with the tile (from dword 768), or the one just
+      // loaded (from dword 0)
+      uint32_t* run = buf;
+      uint32_t off = off0;
+      if (ahead) {
+        run = buf + 768;
+        off = (uint32_t)((e * (LAYOUT == WC_LAYOUT_K15 ? 2u : 1u)) & 15u);
+      } else {
+        wait_vm<0>();
+      }
       uint32_t gm[kLaneGroups], gc[kLaneGroups], gf[kLaneGroups];
       bool few = false;
-      if (kGatherOn && B == 1 && LAYOUT == WC_LAYOUT_K15) {
+      if (kGatherOn && B == 1 && LAYOUT == WC_LAYOUT_K15 && ahead) {
         group_records(l, gm, gc, gf);
         few = !__ballot((gc[0] + gc[1] + gc[2] + gc[3]) > (uint32_t)kGatherMax);
       }
       if (few)
-        patch_tile_gather<LAYOUT>(buf, w, gm, gf, lds_addr(buf + 768) + off);
+        patch_tile_gather<LAYOUT>(buf, w, gm, gf, lds_addr(run) + off);
       else
-        patch_tile_symrun<LAYOUT, kSymPass>(l, w, buf + 768, off);
-    } else if (dense) {
-      wait_vm<0>();
-      patch_tile_symrun<LAYOUT, kSymPass>(l, w, buf, off0);
+        patch_tile_symrun<LAYOUT, kSymPass>(l, w, run, off);
     } else if (cnt_wave) {
       patch_tile<LAYOUT>(buf, w, group_mask(marks), a.esc_pos, a.esc_sym, a.n_esc, a.esc_last, e,
                          cnt_wave, pc.r * a.cols + pc.ct * kTile, kTile, eb);
@@ -691,6 +713,25 @@ static dim3 wave_grid(uint64_t rows, uint64_t rpw) {
   return dim3((unsigned)((waves + wpb - 1) / wpb));
 }
 
+// LDS ring slots of k_decode_gemv_ring.  A 4160-byte slot (4 KB of tile and
+// records, room for a 1056-byte symbol run ahead) lets 4 blocks share a
+// compute unit.  Byte-split at batch 1 on grids of more than one round of
+// such waves, with 8 or more tiles per wave, takes 5152-byte slots instead (3
+// blocks per compute unit): their 2048-byte run ahead holds a tile's symbols
+// even when nearly every weight escapes, so such tiles wait for one load
+// instead of two.  6144 x 24576 with dense escape bands: 55.3 -> 52.6 us;
+// N(0, 0.015): 47.8 -> 47.3.  K15 (more instructions per tile: banded 60.3 ->
+// 62.9 us), batch 4 and short waves (14336 x 4096, 4 tiles per wave: 25.2 ->
+// 27.7 us) measured slower with them.
+#ifndef WC_RING_BIG
+#define WC_RING_BIG 1
+#endif
+constexpr uint32_t kRingBigSlotDwords = 1288;  // 3072 + 2048 + 32 bytes
+static bool ring_big_slots(int layout, uint32_t batch, uint64_t waves, uint64_t tiles_per_wave) {
+  return WC_RING_BIG && layout == WC_LAYOUT_BYTESPLIT && batch == 1 && tiles_per_wave >= 8 &&
+         waves > (uint64_t)cu_count() * 16u;
+}
+
 template <int LAYOUT, bool CMP>
 static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
   GemvArgs a = a0;
@@ -712,6 +753,7 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
       // 4 (or 2) parts of whole tiles, one wave each (see the kernel).
       const uint64_t tpr = a.cols / kTile;
       const uint32_t wpr = b == 4 && tpr > kSplitMinTiles ? (tpr % 4 == 0 ? 4u : tpr % 2 == 0 ? 2u : 1u) : 1u;
+      const uint64_t waves = (a.rows + a.rows_per_wave - 1) / a.rows_per_wave;
       if (wpr > 1) {
         GemvArgs v = p;
         v.wpr = wpr;
@@ -720,6 +762,9 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
         v.cols = a.cols / wpr;
         v.rows_per_wave = 1;
         hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
+      } else if (ring_big_slots(LAYOUT, b, waves, a.rows_per_wave * tpr)) {
+        if constexpr (LAYOUT == WC_LAYOUT_BYTESPLIT)
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, false, kRingBigSlotDwords>), g, t, 0, s, p);
       } else {
         switch (b) {
           case 4: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, false>), g, t, 0, s, p); break;

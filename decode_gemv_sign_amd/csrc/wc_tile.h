@@ -723,18 +723,20 @@ __device__ inline void lds_read_windows2(const uint32_t ad[2], uint32_t (&w)[2][
 
 // A tile's symbol run ahead of its use, in place of its first records:
 // the 16-byte chunks from the one holding record e0, as many as `cnt`
-// symbols need (the count the escape index gives), at most 66, into
-// buf[768 .. 1032) with the tile's ring loads.  Two global->LDS loads, as
-// many as ring_load_esc issues (each with at least one lane), so the ring's
-// waits stay the same.  Chunks past the stream's padded end re-read its last.
-constexpr uint32_t kRunAheadBytes = 66 * 16;
-template <int LAYOUT>
-struct RunAheadSyms {  // records a run ahead holds whatever its alignment
-  static constexpr uint32_t value = (kRunAheadBytes - 16) / (LAYOUT == WC_LAYOUT_K15 ? 2 : 1);
-};
+// symbols need (the count the escape index gives), at most `max_chunks`
+// (<= 128), into the slot from dword 768 on, with the tile's ring loads.  Two
+// global->LDS loads, as many as ring_load_esc issues (each with at least one
+// lane), so the ring's waits stay the same.  Chunks past the stream's padded
+// end re-read its last.  A slot of S bytes holds (S - 3104) / 16 chunks: the
+// run's windows (wc_tile patch paths) read up to 20 bytes past its end.
+__host__ __device__ constexpr uint32_t run_ahead_syms(uint32_t max_chunks, int layout) {
+  // records a run ahead holds whatever its alignment
+  return (16u * max_chunks - 16u) / (layout == WC_LAYOUT_K15 ? 2u : 1u);
+}
 template <int LAYOUT>
 __device__ inline void ring_load_run_ahead(const uint8_t* esc_sym, uint64_t sym_last, uint64_t n_esc,
-                                           uint64_t e0, uint64_t cnt, uint32_t* buf) {
+                                           uint64_t e0, uint64_t cnt, uint32_t max_chunks,
+                                           uint32_t* buf) {
   constexpr uint64_t kSymBytes = LAYOUT == WC_LAYOUT_K15 ? 2 : 1;
   const uint32_t lane = (uint32_t)lane_id();
   uint64_t base = 0, last_chunk = 0;
@@ -744,7 +746,7 @@ __device__ inline void ring_load_run_ahead(const uint8_t* esc_sym, uint64_t sym_
     const uint64_t b0 = e0 * kSymBytes;
     base = b0 >> 4;
     const uint64_t need = ((b0 & 15u) + (cnt < 4096 ? cnt : 4096) * kSymBytes + 15) >> 4;
-    nch = need < kRunAheadBytes / 16 ? (uint32_t)need : kRunAheadBytes / 16;
+    nch = need < max_chunks ? (uint32_t)need : max_chunks;
     nch = nch ? nch : 1u;
   }
   uint64_t c0 = base + lane, c1 = base + kWave + lane;

@@ -253,6 +253,39 @@ def test_clustered_escapes_small(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("form", [0, wc.COMPACT], ids=["full", "compact"])
+def test_gemv_runs_ahead(layout, form):
+    """Tiles whose symbol run comes with their ring loads (every tile of the
+    compact form; byte-split full-form tiles that the index shows dense), in
+    both slot sizes of the ring kernel: 4104 x 16384 (more than one round of
+    waves, 8 tiles per row) takes the large slots at batch 1 and the small
+    ones at batches 2 and 4.  Rows hold 0 to 2048 escapes per tile: graded
+    counts, rows where every weight escapes (runs longer than a slot holds
+    ahead, starting on and off 16-byte boundaries), and uniform rows."""
+    rows, cols = 4104, 16384
+    rng = np.random.default_rng(991)
+    W = synth.random_bits(rows * cols, 990, "normal").reshape(rows, cols)
+    hi = synth.BAND_HIGH_BYTES
+
+    def outliers(n):
+        return (hi[rng.integers(0, hi.size, n)] << 8) | rng.integers(0, 256, n).astype(np.uint16)
+
+    W[1::16] = synth.random_bits(W[1::16].size, 993, "uniform").reshape(-1, cols) & np.uint16(0xBFFF)
+    W[5::512] = outliers(W[5::512].size).reshape(-1, cols)  # too rare for the dictionary
+    counts = np.array([0, 30, 65, 200, 520, 1000, 1500, 2040])
+    for r in range(3, rows, 8):
+        for t, k in enumerate(rng.permutation(counts)):
+            W[r, t * 2048 + rng.choice(2048, k, replace=False)] = outliers(k)
+    x = synth.vectors(992, 4, cols)
+    ref = oracle_gemv(W, x)
+    h, c = wc.encode(dev16(W.reshape(-1)), layout | form)
+    dec = host16(wc.decode(h, c))
+    assert np.array_equal(dec, W.reshape(-1)), "decode"
+    for batch in (1, 2, 4):
+        check_gemv(layout, W, x[:batch], h, c, f"runs ahead form={form} b={batch}", ref=ref)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 def test_gemv_every_batch(layout):
     """Batches 1..16 on shapes with a ragged 16-row block and a partial last
     128-column chunk, and on rows of whole 2048-weight tiles (the LDS-ring
