@@ -304,16 +304,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][SLOT];
   __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][SLOT];
   __shared__ float part_sum[kBlockThreads / kWave][SPLIT ? B : 1];
-  build_pair_table<LAYOUT>(T2, a.dict);
-  __syncthreads();
 
   const int lane = lane_id();
   const int wib = wave_in_block();
   const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wib;
   const uint64_t r0 = wave * a.rows_per_wave;
-  if (!SPLIT && r0 >= a.rows) return;
-  // split rows: every wave of the block reaches the combine below
-  if (!SPLIT || r0 < a.rows) {
+  // Every thread of the block builds its share of the pair table and
+  // reaches the barrier after it (waves without rows, in the else branch);
+  // waves with rows issue their first loads before that.
+  if (r0 < a.rows) {
   const uint64_t r1 = r0 + a.rows_per_wave < a.rows ? r0 + a.rows_per_wave : a.rows;
   const uint64_t gpr = a.cols / kGroup;
   const uint64_t tpr = a.cols / kTile;  // whole tiles
@@ -376,6 +375,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   uint32_t x0[kXpf ? 16 : 1], x1[kXpf ? 16 : 1];
   load_next(s0, x0);  // in flight while the escape index is read
   load_iv();
+  build_pair_table<LAYOUT, true>(T2, a.dict);  // while those loads are in flight
+  __syncthreads();
   // With a tile's ring loads go its first records, or the start of its
   // symbol run, as much of it as the index says the tile holds (the same
   // number of loads either way): always in the compact form, which has no
@@ -496,6 +497,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   }
   if (q < nq) step(q, s0, s1, x0, x1);
   wait_vm<0>();  // the last tile's (unused) record loads land before the wave ends
+  } else {
+    build_pair_table<LAYOUT, true>(T2, a.dict);
+    __syncthreads();
   }
   if constexpr (SPLIT) {
     __syncthreads();

@@ -32,10 +32,27 @@ constexpr int kStageDwords = kTile / 2;             // per-wave LDS stage: one r
 // weight, high nibble = odd weight), holds both weights' symbol bits already
 // in place in a BF16 pair.  Slot 15 of the dictionary is 0 (escape
 // placeholder).
-template <int LAYOUT>
+template <int LAYOUT, bool SELECT = false>
 __device__ inline void build_pair_table(uint32_t* __restrict__ T2, const Dict& d) {
   for (int p = threadIdx.x; p < 256; p += blockDim.x) {
-    const uint32_t lo = d.sym[p & 15], hi = d.sym[p >> 4];
+    uint32_t lo, hi;
+    if constexpr (SELECT) {
+      // the 16 symbols by constant index (scalar loads of the kernel
+      // argument) and a select per lane: no vector-memory load, so a wave
+      // that has issued global->LDS loads builds its share without waiting
+      // for them (the compiler awaits a vector load with vmcnt(0) while
+      // such loads are pending)
+      lo = 0;
+      hi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        lo = (p & 15) == i ? d.sym[i] : lo;
+        hi = (p >> 4) == i ? d.sym[i] : hi;
+      }
+    } else {
+      lo = d.sym[p & 15];
+      hi = d.sym[p >> 4];
+    }
     T2[p] = LAYOUT == WC_LAYOUT_K15 ? (lo << 7) | (hi << 23) : (lo << 8) | (hi << 24);
   }
 }
