@@ -27,13 +27,17 @@
 // Escapes (page "Prueba de GLM-5.2 reduce la memoria BF16 en casi un 25%",
 // section "Cómo funciona la compresión"): the records are in position order,
 // so the records of a lane's weights are one contiguous run of the stream.
-// Each step every wave counts the code-15 marks of its chunk per row and the
+// A chunk's codes arrive two steps before it is multiplied: one step ahead
+// every wave counts the code-15 marks of the next chunk per row and the
 // waves swap these counts through LDS (not needed with contiguous runs);
-// every lane then knows the first record of its own weights (row cursor +
-// counts of the chunks and lanes to its left) and loads the symbols of its
-// run as one window.  Each group of 8 weights then takes its symbols by rank
-// from its part of that window (v_perm selectors, as in the 1D kernels), or,
-// for K15 with sparse escapes, one record at a time through an LDS stage.
+// every lane then knows the first record of its own weights there (row
+// cursor + counts of the chunks and lanes to its left) and issues the load
+// of its run as one window, which arrives with the chunk's raw part and x.
+// Each group of 8 weights then takes its symbols by rank from its part of
+// that window (v_perm selectors, as in the 1D kernels).  Measured at batch
+// 16 against the window loaded within the step: 6144 x 24576 N(0, 0.015)
+// byte-split 107.7 -> 100.0 us, banded 118.3 -> 114.0; 4096 x 14336 44.9
+// -> 40.5.
 // The row cursors start from the escape index: one load for a row that
 // starts on a 2048-weight boundary, else a search of the records of the row
 // start's index tile.
@@ -119,9 +123,12 @@ __device__ inline void lane_of_chunk(const uint32_t c[kLaneGroups], uint32_t cma
 
 template <int LAYOUT, bool PLAIN>
 struct GemmSlot {
-  uint32_t c[kLaneGroups];                                     // codes, group m in c[m]
+  // a lane's symbol window: 32 symbols + alignment
+  static constexpr int kWin = PLAIN ? 1 : (LAYOUT == WC_LAYOUT_K15 ? 17 : 9);
   uint32_t wr[PLAIN ? 16 : (LAYOUT == WC_LAYOUT_K15 ? 7 : 8)];  // raw part, or plain BF16
   uint32_t xv[16];                                             // 32 x values of batch row r
+  uint32_t wd[kWin];  // the step's symbol window (fused), loaded a step ahead
+  uint32_t woff;      // byte of the lane's first record in wd[0]
 };
 
 // CONTIG: wave s takes the contiguous chunks [s * n_steps, (s + 1) * n_steps)
@@ -191,6 +198,7 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
   };
 
   using Slot = GemmSlot<LAYOUT, PLAIN>;
+  // Raw part (or plain BF16 weights) and x of step q into `sl`.
   auto load = [&](uint32_t q, Slot& sl) {
     const uint32_t j = chunk_of(q);
     const uint32_t jc = j < a.chunks ? j : a.chunks - 1;
@@ -214,8 +222,6 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
       }
       return;
     } else {
-      const u32x4 cv = __builtin_nontemporal_load((const u32x4*)(a.codes + base / 2) + le / 32);
-      sl.c[0] = cv[0]; sl.c[1] = cv[1]; sl.c[2] = cv[2]; sl.c[3] = cv[3];
       if constexpr (kK15) {
         const uint32_t* rp = (const uint32_t*)(a.raw + 7 * (base / 8)) + 7 * (le / 32);  // 28 bytes
         const u32x4 v0 = __builtin_nontemporal_load((const u32x4a4*)rp);
@@ -236,75 +242,118 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
       sl.xv[4 * u] = v[0]; sl.xv[4 * u + 1] = v[1]; sl.xv[4 * u + 2] = v[2]; sl.xv[4 * u + 3] = v[3];
     }
   };
+  // Codes of step q (fused), loaded two steps ahead of their rebuild.
+  auto load_codes = [&](uint32_t q, uint32_t c[kLaneGroups]) {
+    const uint32_t j = chunk_of(q);
+    const uint32_t jc = j < a.chunks ? j : a.chunks - 1;
+    const uint64_t base = blk_elt + (uint64_t)jc * kStepCols;
+    // (an offset, not a choice between the two captured values: the
+    // optimizer turns that into a pointer select that keeps the closure,
+    // and what it refers to, in scratch memory)
+    const uint32_t le = lane_elt0 + (lane_ok(q) ? (uint32_t)(kLaneCols * h) : 0u);
+    const u32x4 cv = __builtin_nontemporal_load((const u32x4*)(a.codes + base / 2) + le / 32);
+    c[0] = cv[0]; c[1] = cv[1]; c[2] = cv[2]; c[3] = cv[3];
+  };
 
-  uint64_t e_row = 0;  // escape cursor of row r (set once the searches are done)
+  uint64_t e_row = 0;  // escape cursor of row r: the first record of the next chunk counted
 
-  // One step: rebuild (and patch) the lane's 32 weights of step q from `cur`,
-  // issue step q+1's loads into `nxt`, multiply.
-  auto step = [&](uint32_t q, Slot& cur, Slot& nxt, f32x4& acc) {
+  // The first record of the lane's weights in step q's chunk (row cursor +
+  // escapes of the chunks and lanes to its left), and the lane's escape
+  // count; advances the row cursors past the chunk.  Codes of lanes outside
+  // the rows count no escapes.
+  auto cursor = [&](uint32_t q, const uint32_t c[kLaneGroups], uint32_t& cnt) -> uint64_t {
+    const uint32_t cmask = (lane_ok(q) && row_ok) ? ~0u : 0u;
+    Lane4 l;
+#pragma unroll
+    for (int m = 0; m < kLaneGroups; ++m) l.codes[m] = c[m] & cmask;
+    uint32_t marks[kLaneGroups];
+    escape_marks(l, marks);
+    cnt = count_marks(marks);
+    // escapes of this row in the lanes to the left (same wave), and the row's total
+    const uint32_t c0 = __shfl(cnt, r, kWave), c1 = __shfl(cnt, r + 16, kWave);
+    const uint32_t c2 = __shfl(cnt, r + 32, kWave), c3 = __shfl(cnt, r + 48, kWave);
+    const uint32_t ex = (h > 0 ? c0 : 0u) + (h > 1 ? c1 : 0u) + (h > 2 ? c2 : 0u);
+    uint32_t pre = 0, tot = c0 + c1 + c2 + c3;
+    if constexpr (!CONTIG) {
+      // the chunks of other waves lie between this wave's: swap counts
+      if (h == 0) xcnt[q & 1][r][s] = tot;
+      block_lds_barrier();
+      tot = 0;
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        const uint32_t v = xcnt[q & 1][r][t];
+        pre += t < s ? v : 0u;
+        tot += v;
+      }
+    }
+    const uint64_t e_l = e_row + pre + ex;
+    e_row += tot;
+    return e_l;
+  };
+  // Symbol window of a lane with escapes: the dwords holding records e_l ..
+  // e_l + 31, its end clamped to the stream's padded end (its start may then
+  // fall in the preceding streams of the container, which is harmless).
+  auto load_window = [&](uint64_t e_l, uint32_t cnt, Slot& sl) {
+    if constexpr (!PLAIN) {
+      const int64_t byte = (int64_t)(e_l * kSymBytes);
+      int64_t b = byte >> 2;
+      const int64_t bmax = (int64_t)a.sym_last - (kWinDwords - 1);
+      b = b < bmax ? b : bmax;
+      sl.woff = (uint32_t)(byte - 4 * b);
+      if (cnt != 0) {
+        const uint32_t* sp = (const uint32_t*)a.esc_sym + b;
+#pragma unroll
+        for (int u = 0; u + 4 <= kWinDwords; u += 4) {
+          const u32x4 v = *(const u32x4a4*)(sp + u);
+          sl.wd[u] = v[0]; sl.wd[u + 1] = v[1]; sl.wd[u + 2] = v[2]; sl.wd[u + 3] = v[3];
+        }
+        sl.wd[kWinDwords - 1] = sp[kWinDwords - 1];
+      }
+    }
+  };
+
+  // One step (fused): issue step q+1's raw part and x; rebuild the lane's
+  // 32 weights of step q; issue step q+2's codes into the registers step q's
+  // codes held; count step q+1's escapes and issue its symbol windows; patch
+  // step q's escapes from the windows loaded during the previous step;
+  // multiply.  Every load is thus issued a step (codes: two) before its use.
+  // (Issuing the windows after the patch, so that two steps' windows are not
+  // held at once, saves registers but measured slower: 6144 x 24576 at
+  // batch 16, 120 against 114 us.)
+  // Plain: issue step q+1's loads, multiply.
+  // (always inlined: its slots and code arrays must stay in registers)
+  auto step = [&](uint32_t q, Slot& cur, Slot& nxt, uint32_t cq[kLaneGroups],
+                  const uint32_t cq1[kLaneGroups], f32x4& acc) __attribute__((always_inline)) {
     const bool ok = lane_ok(q);
     // Every lane of the wave is inside its row unless the chunk is the
     // row's partial last one or lies past it (a wave-uniform test); lanes
     // outside contribute zero weights and zero x.
     const bool full = (uint64_t)(chunk_of(q) + 1) * kStepCols <= a.cols;
     const uint32_t cmask = (ok && row_ok) ? ~0u : 0u;  // codes of rows past the end count no escapes
+    load(q + 1, nxt);
     uint32_t wv[16];
-    uint32_t M = 0;
-    bool rebuilt = false;
     if constexpr (!PLAIN) {
-      Lane4 l;
-#pragma unroll
-      for (int m = 0; m < kLaneGroups; ++m) l.codes[m] = cur.c[m] & cmask;
-      uint32_t marks[kLaneGroups];
-      escape_marks(l, marks);
-      const uint32_t cnt = count_marks(marks);
-      if (esc) {
-        M = compress_marks(marks);
-        // escapes of this row in the lanes to the left (same wave), and the row's total
-        const uint32_t c0 = __shfl(cnt, r, kWave), c1 = __shfl(cnt, r + 16, kWave);
-        const uint32_t c2 = __shfl(cnt, r + 32, kWave), c3 = __shfl(cnt, r + 48, kWave);
-        const uint32_t ex = (h > 0 ? c0 : 0u) + (h > 1 ? c1 : 0u) + (h > 2 ? c2 : 0u);
-        uint32_t pre = 0, tot = c0 + c1 + c2 + c3;
-        if constexpr (!CONTIG) {
-          // the chunks of other waves lie between this wave's: swap counts
-          if (h == 0) xcnt[q & 1][r][s] = tot;
-          block_lds_barrier();
-          tot = 0;
-#pragma unroll
-          for (int t = 0; t < S; ++t) {
-            const uint32_t v = xcnt[q & 1][r][t];
-            pre += t < s ? v : 0u;
-            tot += v;
-          }
+      uint32_t M = 0;
+      {
+        Lane4 lr;
+        lane_of_chunk<LAYOUT>(cq, cmask, cur.wr, lr);
+        if (esc) {
+          uint32_t marks[kLaneGroups];
+          escape_marks(lr, marks);
+          M = compress_marks(marks);
         }
-        const uint64_t e_l = e_row + pre + ex;  // first record of this lane's weights
-        e_row += tot;
-        if (__ballot(cnt != 0)) {
-          // symbol window: the dwords holding records e_l .. e_l+31, its end
-          // clamped to the stream's padded end (its start may then fall in
-          // the preceding streams of the container, which is harmless)
-          const int64_t byte = (int64_t)(e_l * kSymBytes);
-          int64_t b = byte >> 2;
-          const int64_t bmax = (int64_t)a.sym_last - (kWinDwords - 1);
-          b = b < bmax ? b : bmax;
-          const uint32_t off = (uint32_t)(byte - 4 * b);
-          uint32_t wd[kWinDwords];
-          if (cnt != 0) {
-            const uint32_t* sp = (const uint32_t*)a.esc_sym + b;
-#pragma unroll
-            for (int u = 0; u + 4 <= kWinDwords; u += 4) {
-              const u32x4 v = *(const u32x4a4*)(sp + u);
-              wd[u] = v[0]; wd[u + 1] = v[1]; wd[u + 2] = v[2]; wd[u + 3] = v[3];
-            }
-            wd[kWinDwords - 1] = sp[kWinDwords - 1];
-          }
-          Lane4 lr;
-          lane_of_chunk<LAYOUT>(l.codes, ~0u, cur.wr, lr);
-          rebuild_lane<LAYOUT>(T2, lr, wv);
+        rebuild_lane<LAYOUT>(T2, lr, wv);
+      }
+      load_codes(q + 2, cq);
+      if (esc) {
+        uint32_t cnt1;
+        const uint64_t e_l1 = cursor(q + 1, cq1, cnt1);
+        load_window(e_l1, cnt1, nxt);
+        if (__ballot(M != 0)) {
           uint32_t* wl = win[s] + lane * kWinStride;
-          if (cnt != 0) {
+          if (M != 0) {
 #pragma unroll
-            for (int u = 0; u < kWinDwords; ++u) wl[u] = wd[u];
+            for (int u = 0; u < kWinDwords; ++u) wl[u] = cur.wd[u];
           }
           wave_lds_sync();
           // Group m's records start fm records into the lane's window (fm =
@@ -316,7 +365,7 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
           for (int m = 0; m < kLaneGroups; ++m) {
             const uint32_t gm = (M >> (8 * m)) & 0xFFu;
             if (__ballot(gm != 0)) {
-              const uint32_t o = off + fm * kSymBytes;  // inside the lane's window
+              const uint32_t o = cur.woff + fm * kSymBytes;  // inside the lane's window
               const uint32_t ad = lds_addr(wl) + (o & ~3u);
               uint32_t w[kGroupWin];
               if constexpr (kGroupWin == 3) {
@@ -334,43 +383,41 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
             fm += (uint32_t)__popc(gm);
           }
           wave_lds_sync();  // the window is rewritten at the next step
-          rebuilt = true;
         }
       }
     }
-    load(q + 1, nxt);
-    if constexpr (!PLAIN) {
-      if (!rebuilt) {
-        Lane4 lr;
-        lane_of_chunk<LAYOUT>(cur.c, cmask, cur.wr, lr);
-        rebuild_lane<LAYOUT>(T2, lr, wv);
-      }
-    }
-    // Operands of blocks past the row end are zeroed with masks rather than
-    // skipped, so the four products are issued on every path (no branch
-    // joins between matrix-core results).
-    const uint32_t* wsrc = PLAIN ? cur.wr : wv;
-    uint32_t wm[16], xm[16];
+    // Operands of blocks past the row end are zeroed in place with masks
+    // rather than skipped, so the four products are issued on every path (no
+    // branch joins between matrix-core results).
+    uint32_t* wsrc = PLAIN ? cur.wr : wv;
+    if (!full) {
 #pragma unroll
-    for (int m = 0; m < kLaneGroups; ++m) {
-      const uint32_t km = PLAIN ? (block_ok(q, m) ? ~0u : 0u) : (ok ? ~0u : 0u);
+      for (int m = 0; m < kLaneGroups; ++m) {
+        const uint32_t km = PLAIN ? (block_ok(q, m) ? ~0u : 0u) : (ok ? ~0u : 0u);
 #pragma unroll
-      for (int k = 4 * m; k < 4 * m + 4; ++k) {
-        wm[k] = full ? wsrc[k] : wsrc[k] & km;
-        xm[k] = full ? cur.xv[k] : cur.xv[k] & km;
+        for (int k = 4 * m; k < 4 * m + 4; ++k) {
+          wsrc[k] &= km;
+          cur.xv[k] &= km;
+        }
       }
     }
 #pragma unroll
-    for (int m = 0; m < kLaneGroups; ++m) acc = mfma_bf16(wm + 4 * m, xm + 4 * m, acc);
+    for (int m = 0; m < kLaneGroups; ++m) acc = mfma_bf16(wsrc + 4 * m, cur.xv + 4 * m, acc);
   };
 
   // Two register sets alternate, each with its own accumulator (so no
   // accumulator is copied inside the loop); an odd last step runs after the
   // loop, so no path leaves the loop body half-way (which would make the
-  // compiler wait for the prefetch at the loop head).
+  // compiler wait for the prefetch at the loop head).  The codes of steps q
+  // and q+1 sit in cA and cB (cA then takes step q+2's).
   f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
   Slot s0, s1;
+  uint32_t cA[kLaneGroups], cB[kLaneGroups];
   load(0, s0);  // in flight while the row cursors are read
+  if constexpr (!PLAIN) {
+    load_codes(0, cA);
+    load_codes(1, cB);
+  }
   if constexpr (CONTIG) {
     // Row cursors at this wave's first column: lane rr reads row rr's
     // escape-index entry (rows past the matrix read the closing entry).
@@ -399,11 +446,17 @@ __global__ __launch_bounds__(kWave * S) void k_gemm_mfma(GemmArgs a) {
     block_lds_barrier();  // pair table and cursors (the first loads stay in flight)
     e_row = esc ? erow0[r] : 0;
   }
-  for (uint32_t q = 0; q + 1 < n_steps; q += 2) {
-    step(q, s0, s1, acc0);
-    step(q + 1, s1, s0, acc1);
+  if (esc) {
+    // step 0's windows
+    uint32_t cnt0;
+    const uint64_t e_l0 = cursor(0, cA, cnt0);
+    load_window(e_l0, cnt0, s0);
   }
-  if (n_steps & 1u) step(n_steps - 1, s0, s1, acc0);
+  for (uint32_t q = 0; q + 1 < n_steps; q += 2) {
+    step(q, s0, s1, cA, cB, acc0);
+    step(q + 1, s1, s0, cB, cA, acc1);
+  }
+  if (n_steps & 1u) step(n_steps - 1, s0, s1, cA, cB, acc0);
   // Matrix-core results are read by vector instructions only after this
   // many idle cycles (more than the longest product needs to retire).
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc0), "+v"(acc1));
@@ -779,16 +832,20 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
 #define WC_GEMM_CONTIG_SLICES 12
 #endif
 
-// Waves per 16-row block: enough to fill the chip about once, 12 for up to
-// 256 blocks, 8 up to 512, else 4.  Measured at batches 8 and 16 (us, batch
-// 16, against the fixed 8 waves): 4096 x 4096 14.8 against 15.6 (12 waves),
-// 14336 x 4096 43.8 against 48.5 (4 waves); 6144 x 24576 best with 8.
-// The plain kernel takes 4 waves everywhere (5-10% faster than 8 on all
-// four shapes).
-static int mfma_slices(uint64_t rows) {
+// Waves per 16-row block.  The fused kernel holds three waves per SIMD (its
+// registers), so blocks of 12, 6 or 4 waves pack a compute unit whole.
+// Measured at batches 8 and 16 (us at batch 16, 12 / 6 / 4 waves):
+// byte-split 4096 x 4096 14.6 / 14.0 / 14.0, 4096 x 14336 40.6 / 40.5 /
+// 45.1, 6144 x 24576 banded 116.8 / 114.0 / 116.1, 14336 x 4096 54.7 /
+// 54.0 / 40.9; K15 4096 x 4096 18.2 / 18.2 / 19.3, 4096 x 14336 49.6 / 48.7 /
+// 53.5, 6144 x 24576 N(0, 0.015) 140.5 / 151.5 / 138.5, 14336 x 4096 67.3 /
+// 66.7 / 53.0.  The plain kernel takes 4 waves everywhere (5-10% faster
+// than 8 on all four shapes).
+static int mfma_slices(int layout, uint64_t rows) {
   if (WC_GEMM_SLICES) return WC_GEMM_SLICES;
   const uint64_t blocks = (rows + kMRows - 1) / kMRows;
-  return blocks <= 256 ? 12 : blocks <= 512 ? 8 : 4;
+  if (layout == WC_LAYOUT_K15) return blocks <= 256 ? 12 : 4;
+  return blocks <= 512 ? 6 : 4;
 }
 
 template <int LAYOUT, bool PLAIN>
@@ -810,9 +867,9 @@ static void launch_mfma(const GemmArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, SC, true>), g, dim3(kWave * SC), 0, s, a);
       return;
     }
-    switch (mfma_slices(a.rows)) {
+    switch (mfma_slices(LAYOUT, a.rows)) {
       case 12: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 12, false>), g, dim3(kWave * 12), 0, s, a); break;
-      case 8: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 8, false>), g, dim3(kWave * 8), 0, s, a); break;
+      case 6: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 6, false>), g, dim3(kWave * 6), 0, s, a); break;
       default: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 4, false>), g, dim3(kWave * 4), 0, s, a); break;
     }
   }
