@@ -606,7 +606,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
       bb = bb < a.batch ? bb : a.batch - 1;
       const uint16_t* src =
           a.x + (uint64_t)bb * a.cols + col0 + (uint64_t)j * kStepCols + 8u * (uint32_t)(r ^ q);
-      lds_dma16(src, (uint32_t*)(dst + 1024 * i));
+      lds_dma16_keep(src, (uint32_t*)(dst + 1024 * i));  // x: read by the other batch groups' blocks too
     }
   };
 
@@ -829,7 +829,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
 #endif
 
 #ifndef WC_GEMM_CONTIG_SLICES
-#define WC_GEMM_CONTIG_SLICES 12
+#define WC_GEMM_CONTIG_SLICES 4
 #endif
 
 // Waves per 16-row block.  The fused kernel holds three waves per SIMD (its
@@ -859,9 +859,10 @@ static void launch_mfma(const GemmArgs& a, hipStream_t s) {
     // K15 on escape-heavy tensors (more than one weight in 32) whose rows of
     // whole tiles split evenly over SC waves: contiguous per-wave ranges
     // with cursors from the escape index, no count exchange.  Measured on
-    // the 6144 x 24576 banded tensor (5% escapes) at batch 16: 161 against
-    // 194 us interleaved; byte-split there is faster interleaved (118
-    // against 128 us), so it always takes the interleaved ranges.
+    // the 6144 x 24576 banded tensor (5% escapes) at batch 16: 150 us with
+    // 4 waves, 158 with 12, 158 interleaved; byte-split there is faster
+    // interleaved (114 against 119 us with 4 contiguous waves), so it always
+    // takes the interleaved ranges.
     if (LAYOUT == WC_LAYOUT_K15 && a.cols % ((uint64_t)WC_INDEX_TILE * SC) == 0 &&
         a.n_esc * 32 > a.rows * a.cols) {
       hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, SC, true>), g, dim3(kWave * SC), 0, s, a);
