@@ -175,11 +175,14 @@ typedef const __attribute__((address_space(1))) void glb_void_t;
 // 16 bytes per lane from `src` (per lane) into LDS at dst + 16 * lane (dst
 // wave-uniform).  Completion is counted by vmcnt; the compiler does not
 // track the LDS write, so readers wait explicitly (wait_vm).  lds_dma16
-// marks the load non-temporal (cache policy bit 1): the coded streams are
-// read once, and so leave the caches to what is reused (x).  Measured on
-// 6144 x 24576: batch-1 fused GEMV 51.9 -> 50.2 us byte-split, 60.9 -> 58.8
-// K15; decode 91.5 -> 87.3 us K15.  lds_dma16_keep, for data that other
-// waves read again, keeps the default policy.
+// marks the load non-temporal (cache policy bit 1): a tile's codes and raw
+// part are read once, and so leave the caches to what is reused (x).
+// Measured on 6144 x 24576: batch-1 fused GEMV 51.9 -> 50.2 us byte-split,
+// 60.9 -> 58.8 K15; decode 91.5 -> 87.3 us K15.  lds_dma16_keep keeps the
+// default policy, for data that other waves read again: x, and symbol runs,
+// whose first and last 16-byte chunks the neighbouring tiles load too (taken
+// non-temporal, the compact-form decode of 4096 x 4096 went from 10.9 to
+// 15.9 us).
 __device__ inline void lds_dma16(const void* src, uint32_t* dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 2);
 }

@@ -650,7 +650,7 @@ __device__ inline uint32_t ring_load_symrun(const uint8_t* esc_sym, uint64_t sym
     if (c0 + lane < nch) {
       uint64_t ch = (base >> 4) + c0 + lane;
       ch = ch < last_chunk ? ch : last_chunk;
-      lds_dma16(esc_sym + 16 * ch, buf + 4 * c0);
+      lds_dma16_keep(esc_sym + 16 * ch, buf + 4 * c0);
     }
   }
   return (uint32_t)(b0 - base);
@@ -678,8 +678,8 @@ __device__ inline void ring_load_symrun_ahead(const uint8_t* esc_sym, uint64_t s
     c1 = c1 < last_chunk ? c1 : last_chunk;
   }
   if (lane < 16) {
-    lds_dma16(esc_sym + 16 * c0, buf + 768);
-    lds_dma16(esc_sym + 16 * c1, buf + 832);
+    lds_dma16_keep(esc_sym + 16 * c0, buf + 768);
+    lds_dma16_keep(esc_sym + 16 * c1, buf + 832);
   }
 }
 template <int LAYOUT>
@@ -769,8 +769,8 @@ __device__ inline void ring_load_run_ahead(const uint8_t* esc_sym, uint64_t sym_
   uint64_t c0 = base + lane, c1 = base + kWave + lane;
   c0 = c0 < last_chunk ? c0 : last_chunk;
   c1 = c1 < last_chunk ? c1 : last_chunk;
-  if (lane < nch || lane == 0) lds_dma16(esc_sym + 16 * c0, buf + 768);
-  if (lane + kWave < nch || lane == 0) lds_dma16(esc_sym + 16 * c1, buf + 1024);
+  if (lane < nch || lane == 0) lds_dma16_keep(esc_sym + 16 * c0, buf + 768);
+  if (lane + kWave < nch || lane == 0) lds_dma16_keep(esc_sym + 16 * c1, buf + 1024);
 }
 
 // Patch a dense tile from its symbol run in LDS (ring_load_symrun, run byte
