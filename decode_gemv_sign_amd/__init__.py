@@ -207,7 +207,7 @@ def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
 
 def workspace_bytes(n: int) -> int:
     """WC_WORKSPACE_BYTES(n)."""
-    return 20512 + (8 + 2 * STAGE_SYMBOLS) * ((n + 8191) // 8192)
+    return 20528 + (16 + 6 * STAGE_SYMBOLS) * ((n + 8191) // 8192)
 
 
 def _workspace(n: int, device) -> torch.Tensor:

@@ -199,11 +199,14 @@ hipError_t launch_build_dict(int layout, const uint16_t* w, uint64_t n, uint8_t*
 // The escape records of the tensor are in weight order: block b's first
 // record is the number of escapes in blocks 0 .. b-1.  k_pack counts each
 // block's escapes; k_scan turns the counts into those prefix sums; k_emit
-// writes each block's records from there.  The records need the escaped
-// symbols, which the code stream does not hold: k_pack stages them (in
-// weight order, u16 each) for every block with at most `stage_cap` escapes,
-// so k_emit reads them back instead of the weights; only a block with more
-// escapes (a dense escape band) has its weights read again, in whole lines.
+// writes each block's records from there.  For every block with at most
+// `stage_cap` escapes k_pack stages the records themselves in the workspace
+// (in weight order: the symbols as u16, the positions as u32, and the
+// block's four per-tile counts), so k_emit copies them to their place in
+// whole lines and reads neither the codes nor the weights again.  A block
+// with more escapes (a dense escape band), or any block when nothing is
+// staged (wc_encode_noalloc), has its codes and the weights of its escapes
+// read again.
 
 constexpr uint32_t kDirectRecords = 256;  // blocks with more records write them through LDS
 
@@ -260,8 +263,10 @@ __device__ inline BlockEsc block_escape_scan(const uint32_t emask[4], uint32_t (
 struct PackArgs {
   const uint16_t* w;
   uint8_t* container;
-  uint32_t* cnt;      // per-block escape counts
-  uint16_t* stage;    // stage_cap symbols per block
+  uint32_t* cnt;        // per-block escape counts
+  uint16_t* tcnt;       // staged blocks: escape counts of the block's 4 tiles
+  uint16_t* stage;      // stage_cap symbols per block
+  uint32_t* stage_pos;  // stage_cap positions per block (full form)
   uint32_t stage_cap;
   uint64_t n;
   wc_header h;
@@ -362,15 +367,20 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
     const uint32_t total = be.total();
     if (tid == 0) a.cnt[blk] = total;
     if (total != 0 && total <= a.stage_cap) {
-      // the block's escaped symbols, in weight order
+      // the block's records, in weight order, and its tiles' counts
       uint16_t* st = a.stage + blk * a.stage_cap;
+      uint32_t* sp = a.stage_pos + blk * a.stage_cap;
+      const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
+      if (tid < 4) a.tcnt[4u * blk + tid] = (uint16_t)be.tile(tid);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t m = emask[j];
         uint32_t o = be.tile_base(j) + be.ex(j);
+        const uint64_t gw = w0 + 8u * (uint64_t)(tid + kBlockThreads * j);
         while (m) {
           const int i = __builtin_ctz(m);
           m &= m - 1u;
+          if (!compact) sp[o] = (uint32_t)(gw + (uint64_t)i);
           st[o++] = (uint16_t)(((wd[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) >> kShift);
         }
       }
@@ -484,7 +494,9 @@ struct EmitArgs {
   uint8_t* container;
   const uint32_t* cnt;
   const uint32_t* off;
+  const uint16_t* tcnt;
   const uint16_t* stage;
+  const uint32_t* stage_pos;
   uint32_t stage_cap;
   uint64_t n;
   wc_header h;
@@ -510,6 +522,29 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
     if (tid < 4 && 4u * blk + (uint64_t)tid < n_tiles) index[4u * blk + tid] = excl;
     return;
   }
+  uint32_t* pos = (uint32_t*)(a.container + h.off_esc_pos);
+  uint8_t* sym = a.container + h.off_esc_sym;
+  const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
+  if (cntb <= a.stage_cap) {  // block-uniform: the records k_pack staged, copied in order
+    if (tid < 4 && 4u * blk + (uint64_t)tid < n_tiles) {
+      uint32_t base = 0;
+      for (int q = 0; q < tid; ++q) base += a.tcnt[4u * blk + q];
+      index[4u * blk + tid] = excl + base;
+    }
+    const uint16_t* st = a.stage + blk * a.stage_cap;
+    const uint32_t* sp = a.stage_pos + blk * a.stage_cap;
+    for (uint32_t q = (uint32_t)tid; q < cntb; q += kBlockThreads) {
+      const uint64_t o = (uint64_t)excl + q;
+      if (o < h.n_esc) {
+        if (!compact) pos[o] = sp[q];
+        if (LAYOUT == WC_LAYOUT_K15)
+          ((uint16_t*)sym)[o] = st[q];
+        else
+          sym[o] = (uint8_t)st[q];
+      }
+    }
+    return;
+  }
   // the block's codes, in k_pack's group mapping; codes past n are 0
   const uint32_t* codes = (const uint32_t*)(a.container + h.off_codes) + w0 / 8;
   uint32_t emask[4];
@@ -521,30 +556,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
   }
   const BlockEsc be = block_escape_scan(emask, wtot);
   if (tid < 4 && 4u * blk + (uint64_t)tid < n_tiles) index[4u * blk + tid] = excl + be.tile_base(tid);
-  // the escaped symbols: staged by k_pack, or from the weights again
-  const bool staged = cntb <= a.stage_cap;
-  const uint16_t* st = a.stage + blk * a.stage_cap;
+  // the escaped symbols, from the weights again
   uint32_t wd[4][4];
-  if (!staged) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wd[j][0] = wd[j][1] = wd[j][2] = wd[j][3] = 0;
-      if (!emask[j]) continue;
-      const uint64_t gw = w0 + 8u * (uint64_t)(tid + kBlockThreads * j);
-      if (gw + 8 <= a.n) {
-        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + gw));
-        wd[j][0] = v[0]; wd[j][1] = v[1]; wd[j][2] = v[2]; wd[j][3] = v[3];
-      } else {
-        for (int i = 0; gw + i < a.n; ++i) wd[j][i >> 1] |= (uint32_t)a.w[gw + i] << (16 * (i & 1));
-      }
+  for (int j = 0; j < 4; ++j) {
+    wd[j][0] = wd[j][1] = wd[j][2] = wd[j][3] = 0;
+    if (!emask[j]) continue;
+    const uint64_t gw = w0 + 8u * (uint64_t)(tid + kBlockThreads * j);
+    if (gw + 8 <= a.n) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + gw));
+      wd[j][0] = v[0]; wd[j][1] = v[1]; wd[j][2] = v[2]; wd[j][3] = v[3];
+    } else {
+      for (int i = 0; gw + i < a.n; ++i) wd[j][i >> 1] |= (uint32_t)a.w[gw + i] << (16 * (i & 1));
     }
   }
-  auto sym_at = [&](int j, int i, uint32_t rank) -> uint32_t {
-    return staged ? (uint32_t)st[rank] : ((wd[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) >> kShift;
+  auto sym_at = [&](int j, int i, uint32_t) -> uint32_t {
+    return ((wd[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) >> kShift;
   };
-  uint32_t* pos = (uint32_t*)(a.container + h.off_esc_pos);
-  uint8_t* sym = a.container + h.off_esc_sym;
-  const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
   if (cntb <= kDirectRecords) {
     // few records: each thread stores its own
 #pragma unroll
@@ -602,7 +630,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
 }
 
 // Encode with the block state at `state` (16-byte aligned: counts, offsets,
-// then the symbol stage of `stage_cap` u16 per block, which may be 0).
+// then, when stage_cap > 0, per block 4 u16 tile counts, stage_cap u16
+// symbols and stage_cap u32 positions).
 static hipError_t launch_encode_state(const wc_header& h, const uint16_t* w, uint8_t* container,
                                       uint8_t* state, uint32_t stage_cap, hipStream_t s) {
   if (h.layout == WC_LAYOUT_RAW) return launch_encode_raw(h, w, container, s);
@@ -611,12 +640,17 @@ static hipError_t launch_encode_state(const wc_header& h, const uint16_t* w, uin
   const uint64_t nblk4 = (nblk + 3) & ~(uint64_t)3;
   uint32_t* cnt = (uint32_t*)state;
   uint32_t* off = cnt + nblk4;
-  uint16_t* stage = (uint16_t*)(state + 8u * nblk4);
+  uint16_t* tcnt = stage_cap ? (uint16_t*)(state + 8u * nblk4) : nullptr;
+  uint16_t* stage = stage_cap ? (uint16_t*)(state + 16u * nblk4) : nullptr;
+  uint32_t* stage_pos =
+      stage_cap ? (uint32_t*)(state + 16u * nblk4 + 2u * (uint64_t)stage_cap * nblk) : nullptr;
   PackArgs p;
   p.w = w;
   p.container = container;
   p.cnt = cnt;
+  p.tcnt = tcnt;
   p.stage = stage;
+  p.stage_pos = stage_pos;
   p.stage_cap = stage_cap;
   p.n = h.n;
   p.h = h;
@@ -635,7 +669,9 @@ static hipError_t launch_encode_state(const wc_header& h, const uint16_t* w, uin
   e.container = container;
   e.cnt = cnt;
   e.off = off;
+  e.tcnt = tcnt;
   e.stage = stage;
+  e.stage_pos = stage_pos;
   e.stage_cap = stage_cap;
   e.n = h.n;
   e.h = h;
@@ -656,7 +692,8 @@ hipError_t launch_encode(const wc_header& h, const uint16_t* w, uint8_t* contain
 // fixed device array of the library, one per GPU, held until the process
 // ends, sized for the largest tensor taken (WC_NOALLOC_MAX_N weights, 8
 // bytes per 8192-weight block).  Nothing is staged there, so k_emit reads
-// the weights of every block with escapes again; the container is the same.
+// the codes and weights of every block with escapes again; the container is
+// the same.
 // In host code the array's name stands for a host-side symbol, not a device
 // address: its device address is looked up once per device and only that
 // address reaches the kernels.  Every call rewrites the counts and offsets

@@ -98,13 +98,14 @@ extern "C" {
 #define WC_FLAG_COMPACT 1u
 #define WC_COMPACT 0x10
 
-/* Scratch bytes wc_build_dict and wc_encode need for n weights: 20512, plus
- * 8 per 8192-weight block for its escape count and first record, plus
- * 2 * WC_STAGE_SYMBOLS per block, where encode stages the escaped symbols of
- * blocks that have at most WC_STAGE_SYMBOLS of them (0.063 bytes/weight). */
+/* Scratch bytes wc_build_dict and wc_encode need for n weights: 20528, plus
+ * 16 per 8192-weight block for its escape count, first record and tile
+ * counts, plus 6 * WC_STAGE_SYMBOLS per block, where encode stages the
+ * escape records (2-byte symbol, 4-byte position) of blocks that have at
+ * most WC_STAGE_SYMBOLS of them (0.19 bytes/weight). */
 #define WC_STAGE_SYMBOLS 256u
 #define WC_WORKSPACE_BYTES(n) \
-  ((size_t)20512 + (size_t)(8u + 2u * WC_STAGE_SYMBOLS) * (((uint64_t)(n) + 8191u) / 8192u))
+  ((size_t)20528 + (size_t)(16u + 6u * WC_STAGE_SYMBOLS) * (((uint64_t)(n) + 8191u) / 8192u))
 
 /* The first 128 bytes of every container, byte for byte. */
 typedef struct wc_header {

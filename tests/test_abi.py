@@ -138,7 +138,7 @@ def test_workspace_formula(wc, tmp_path):
     got = [int(v) for v in subprocess.check_output([str(exe)], text=True).split()]
     assert got == [wc.workspace_bytes(n) for n in ns]
     # counts and offsets (8 bytes) plus the symbol stage per 8192-weight block
-    assert wc.workspace_bytes(8192) - wc.workspace_bytes(0) == 8 + 2 * wc.STAGE_SYMBOLS
+    assert wc.workspace_bytes(8192) - wc.workspace_bytes(0) == 16 + 6 * wc.STAGE_SYMBOLS
 
 
 def test_header_struct_layout(wc):
