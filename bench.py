@@ -49,7 +49,7 @@ METRIC = ("decoded BF16 GB/s (% HBM peak); fused decode-GEMV µs vs BF16 GEMV; "
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 LAYOUT_NAMES = {0: "byte-split", 1: "K15"}
 WORKSET_BYTES = 512 << 20  # rotate copies until the inputs span 2x the 256 MB cache
-ENC_THREADS = 4  # layer set: host threads (one stream each) that encode tensors side by side
+ENC_THREADS = 2  # layer set: host threads (one stream each) that encode tensors side by side
 CPU_THREADS_MAX = 16  # the host-core share of one GPU
 BURST = 20  # back-to-back launches per timed burst
 GEMV_BATCHES = (1, 4, 16)

@@ -286,14 +286,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
   const bool with_esc = h.n_esc != 0;
   for (int sidx = tid; sidx < 512; sidx += kBlockThreads) lut[sidx] = 15;
   for (int q = tid; q < kGroups; q += kBlockThreads) img_codes[q] = 0;
-  for (int q = tid; q < kRawBytes / 4; q += kBlockThreads) img_raw[q] = 0;
+  if (LAYOUT == WC_LAYOUT_BYTESPLIT)  // (the K15 image is written whole below)
+    for (int q = tid; q < kRawBytes / 4; q += kBlockThreads) img_raw[q] = 0;
   __syncthreads();
   if (tid < (int)h.n_dict) lut[h.dict[tid]] = (uint8_t)tid;
   __syncthreads();
 
   const uint64_t blk = blockIdx.x;
   const uint64_t w0 = blk * kPackBlock;  // first weight of the block
-  uint8_t* rimg = (uint8_t*)img_raw;
   // a full block (every block but possibly the last) loads its four groups at once
   const bool full = w0 + kPackBlock <= a.n;
   uint32_t wd[4][4];  // per group: weights 2i (low half) and 2i+1 (high half)
@@ -312,8 +312,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
     emask[j] = 0;
     if (!full) {
       wd[j][0] = wd[j][1] = wd[j][2] = wd[j][3] = 0;
-      if (gw >= a.n) continue;
-      const uint32_t valid = a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
+      const uint32_t valid = gw >= a.n ? 0u : a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
       if (valid == 8) {
         const u32x4 v = __builtin_nontemporal_load((const u32x4*)(a.w + gw));
         wd[j][0] = v[0]; wd[j][1] = v[1]; wd[j][2] = v[2]; wd[j][3] = v[3];
@@ -326,7 +325,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
         }
       }
     }
-    const uint32_t valid = a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
+    // (a group past n has no valid weights: zero codes and raw bytes)
+    const uint32_t valid = gw >= a.n ? 0u : a.n - gw >= 8 ? 8u : (uint32_t)(a.n - gw);
     // codes: nibble i = code of weight i (even weight in the low nibble)
     uint32_t cd = 0;
 #pragma unroll
@@ -349,15 +349,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_pack(PackArgs a) {
       img_raw[2 * g] = r0;
       img_raw[2 * g + 1] = r1;
     } else {
-      // 8 mantissas of 7 bits = 56 bits, LSB first, at byte 7g of the image
+      // The group's 8 mantissas of 7 bits (56 bits, LSB first) go to byte
+      // 7g of the image.  Eight consecutive groups (lanes 8s..8s+7) fill 56
+      // bytes = 7 aligned u64 words; word k of them is bits [8k, 8k+64) of
+      // the lane-k and lane-(k+1) values side by side, so lanes 0..6 of each
+      // eight store one word each, with their right neighbour's value from a
+      // row shift.  (Every lane reaches this point: no divergence.)
       uint64_t m = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint64_t mi = (uint32_t)i < valid ? (wd[j][i >> 1] >> (16 * (i & 1))) & 0x7Fu : 0u;
         m |= mi << (7 * i);
       }
-#pragma unroll
-      for (int k = 0; k < 7; ++k) rimg[7 * g + k] = (uint8_t)(m >> (8 * k));
+      const uint32_t nlo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)m, 0x101, 0xF, 0xF, false);  // row_shl:1
+      const uint32_t nhi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(m >> 32), 0x101, 0xF, 0xF, false);
+      const uint64_t nxt = (uint64_t)nlo | ((uint64_t)nhi << 32);
+      const int l8 = tid & 7;
+      if (l8 < 7) ((uint64_t*)img_raw)[7 * (g >> 3) + l8] = (m >> (8 * l8)) | (nxt << (56 - 8 * l8));
     }
   }
 
@@ -488,6 +496,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t* __restric
 }
 
 // ---- escape records ---------------------------------------------------------
+// A workgroup covers `group` consecutive encode blocks (kEmitMax when the
+// escapes are sparse, so the grid is small and each workgroup's loads are in
+// flight together; 1 when they average more than a stage per block, so that
+// the blocks of dense bands, which read their codes and weights again, each
+// keep a workgroup of their own).  Thread t copies record t of each staged
+// block, so a block's records go out as one run of lane-contiguous stores.
+
+constexpr int kEmitMax = 8;
 
 struct EmitArgs {
   const uint16_t* w;
@@ -498,53 +514,29 @@ struct EmitArgs {
   const uint16_t* stage;
   const uint32_t* stage_pos;
   uint32_t stage_cap;
+  uint32_t group;  // encode blocks per workgroup, 1..kEmitMax
+  uint32_t ahead;  // load every stage slot before the counts arrive
+  uint64_t nblk;
   uint64_t n;
   wc_header h;
 };
 
+// Block `blk`'s `cntb` records from `excl` on, and its index entries, when
+// they were not staged: the block's codes and the weights of its escapes are
+// read again.  Contains block barriers (call it block-uniformly).
 template <int LAYOUT>
-__global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
-  constexpr int kGroups = kPackBlock / 8;
+__device__ void emit_dense(const EmitArgs& a, uint64_t blk, uint32_t cntb, uint32_t excl,
+                           uint32_t (*wtot)[kBlockThreads / kWave], uint32_t* st_pos,
+                           uint16_t* st_sym) {
   constexpr int kShift = LAYOUT == WC_LAYOUT_K15 ? 7 : 8;
-  __shared__ uint32_t wtot[2][kBlockThreads / kWave];
-  // a dense tile's records: 8 KB of positions, 4 KB of symbols
-  __shared__ __attribute__((aligned(16))) uint32_t st_pos[2 * kGroups];
-  __shared__ __attribute__((aligned(16))) uint16_t st_sym[2 * kGroups];
   const int tid = threadIdx.x;
   const wc_header& h = a.h;
-  const uint64_t blk = blockIdx.x;
   const uint64_t w0 = blk * kPackBlock;
   const uint64_t n_tiles = (a.n + kTile - 1) / kTile;
   uint32_t* const index = (uint32_t*)(a.container + h.off_esc_idx);
-  const uint32_t cntb = a.cnt[blk];
-  const uint32_t excl = a.off[blk];
-  if (cntb == 0) {  // block-uniform: index entries only
-    if (tid < 4 && 4u * blk + (uint64_t)tid < n_tiles) index[4u * blk + tid] = excl;
-    return;
-  }
   uint32_t* pos = (uint32_t*)(a.container + h.off_esc_pos);
   uint8_t* sym = a.container + h.off_esc_sym;
   const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
-  if (cntb <= a.stage_cap) {  // block-uniform: the records k_pack staged, copied in order
-    if (tid < 4 && 4u * blk + (uint64_t)tid < n_tiles) {
-      uint32_t base = 0;
-      for (int q = 0; q < tid; ++q) base += a.tcnt[4u * blk + q];
-      index[4u * blk + tid] = excl + base;
-    }
-    const uint16_t* st = a.stage + blk * a.stage_cap;
-    const uint32_t* sp = a.stage_pos + blk * a.stage_cap;
-    for (uint32_t q = (uint32_t)tid; q < cntb; q += kBlockThreads) {
-      const uint64_t o = (uint64_t)excl + q;
-      if (o < h.n_esc) {
-        if (!compact) pos[o] = sp[q];
-        if (LAYOUT == WC_LAYOUT_K15)
-          ((uint16_t*)sym)[o] = st[q];
-        else
-          sym[o] = (uint8_t)st[q];
-      }
-    }
-    return;
-  }
   // the block's codes, in k_pack's group mapping; codes past n are 0
   const uint32_t* codes = (const uint32_t*)(a.container + h.off_codes) + w0 / 8;
   uint32_t emask[4];
@@ -570,7 +562,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
       for (int i = 0; gw + i < a.n; ++i) wd[j][i >> 1] |= (uint32_t)a.w[gw + i] << (16 * (i & 1));
     }
   }
-  auto sym_at = [&](int j, int i, uint32_t) -> uint32_t {
+  auto sym_at = [&](int j, int i) -> uint32_t {
     return ((wd[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) >> kShift;
   };
   if (cntb <= kDirectRecords) {
@@ -588,9 +580,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
         if (o < h.n_esc) {
           if (!compact) pos[o] = (uint32_t)(gw + (uint64_t)i);  // the compact form keeps symbols only
           if (LAYOUT == WC_LAYOUT_K15)
-            ((uint16_t*)sym)[o] = (uint16_t)sym_at(j, i, r);
+            ((uint16_t*)sym)[o] = (uint16_t)sym_at(j, i);
           else
-            sym[o] = (uint8_t)sym_at(j, i, r);
+            sym[o] = (uint8_t)sym_at(j, i);
         }
         ++r;
       }
@@ -610,7 +602,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
         const int i = __builtin_ctz(m);
         m &= m - 1u;
         st_pos[o] = (uint32_t)(gw + (uint64_t)i);
-        st_sym[o] = (uint16_t)sym_at(j, i, tb + o);
+        st_sym[o] = (uint16_t)sym_at(j, i);
         ++o;
       }
       __syncthreads();
@@ -626,6 +618,95 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
       }
       __syncthreads();
     }
+  }
+}
+
+template <int LAYOUT>
+__global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
+  constexpr int kGroups = kPackBlock / 8;
+  static_assert(WC_STAGE_SYMBOLS <= kBlockThreads, "one staged record of a block per thread");
+  __shared__ uint32_t wtot[2][kBlockThreads / kWave];
+  // a dense tile's records: 8 KB of positions, 4 KB of symbols
+  __shared__ __attribute__((aligned(16))) uint32_t st_pos[2 * kGroups];
+  __shared__ __attribute__((aligned(16))) uint16_t st_sym[2 * kGroups];
+  const int tid = threadIdx.x;
+  const wc_header& h = a.h;
+  const uint64_t n_tiles = (a.n + kTile - 1) / kTile;
+  const uint64_t b0 = (uint64_t)blockIdx.x * a.group;
+  const uint32_t nb = (uint32_t)(a.nblk - b0 < a.group ? a.nblk - b0 : a.group);
+  uint32_t* const index = (uint32_t*)(a.container + h.off_esc_idx);
+  uint32_t* pos = (uint32_t*)(a.container + h.off_esc_pos);
+  uint8_t* sym = a.container + h.off_esc_sym;
+  const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
+  // Thread t takes record t of each block's stage.  With `ahead` (many
+  // escapes) every stage load is issued before any count is known: the
+  // stage holds stage_cap records per block, so the loads stay inside it,
+  // and those past a block's count are not used.  Otherwise only the
+  // records that exist are loaded, once the counts are in.
+  uint32_t rs[kEmitMax], rp[kEmitMax];
+  const bool staging = a.stage_cap != 0;
+  auto load_stage = [&](int i) {
+    const uint64_t e = (b0 + (uint64_t)i) * a.stage_cap + (uint64_t)tid;
+    rs[i] = a.stage[e];
+    if (!compact) rp[i] = a.stage_pos[e];
+  };
+#pragma unroll
+  for (int i = 0; i < kEmitMax; ++i) {
+    rs[i] = rp[i] = 0;
+    if (a.ahead && staging && (uint32_t)i < nb && (uint32_t)tid < a.stage_cap) load_stage(i);
+  }
+  // index entries of the blocks that are not dense: lane 4i + j takes tile j of block i
+  uint32_t ix_cnt = 0, ix_off = 0;
+  uint64_t ix_tc = 0;
+  const bool ix = tid < 4 * (int)nb;
+  const uint64_t ix_blk = b0 + (uint64_t)(tid >> 2);
+  if (ix) {
+    ix_cnt = a.cnt[ix_blk];
+    ix_off = a.off[ix_blk];
+    if (staging) ix_tc = *(const uint64_t*)(a.tcnt + 4u * ix_blk);
+  }
+  // the group's counts and first records (uniform); dense: the blocks whose
+  // records were not staged
+  uint32_t c[kEmitMax], o[kEmitMax];
+  uint32_t dense = 0;
+#pragma unroll
+  for (int i = 0; i < kEmitMax; ++i) {
+    c[i] = (uint32_t)i < nb ? a.cnt[b0 + i] : 0u;
+    o[i] = (uint32_t)i < nb ? a.off[b0 + i] : 0u;
+    dense |= (c[i] <= a.stage_cap ? 0u : 1u) << i;
+  }
+  if (!a.ahead && staging) {
+#pragma unroll
+    for (int i = 0; i < kEmitMax; ++i)
+      if ((uint32_t)tid < c[i] && c[i] <= a.stage_cap) load_stage(i);
+  }
+  if (ix) {
+    const int j = tid & 3;
+    if (ix_cnt <= a.stage_cap && 4u * ix_blk + (uint64_t)j < n_tiles) {
+      uint32_t base = 0;
+      if (ix_cnt != 0)  // the tile counts were staged with the records
+        for (int q = 0; q < j; ++q) base += (uint32_t)(ix_tc >> (16 * q)) & 0xFFFFu;
+      index[4u * ix_blk + j] = ix_off + base;
+    }
+  }
+  if (staging) {
+#pragma unroll
+    for (int i = 0; i < kEmitMax; ++i) {
+      const uint64_t r = (uint64_t)o[i] + (uint64_t)tid;
+      if ((uint32_t)tid < c[i] && c[i] <= a.stage_cap && r < h.n_esc) {
+        if (!compact) pos[r] = rp[i];
+        if (LAYOUT == WC_LAYOUT_K15)
+          ((uint16_t*)sym)[r] = (uint16_t)rs[i];
+        else
+          sym[r] = (uint8_t)rs[i];
+      }
+    }
+  }
+  while (dense) {  // uniform
+    const int i = __builtin_ctz(dense);
+    dense &= dense - 1u;
+    const uint64_t blk = b0 + (uint64_t)i;
+    emit_dense<LAYOUT>(a, blk, a.cnt[blk], a.off[blk], wtot, st_pos, st_sym);
   }
 }
 
@@ -673,12 +754,19 @@ static hipError_t launch_encode_state(const wc_header& h, const uint16_t* w, uin
   e.stage = stage;
   e.stage_pos = stage_pos;
   e.stage_cap = stage_cap;
+  // kEmitMax blocks per workgroup, unless the escapes average more than a
+  // stage per block (dense bands) or nothing is staged
+  e.group = h.n_esc > (uint64_t)stage_cap * nblk ? 1u : (uint32_t)kEmitMax;
+  // stage slots loaded ahead when the blocks average a quarter stage or more
+  e.ahead = 4u * h.n_esc >= (uint64_t)stage_cap * nblk ? 1u : 0u;
+  e.nblk = nblk;
   e.n = h.n;
   e.h = h;
+  const dim3 egrid((unsigned)((nblk + e.group - 1) / e.group));
   if (h.layout == WC_LAYOUT_K15)
-    hipLaunchKernelGGL(k_emit<WC_LAYOUT_K15>, dim3((unsigned)nblk), dim3(kBlockThreads), 0, s, e);
+    hipLaunchKernelGGL(k_emit<WC_LAYOUT_K15>, egrid, dim3(kBlockThreads), 0, s, e);
   else
-    hipLaunchKernelGGL(k_emit<WC_LAYOUT_BYTESPLIT>, dim3((unsigned)nblk), dim3(kBlockThreads), 0, s, e);
+    hipLaunchKernelGGL(k_emit<WC_LAYOUT_BYTESPLIT>, egrid, dim3(kBlockThreads), 0, s, e);
   return hipGetLastError();
 }
 
