@@ -925,15 +925,16 @@ static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint3
 // LDS (fewer blocks per compute unit).  Measured (us, 4 vs 8 tiles): K15
 // fused on 6144 x 24576 265 -> 225 at batch 64 and 522 -> 462 at 256, but
 // 42 -> 49 on 4096 x 4096 at batch 64; byte-split fused 132 -> 155 and
-// 288 -> 326 on 6144 x 24576; the plain kernel 386 -> 340 at batch 256 and
-// 150 -> 166 at 64.
+// 288 -> 326 on 6144 x 24576.  The plain kernel, whose batch groups share
+// their weight lines in L2, takes 4 (batch 256: 6144 x 24576 banded 302 ->
+// 288 us, 4096 x 4096 50 -> 36; 14336 x 4096 103 either way).
 static_assert(WC_WIDE_NB == 0 || WC_WIDE_NB == 4 || WC_WIDE_NB == 8, "instantiated tile counts");
 static_assert(WC_WIDE_NW == 0 || WC_WIDE_NW == 2 || WC_WIDE_NW == 4, "instantiated wave counts");
 
 template <int LAYOUT, bool PLAIN>
 static int wide_tiles(const GemmArgs& a) {
   if (WC_WIDE_NB) return WC_WIDE_NB;
-  if (PLAIN) return a.batch >= 128 ? 8 : 4;
+  if (PLAIN) return 4;
   if (LAYOUT == WC_LAYOUT_K15) return a.batch > 64 || a.rows * a.cols >= (1ull << 26) ? 8 : 4;
   return 4;
 }
