@@ -871,15 +871,15 @@ static void launch_mfma(const GemmArgs& a, hipStream_t s) {
     constexpr int SP = WC_GEMM_PLAIN_SLICES;
     hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, true, SP, false>), g, dim3(kWave * SP), 0, s, a);
   } else {
-    // K15 on escape-heavy tensors (more than one weight in 32) whose rows of
-    // whole tiles split evenly over SC waves: contiguous per-wave ranges
-    // with cursors from the escape index, no count exchange.  Measured on
-    // the 6144 x 24576 banded tensor (5% escapes) at batch 16: 150 us with
-    // 4 waves, 158 with 12, 158 interleaved; byte-split there is faster
-    // interleaved (114 against 119 us with 4 contiguous waves), so it always
+    // K15 whose rows of whole tiles split evenly over SC waves: contiguous
+    // per-wave ranges with cursors from the escape index, no count exchange.
+    // Measured on the 6144 x 24576 banded tensor (5% escapes) at batch 16:
+    // 150 us with 4 waves, 158 with 6 or 12, 158 interleaved; on 6144 x 24576
+    // N(0, 0.02) (1.6% escapes) at batch 8: 121 against 128 interleaved
+    // (batch 16: 138 either way).  Byte-split is faster interleaved (banded,
+    // batch 16: 114 against 126 us with 6 contiguous waves), so it always
     // takes the interleaved ranges.
-    if (LAYOUT == WC_LAYOUT_K15 && a.cols % ((uint64_t)WC_INDEX_TILE * SC) == 0 &&
-        a.n_esc * 32 > a.rows * a.cols) {
+    if (LAYOUT == WC_LAYOUT_K15 && a.cols % ((uint64_t)WC_INDEX_TILE * SC) == 0) {
       hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, SC, true>), g, dim3(kWave * SC), 0, s, a);
       return;
     }
