@@ -919,7 +919,7 @@ static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint3
 #define WC_WIDE_SPLITS 2
 #endif
 
-// Wide batches: 4 or 8 batch tiles per block, 4 waves (64 rows) per block,
+// Wide batches: 2, 4 or 8 batch tiles per block, 4 waves (64 rows) per block,
 // or 2 when that leaves fewer than two blocks per compute unit.  Eight tiles
 // halve the decode work per product and the weight re-reads, at the cost of
 // LDS (fewer blocks per compute unit).  Measured (us, 4 vs 8 tiles): K15
@@ -928,13 +928,19 @@ static GemmArgs gemm_args(uint64_t rows, uint64_t cols, const uint16_t* x, uint3
 // 288 -> 326 on 6144 x 24576.  The plain kernel, whose batch groups share
 // their weight lines in L2, takes 4 (batch 256: 6144 x 24576 banded 302 ->
 // 288 us, 4096 x 4096 50 -> 36; 14336 x 4096 103 either way).
-static_assert(WC_WIDE_NB == 0 || WC_WIDE_NB == 4 || WC_WIDE_NB == 8, "instantiated tile counts");
+static_assert(WC_WIDE_NB == 0 || WC_WIDE_NB == 2 || WC_WIDE_NB == 4 || WC_WIDE_NB == 8,
+              "instantiated tile counts");
 static_assert(WC_WIDE_NW == 0 || WC_WIDE_NW == 2 || WC_WIDE_NW == 4, "instantiated wave counts");
 
 template <int LAYOUT, bool PLAIN>
 static int wide_tiles(const GemmArgs& a) {
   if (WC_WIDE_NB) return WC_WIDE_NB;
   if (PLAIN) return 4;
+  // tensors of 2^26 weights or more at batches up to 64: two tiles, so that
+  // twice the waves share the decode (6144 x 24576 banded, batch 32: 154 ->
+  // 142 us byte-split, 221 -> 204 K15; batch 64: 160 -> 156, 221 -> 211);
+  // on 4096 x 4096 two tiles measured slower (batch 64: 31 -> 35 us)
+  if (a.batch <= 64 && a.rows * a.cols >= (1ull << 26)) return 2;
   if (LAYOUT == WC_LAYOUT_K15) return a.batch > 64 || a.rows * a.cols >= (1ull << 26) ? 8 : 4;
   return 4;
 }
@@ -973,7 +979,11 @@ static void launch_wide(GemmArgs a, hipStream_t s) {
   const dim3 t(kWave * nw);
 #define WC_WIDE_LAUNCH(NW, NB) \
   hipLaunchKernelGGL((k_gemm_wide<LAYOUT, PLAIN, NW, NB, WC_WIDE_U>), g, t, 0, s, a)
-  if (nw == 4 && nb == 8)
+  if (nw == 4 && nb == 2)
+    WC_WIDE_LAUNCH(4, 2);
+  else if (nb == 2)
+    WC_WIDE_LAUNCH(2, 2);
+  else if (nw == 4 && nb == 8)
     WC_WIDE_LAUNCH(4, 8);
   else if (nw == 4)
     WC_WIDE_LAUNCH(4, 4);

@@ -26,7 +26,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import decode_gemv_sign_amd as wc  # noqa: E402
-from tests.test_gpu_parity import dev16, gpu_encode, oracle_gemv  # noqa: E402
+from tests.test_gpu_parity import DEV, dev16, gpu_encode, oracle_gemv  # noqa: E402
 
 LAYOUTS = [wc.BYTESPLIT, wc.K15]
 BATCHES = (17, 31, 32, 33, 64, 65, 100, 256)
@@ -109,6 +109,25 @@ def test_wide_banded_sampled():
             torch.cuda.synchronize()
             assert_gemv_close(y.cpu().numpy()[:, sample], y64[:batch], a[:batch],
                               f"banded layout {layout} b={batch}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wide_tall_sampled(layout):
+    """24576 x 6144 N(0, 0.015) (a tall tensor of the layer set, drawn on the
+    GPU): at batches up to 64 a tensor this large takes two batch tiles per
+    block, with 2 waves per block at batch 32 and 4 at batches 48 and 64 (two
+    batch groups); 256 sampled rows against the oracle."""
+    _, (rows, cols), w = synth.layerset_tensor_device(48, DEV)
+    h, c = wc.encode(w, layout)
+    X = synth.vectors(2700, 64, cols)
+    sample = np.sort(np.random.default_rng(10).choice(rows, 256, replace=False))
+    Ws = w.view(rows, cols)[torch.from_numpy(sample).to(DEV)].cpu().numpy().view(np.uint16)
+    y64, a = oracle.gemv_f64(np.ascontiguousarray(Ws), X)
+    for batch in (32, 48, 64):
+        y = wc.decode_gemv(h, c, rows, cols, dev16(X[:batch]))
+        torch.cuda.synchronize()
+        assert_gemv_close(y.cpu().numpy()[:, sample], y64[:batch], a[:batch],
+                          f"tall layout {layout} b={batch}")
 
 
 def test_wide_deterministic():
