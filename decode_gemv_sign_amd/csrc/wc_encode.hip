@@ -515,7 +515,7 @@ struct EmitArgs {
   const uint32_t* stage_pos;
   uint32_t stage_cap;
   uint32_t group;  // encode blocks per workgroup, 1..kEmitMax
-  uint32_t ahead;  // load every stage slot before the counts arrive
+  uint32_t ahead;  // stage slots (per block) loaded before the counts arrive, <= stage_cap
   uint64_t nblk;
   uint64_t n;
   wc_header h;
@@ -621,8 +621,9 @@ __device__ void emit_dense(const EmitArgs& a, uint64_t blk, uint32_t cntb, uint3
   }
 }
 
-template <int LAYOUT>
+template <int LAYOUT, int G>
 __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
+  static_assert(G >= 1 && G <= kEmitMax, "blocks per workgroup");
   constexpr int kGroups = kPackBlock / 8;
   static_assert(WC_STAGE_SYMBOLS <= kBlockThreads, "one staged record of a block per thread");
   __shared__ uint32_t wtot[2][kBlockThreads / kWave];
@@ -632,28 +633,29 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
   const int tid = threadIdx.x;
   const wc_header& h = a.h;
   const uint64_t n_tiles = (a.n + kTile - 1) / kTile;
-  const uint64_t b0 = (uint64_t)blockIdx.x * a.group;
-  const uint32_t nb = (uint32_t)(a.nblk - b0 < a.group ? a.nblk - b0 : a.group);
+  const uint64_t b0 = (uint64_t)blockIdx.x * G;
+  const uint32_t nb = (uint32_t)(a.nblk - b0 < (uint64_t)G ? a.nblk - b0 : (uint64_t)G);
   uint32_t* const index = (uint32_t*)(a.container + h.off_esc_idx);
   uint32_t* pos = (uint32_t*)(a.container + h.off_esc_pos);
   uint8_t* sym = a.container + h.off_esc_sym;
   const bool compact = (h.flags & WC_FLAG_COMPACT) != 0;
-  // Thread t takes record t of each block's stage.  With `ahead` (many
-  // escapes) every stage load is issued before any count is known: the
-  // stage holds stage_cap records per block, so the loads stay inside it,
-  // and those past a block's count are not used.  Otherwise only the
-  // records that exist are loaded, once the counts are in.
-  uint32_t rs[kEmitMax], rp[kEmitMax];
+  // Thread t takes record t of each block's stage.  Threads below `ahead`
+  // issue their stage loads before any count is known (the stage holds
+  // stage_cap records per block, so the loads stay inside it, and those past
+  // a block's count are not used); the others load only records that exist,
+  // once the counts are in.
+  uint32_t rs[G], rp[G];
   const bool staging = a.stage_cap != 0;
+  const bool early = (uint32_t)tid < a.ahead;
   auto load_stage = [&](int i) {
     const uint64_t e = (b0 + (uint64_t)i) * a.stage_cap + (uint64_t)tid;
     rs[i] = a.stage[e];
     if (!compact) rp[i] = a.stage_pos[e];
   };
 #pragma unroll
-  for (int i = 0; i < kEmitMax; ++i) {
+  for (int i = 0; i < G; ++i) {
     rs[i] = rp[i] = 0;
-    if (a.ahead && staging && (uint32_t)i < nb && (uint32_t)tid < a.stage_cap) load_stage(i);
+    if (early && staging && (uint32_t)i < nb) load_stage(i);
   }
   // index entries of the blocks that are not dense: lane 4i + j takes tile j of block i
   uint32_t ix_cnt = 0, ix_off = 0;
@@ -667,17 +669,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
   }
   // the group's counts and first records (uniform); dense: the blocks whose
   // records were not staged
-  uint32_t c[kEmitMax], o[kEmitMax];
+  uint32_t c[G], o[G];
   uint32_t dense = 0;
 #pragma unroll
-  for (int i = 0; i < kEmitMax; ++i) {
+  for (int i = 0; i < G; ++i) {
     c[i] = (uint32_t)i < nb ? a.cnt[b0 + i] : 0u;
     o[i] = (uint32_t)i < nb ? a.off[b0 + i] : 0u;
     dense |= (c[i] <= a.stage_cap ? 0u : 1u) << i;
   }
-  if (!a.ahead && staging) {
+  if (!early && staging) {
 #pragma unroll
-    for (int i = 0; i < kEmitMax; ++i)
+    for (int i = 0; i < G; ++i)
       if ((uint32_t)tid < c[i] && c[i] <= a.stage_cap) load_stage(i);
   }
   if (ix) {
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_emit(EmitArgs a) {
   }
   if (staging) {
 #pragma unroll
-    for (int i = 0; i < kEmitMax; ++i) {
+    for (int i = 0; i < G; ++i) {
       const uint64_t r = (uint64_t)o[i] + (uint64_t)tid;
       if ((uint32_t)tid < c[i] && c[i] <= a.stage_cap && r < h.n_esc) {
         if (!compact) pos[r] = rp[i];
@@ -757,16 +759,32 @@ static hipError_t launch_encode_state(const wc_header& h, const uint16_t* w, uin
   // kEmitMax blocks per workgroup, unless the escapes average more than a
   // stage per block (dense bands) or nothing is staged
   e.group = h.n_esc > (uint64_t)stage_cap * nblk ? 1u : (uint32_t)kEmitMax;
-  // stage slots loaded ahead when the blocks average a quarter stage or more
-  e.ahead = 4u * h.n_esc >= (uint64_t)stage_cap * nblk ? 1u : 0u;
+  // Stage slots loaded ahead of the counts: all of them when the blocks of
+  // a sparse tensor average a quarter stage or more (6144x24576 N(0,0.015)
+  // K15, 160 records per block: 14.1 -> 10.5 us), none when they average
+  // less (byte-split there, 2 per block: 7.6 against 8.2 us with all); with
+  // dense bands (one block per workgroup), whose other blocks hold few
+  // records, the first 64 (all slots: 6144x24576 banded byte-split 45 ->
+  // 56 us).
+  e.ahead = e.group == 1u ? (stage_cap < 64u ? stage_cap : 64u)
+            : 4u * h.n_esc >= (uint64_t)stage_cap * nblk ? stage_cap : 0u;
   e.nblk = nblk;
   e.n = h.n;
   e.h = h;
   const dim3 egrid((unsigned)((nblk + e.group - 1) / e.group));
-  if (h.layout == WC_LAYOUT_K15)
-    hipLaunchKernelGGL(k_emit<WC_LAYOUT_K15>, egrid, dim3(kBlockThreads), 0, s, e);
-  else
-    hipLaunchKernelGGL(k_emit<WC_LAYOUT_BYTESPLIT>, egrid, dim3(kBlockThreads), 0, s, e);
+  // (one block per workgroup has its own instance: the group's arrays would
+  // take registers from the dense path and halve the waves per SIMD)
+  if (h.layout == WC_LAYOUT_K15) {
+    if (e.group == 1)
+      hipLaunchKernelGGL((k_emit<WC_LAYOUT_K15, 1>), egrid, dim3(kBlockThreads), 0, s, e);
+    else
+      hipLaunchKernelGGL((k_emit<WC_LAYOUT_K15, kEmitMax>), egrid, dim3(kBlockThreads), 0, s, e);
+  } else {
+    if (e.group == 1)
+      hipLaunchKernelGGL((k_emit<WC_LAYOUT_BYTESPLIT, 1>), egrid, dim3(kBlockThreads), 0, s, e);
+    else
+      hipLaunchKernelGGL((k_emit<WC_LAYOUT_BYTESPLIT, kEmitMax>), egrid, dim3(kBlockThreads), 0, s, e);
+  }
   return hipGetLastError();
 }
 
