@@ -59,6 +59,7 @@ WORKLOADS = {
     "square": "4096x4096 N(0,0.02), 1% zeros, 0.1% outliers N(0,2); batch 1",
     "mlp": "14336x4096 + 4096x14336, row std 10^U(-4,-1); batch 1",
     "banded": "6144x24576 N(0,0.02) + 5% escapes in 64-row bands; batch 1/4/16",
+    "layer": "6144x24576 N(0,0.015), the layer set's first tensor (host draw); batch 1..256",
     "layerset": "96 tensors, 20.25 GiB: 48 x (6144x24576), 24 x (24576x6144) N(0,0.015), "
                 "24 x [6144] N(1,0.05); streamed encode + decode, per-tensor dictionaries",
 }
@@ -102,6 +103,9 @@ def load_workload(name: str, batch: int):
         d = synth.banded()
         # the same draw as the workload's own x, extended to `batch` rows
         return [d["W"]], synth.vectors(synth.SEEDS["banded"], batch, d["W"].shape[1])
+    if name == "layer":
+        _, W = synth.layerset_tensor(0)
+        return [W], synth.vectors(synth.SEEDS["layerset"], batch, W.shape[1])
     raise ValueError(name)
 
 

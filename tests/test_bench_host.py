@@ -13,7 +13,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-@pytest.mark.parametrize("workload,batches", [("small", (1, 17, 256)), ("square", (1, 64))])
+@pytest.mark.parametrize("workload,batches", [("small", (1, 17, 256)), ("square", (1, 64)), ("layer", (256,))])
 def test_workload_x_has_the_requested_batch(workload, batches):
     for batch in batches:
         mats, x = bench.load_workload(workload, batch)
