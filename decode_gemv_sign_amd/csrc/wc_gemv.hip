@@ -421,6 +421,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     const EscBatch eb = ring_read_esc<LAYOUT>(buf, e, (CMP ? 0ull : a.n_esc), a.esc_last);
     uint32_t xb1[kXpf ? 1 : 16];
     if (!kXpf && B == 1) load_x_lane(a.x + pc.ct * kTile, lg, xb1);
+    // Batches 2..4: x of the first XE batch rows issued now, in flight during
+    // the rebuild and patch (both rows at batch 2, one above, where more
+    // registers cost waves).  6144 x 24576 banded: batch 2 66.6 -> 64.3 us
+    // byte-split, 68.9 -> 67.6 K15; batch 4 K15 86.1 -> 84.3.
+    constexpr int XE = B == 2 ? 2 : (B > 2 ? 1 : 0);
+    uint32_t xe[XE > 0 ? XE : 1][16];
+#pragma unroll
+    for (int b = 0; b < XE; ++b)
+      load_x_lane(xrow(pc.r) + (uint64_t)b * (SPLIT ? a.x_cols : a.cols) + pc.ct * kTile, lg, xe[b]);
     uint32_t marks[kLaneGroups];
     const bool any = escape_marks(l, marks);
     const uint32_t cnt_wave = __ballot(any) ? wave_total(count_marks(marks)) : 0u;
@@ -470,9 +479,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
     } else {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        uint32_t xb[16];
-        load_x_lane(xrow(pc.r) + (uint64_t)b * (SPLIT ? a.x_cols : a.cols) + pc.ct * kTile, lg, xb);
-        acc[b] = dot_lane(w, xb, acc[b]);
+        if (b < XE) {
+          acc[b] = dot_lane(w, xe[b < XE ? b : 0], acc[b]);
+        } else {
+          uint32_t xb[16];
+          load_x_lane(xrow(pc.r) + (uint64_t)b * (SPLIT ? a.x_cols : a.cols) + pc.ct * kTile, lg, xb);
+          acc[b] = dot_lane(w, xb, acc[b]);
+        }
       }
     }
     if (pc.ct + 1 == tpr) {
@@ -675,11 +688,19 @@ __global__ void k_fill_zero(float* y, uint64_t count) {
 // ---- launchers -----------------------------------------------------------
 
 // Batches from this size on take the matrix-core kernels of wc_gemm.hip
-// (when cols is a multiple of 32).
+// (when cols is a multiple of 32): the fused kernel from 5, where the 1D
+// kernels need two passes over W (6144 x 24576 banded, batch 5: 133 -> 94
+// us byte-split, 144 -> 126 K15; at batch 4 the LDS ring is faster there,
+// 84 against 92), the plain one from 4 (86 -> 84 us; 4096 x 4096 13.0 ->
+// 9.8).  Unused lanes of the 16-wide batch operand re-read x row 0.
 #ifndef WC_MFMA_MIN_BATCH
-#define WC_MFMA_MIN_BATCH 8
+#define WC_MFMA_MIN_BATCH 5
+#endif
+#ifndef WC_MFMA_MIN_BATCH_PLAIN
+#define WC_MFMA_MIN_BATCH_PLAIN 4
 #endif
 constexpr uint32_t kMfmaMinBatch = WC_MFMA_MIN_BATCH;
+constexpr uint32_t kMfmaMinBatchPlain = WC_MFMA_MIN_BATCH_PLAIN;
 // Rows of whole tiles take the LDS-ring kernel.
 #ifndef WC_GEMV_RING
 #define WC_GEMV_RING 1
@@ -740,15 +761,15 @@ template <int LAYOUT, bool CMP>
 static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
   GemvArgs a = a0;
   a.rows_per_wave = rows_per_wave(a.rows, a.cols);
-  // Batch sizes 1, 2, 4, 8 and 16 have their own kernels; other sizes run as
-  // a sum of those over consecutive slices of x and y.
+  // Batch sizes 1, 2, 3, 4, 8 and 16 have their own kernels; other sizes run
+  // as a sum of those over consecutive slices of x and y.
   uint32_t done = 0;
   while (done < a.batch) {
     const uint32_t left = a.batch - done;
     GemvArgs p = a;
     p.x = a.x + (uint64_t)done * a.cols;
     p.y = a.y + (uint64_t)done * a.rows;
-    uint32_t b = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
+    uint32_t b = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left;
     p.batch = b;
     const dim3 g = wave_grid(a.rows, a.rows_per_wave), t(kBlockThreads);
     // (batches of 8 and 16 with whole-tile rows take the matrix-core kernel)
@@ -772,6 +793,7 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
       } else {
         switch (b) {
           case 4: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, false>), g, t, 0, s, p); break;
+          case 3: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, false>), g, t, 0, s, p); break;
           case 2: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2, CMP, false>), g, t, 0, s, p); break;
           default: hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, false>), g, t, 0, s, p); break;
         }
@@ -781,6 +803,7 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
         case 16: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 16, CMP>), g, t, 0, s, p); break;
         case 8: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 8, CMP>), g, t, 0, s, p); break;
         case 4: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 4, CMP>), g, t, 0, s, p); break;
+        case 3: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 3, CMP>), g, t, 0, s, p); break;
         case 2: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 2, CMP>), g, t, 0, s, p); break;
         default: hipLaunchKernelGGL((k_decode_gemv<LAYOUT, 1, CMP>), g, t, 0, s, p); break;
       }
@@ -882,7 +905,7 @@ hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, con
     }
     return hipSuccess;
   }
-  if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
+  if (batch >= kMfmaMinBatchPlain && gemm_mfma_fits(rows, cols, batch))
     return launch_gemm_bf16_mfma(w, rows, cols, x, batch, y, s);
   GemvArgs a = {};
   a.w = w;
@@ -902,13 +925,14 @@ hipError_t launch_gemv_bf16(const uint16_t* w, uint64_t rows, uint64_t cols, con
     GemvArgs p = a;
     p.x = x + (uint64_t)done * cols;
     p.y = y + (uint64_t)done * rows;
-    uint32_t b = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
+    uint32_t b = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left;
     p.batch = b;
     const dim3 g = wave_grid(rows, a.rows_per_wave), t(kBlockThreads);
     switch (b) {
       case 16: hipLaunchKernelGGL(k_gemv_bf16<16>, g, t, 0, s, p); break;
       case 8: hipLaunchKernelGGL(k_gemv_bf16<8>, g, t, 0, s, p); break;
       case 4: hipLaunchKernelGGL(k_gemv_bf16<4>, g, t, 0, s, p); break;
+      case 3: hipLaunchKernelGGL(k_gemv_bf16<3>, g, t, 0, s, p); break;
       case 2: hipLaunchKernelGGL(k_gemv_bf16<2>, g, t, 0, s, p); break;
       default: hipLaunchKernelGGL(k_gemv_bf16<1>, g, t, 0, s, p); break;
     }
