@@ -840,7 +840,7 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
 #endif
 
 #ifndef WC_GEMM_PLAIN_SLICES
-#define WC_GEMM_PLAIN_SLICES 4
+#define WC_GEMM_PLAIN_SLICES 0  // waves per block of the plain kernel: 0 = chosen by shape
 #endif
 
 #ifndef WC_GEMM_CONTIG_SLICES
@@ -854,13 +854,25 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
 // 45.1, 6144 x 24576 banded 116.8 / 114.0 / 116.1, 14336 x 4096 54.7 /
 // 54.0 / 40.9; K15 4096 x 4096 18.2 / 18.2 / 19.3, 4096 x 14336 49.6 / 48.7 /
 // 53.5, 6144 x 24576 N(0, 0.015) 140.5 / 151.5 / 138.5, 14336 x 4096 67.3 /
-// 66.7 / 53.0.  The plain kernel takes 4 waves everywhere (5-10% faster
-// than 8 on all four shapes).
+// 66.7 / 53.0.  Grids of more than 768 blocks take 2 (14336 x 4096 at
+// batch 16: 41.1 -> 38.1 us byte-split, 53.7 -> 51.3 K15; 24576 x 6144:
+// 84.7 -> 82.9, 106.6 -> 105.4).  The plain kernel takes 2 waves on grids of
+// up to 1024 blocks with rows of up to 16384 columns, else 4 (batch 16:
+// 4096 x 4096 11.8 -> 11.2 us, 14336 x 4096 40.4 -> 38.5, 4096 x 14336
+// 36.9 -> 34.1; 6144 x 24576 117 against 123 with 2; 8 or 12 waves were
+// slower everywhere).
 static int mfma_slices(int layout, uint64_t rows) {
   if (WC_GEMM_SLICES) return WC_GEMM_SLICES;
   const uint64_t blocks = (rows + kMRows - 1) / kMRows;
+  if (blocks > 768) return 2;
   if (layout == WC_LAYOUT_K15) return blocks <= 256 ? 12 : 4;
   return blocks <= 512 ? 6 : 4;
+}
+
+static int mfma_plain_slices(uint64_t rows, uint64_t cols) {
+  if (WC_GEMM_PLAIN_SLICES) return WC_GEMM_PLAIN_SLICES;
+  const uint64_t blocks = (rows + kMRows - 1) / kMRows;
+  return blocks <= 1024 && cols <= 16384 ? 2 : 4;
 }
 
 template <int LAYOUT, bool PLAIN>
@@ -868,8 +880,10 @@ static void launch_mfma(const GemmArgs& a, hipStream_t s) {
   const dim3 g((unsigned)((a.rows + kMRows - 1) / kMRows));
   constexpr int SC = WC_GEMM_CONTIG_SLICES;
   if constexpr (PLAIN) {
-    constexpr int SP = WC_GEMM_PLAIN_SLICES;
-    hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, true, SP, false>), g, dim3(kWave * SP), 0, s, a);
+    if (mfma_plain_slices(a.rows, a.cols) == 2)
+      hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, true, 2, false>), g, dim3(kWave * 2), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, true, 4, false>), g, dim3(kWave * 4), 0, s, a);
   } else {
     // K15 whose rows of whole tiles split evenly over SC waves: contiguous
     // per-wave ranges with cursors from the escape index, no count exchange.
@@ -886,6 +900,7 @@ static void launch_mfma(const GemmArgs& a, hipStream_t s) {
     switch (mfma_slices(LAYOUT, a.rows)) {
       case 12: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 12, false>), g, dim3(kWave * 12), 0, s, a); break;
       case 6: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 6, false>), g, dim3(kWave * 6), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 2, false>), g, dim3(kWave * 2), 0, s, a); break;
       default: hipLaunchKernelGGL((k_gemm_mfma<LAYOUT, false, 4, false>), g, dim3(kWave * 4), 0, s, a); break;
     }
   }
