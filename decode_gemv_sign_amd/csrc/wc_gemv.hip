@@ -837,7 +837,13 @@ hipError_t launch_decode_gemv(const wc_header& h, const uint8_t* container, uint
     }
     return hipSuccess;
   }
-  if (batch >= kMfmaMinBatch && gemm_mfma_fits(rows, cols, batch))
+  // Batch 4 also takes the matrix cores on grids of 384 row blocks or more
+  // when fewer than one weight in 64 escapes (6144 x 24576 N(0, 0.015)
+  // byte-split: 82.6 -> 77.8 us; 14336 x 4096 byte-split 34.9 -> 31.7); with
+  // denser escapes (the banded tensor, K15 at 2%) or on smaller grids
+  // (4096 x 4096: 10.8 against 12.5) the LDS ring is faster.
+  const bool mfma4 = batch == 4 && rows >= 384u * 16u && 64u * h.n_esc < h.n;
+  if ((batch >= kMfmaMinBatch || mfma4) && gemm_mfma_fits(rows, cols, batch))
     return launch_decode_gemm_mfma(h, container, rows, cols, x, batch, y, s);
   GemvArgs a{};
   a.codes = container + h.off_codes;

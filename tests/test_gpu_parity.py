@@ -547,6 +547,26 @@ def test_workload_layerset_tensors(t):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("t", [0, 48])
+def test_gemv_layerset_sampled(layout, t):
+    """The layer set's 6144 x 24576 and 24576 x 6144 tensors (drawn on the
+    GPU) at batches 1, 4 and 16: byte-split at batch 4 takes the matrix
+    cores on grids this large (fewer than one weight in 64 escapes), K15
+    the LDS ring; 256 sampled rows against the oracle."""
+    _, (rows, cols), w = synth.layerset_tensor_device(t, DEV)
+    h, c = wc.encode(w, layout)
+    X = synth.vectors(2800 + t, 16, cols)
+    sample = np.sort(np.random.default_rng(11 + t).choice(rows, 256, replace=False))
+    Ws = w.view(rows, cols)[torch.from_numpy(sample).to(DEV)].cpu().numpy().view(np.uint16)
+    y64, a = oracle.gemv_f64(np.ascontiguousarray(Ws), X)
+    for batch in (1, 4, 16):
+        y = wc.decode_gemv(h, c, rows, cols, dev16(X[:batch]))
+        torch.cuda.synchronize()
+        assert_gemv_close(y.cpu().numpy()[:, sample], y64[:batch], a[:batch],
+                          f"layerset {t} layout {layout} b={batch}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 def test_workload_banded(layout):
     d = synth.banded()
     W = d["W"]
