@@ -290,8 +290,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
 // p * a.cols on, and the waves of the block that hold one row's parts add
 // their sums in LDS in column order, so the result does not depend on which
 // wave ends first.  Measured at batch 4 on 6144 x 24576 (4 parts of 3
-// tiles): 82 against 87 us byte-split, 89 against 91 K15; at batch 1 it was
-// slower (57 against 50), so batch 1 keeps whole rows.
+// tiles): 82 against 87 us byte-split, 89 against 91 K15; 2 parts of 6 are
+// faster still (the launcher's numbers).  At batch 1 it was slower (57
+// against 50 with 4 parts), so batches 1 and 2 keep whole rows.
 template <int LAYOUT, int B, bool CMP, bool SPLIT, uint32_t SLOT = kRingSlotDwords>
 __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) {
   // 16-byte chunks of symbol run a slot takes ahead (wc_tile.h run_ahead)
@@ -709,7 +710,7 @@ constexpr bool kGemvRing = WC_GEMV_RING;
 #ifndef WC_SPLIT_MIN_TILES
 #define WC_SPLIT_MIN_TILES 4
 #endif
-constexpr uint64_t kSplitMinTiles = WC_SPLIT_MIN_TILES;  // rows of more tiles are split at batch 4
+constexpr uint64_t kSplitMinTiles = WC_SPLIT_MIN_TILES;  // rows of more tiles are split at batches 3 and 4
 
 static dim3 row_grid(uint64_t rows) {
   const uint64_t wpb = kBlockThreads / kWave;
@@ -774,10 +775,15 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
     const dim3 g = wave_grid(a.rows, a.rows_per_wave), t(kBlockThreads);
     // (batches of 8 and 16 with whole-tile rows take the matrix-core kernel)
     if (kGemvRing && a.cols % kTile == 0 && b <= 4) {
-      // Batch 4 on rows of more than kSplitMinTiles tiles: each row split into
-      // 4 (or 2) parts of whole tiles, one wave each (see the kernel).
+      // Batches 3 and 4 on rows of more than kSplitMinTiles tiles: each row
+      // split into 2 parts of whole tiles, one wave each (see the kernel).
+      // Two parts measured faster than four (6144 x 24576 banded, batch 4:
+      // 85.3 -> 82.7 us byte-split, 86.8 -> 84.9 K15; N(0, 0.015) K15 85.5 ->
+      // 81.5) and, at batch 3, than whole rows (banded 76.3 -> 72.0, 79.5 ->
+      // 74.3); at batches 1 and 2 they cost 3-7% on tensors without dense
+      // escape rows, which keep whole rows.
       const uint64_t tpr = a.cols / kTile;
-      const uint32_t wpr = b == 4 && tpr > kSplitMinTiles ? (tpr % 4 == 0 ? 4u : tpr % 2 == 0 ? 2u : 1u) : 1u;
+      const uint32_t wpr = (b == 4 || b == 3) && tpr > kSplitMinTiles && tpr % 2 == 0 ? 2u : 1u;
       const uint64_t waves = (a.rows + a.rows_per_wave - 1) / a.rows_per_wave;
       if (wpr > 1) {
         GemvArgs v = p;
@@ -786,7 +792,10 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
         v.rows = a.rows * wpr;
         v.cols = a.cols / wpr;
         v.rows_per_wave = 1;
-        hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
+        if (b == 4)
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
+        else
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
       } else if (ring_big_slots(LAYOUT, b, waves, a.rows_per_wave * tpr)) {
         if constexpr (LAYOUT == WC_LAYOUT_BYTESPLIT)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, false, kRingBigSlotDwords>), g, t, 0, s, p);

@@ -197,17 +197,19 @@ def test_gemv_shapes_and_batches(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_gemv_split_rows_batch4(layout):
-    """Batch 4 on rows of more than 4 whole tiles runs each row as 4 (or 2)
-    parts on separate waves whose sums meet in LDS: odd row counts (a block
-    with an unused part), 2- and 4-way splits, an escape-dense row, both
-    escape forms; bit-identical on a second launch."""
-    for i, (rows, tiles) in enumerate([(5, 12), (7, 6), (1, 8), (3, 10), (9, 16)]):
+@pytest.mark.parametrize("batch", [3, 4])
+def test_gemv_split_rows_batch4(layout, batch):
+    """Batches 3 and 4 on rows of more than 4 whole tiles (an even number)
+    run each row as 2 parts on separate waves whose sums meet in LDS: odd
+    row counts (a block with unused waves), an escape-dense row, an odd
+    tile count (whole rows), both escape forms; bit-identical on a second
+    launch."""
+    for i, (rows, tiles) in enumerate([(5, 12), (7, 6), (1, 8), (3, 10), (9, 16), (4, 7)]):
         cols = 2048 * tiles
         W = synth.random_bits(rows * cols, 950 + i, "normal").reshape(rows, cols)
         W.reshape(-1)[::97] ^= 0x3000
         W[rows // 2] = synth.random_bits(cols, 960 + i, "uniform") & np.uint16(0xBFFF)
-        x = synth.vectors(970 + i, 4, cols)
+        x = synth.vectors(970 + i, batch, cols)
         y, _ = check_gemv(layout, W, x, what=f"split {rows}x{cols}")
         for form in (0, wc.COMPACT):
             h, c = wc.encode(dev16(W.reshape(-1)), layout | form)
