@@ -782,8 +782,14 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
       // 81.5) and, at batch 3, than whole rows (banded 76.3 -> 72.0, 79.5 ->
       // 74.3); at batches 1 and 2 they cost 3-7% on tensors without dense
       // escape rows, which keep whole rows.
+      // K15 at batch 1 splits escape-rich tensors (more than one weight in
+      // 32), whose dense rows make long waves: 6144 x 24576 banded 56.7 ->
+      // 55.7 us. Byte-split there keeps whole rows in the large ring slots
+      // (50.5 us whole, 54.3 split).
       const uint64_t tpr = a.cols / kTile;
-      const uint32_t wpr = (b == 4 || b == 3) && tpr > kSplitMinTiles && tpr % 2 == 0 ? 2u : 1u;
+      const bool split_b = b == 4 || b == 3 ||
+                           (LAYOUT == WC_LAYOUT_K15 && b == 1 && 32u * a.n_esc > a.rows * a.cols);
+      const uint32_t wpr = split_b && tpr > kSplitMinTiles && tpr % 2 == 0 ? 2u : 1u;
       const uint64_t waves = (a.rows + a.rows_per_wave - 1) / a.rows_per_wave;
       if (wpr > 1) {
         GemvArgs v = p;
@@ -794,8 +800,10 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
         v.rows_per_wave = 1;
         if (b == 4)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
-        else
+        else if (b == 3)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
+        else
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
       } else if (ring_big_slots(LAYOUT, b, waves, a.rows_per_wave * tpr)) {
         if constexpr (LAYOUT == WC_LAYOUT_BYTESPLIT)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, false, kRingBigSlotDwords>), g, t, 0, s, p);

@@ -197,12 +197,13 @@ def test_gemv_shapes_and_batches(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("batch", [3, 4])
-def test_gemv_split_rows_batch4(layout, batch):
-    """Batches 3 and 4 on rows of more than 4 whole tiles (an even number)
-    run each row as 2 parts on separate waves whose sums meet in LDS: odd
-    row counts (a block with unused waves), an escape-dense row, an odd
-    tile count (whole rows), both escape forms; bit-identical on a second
+@pytest.mark.parametrize("batch", [1, 3, 4])
+def test_gemv_split_rows(layout, batch):
+    """Batches 3 and 4, and K15 at batch 1 when more than one weight in 32
+    escapes (true here: one row is escape-dense), on rows of more than 4 whole tiles
+    (an even number) run each row as 2 parts on separate waves whose sums
+    meet in LDS: odd row counts (a block with unused waves), an odd tile
+    count (whole rows), both escape forms; bit-identical on a second
     launch."""
     for i, (rows, tiles) in enumerate([(5, 12), (7, 6), (1, 8), (3, 10), (9, 16), (4, 7)]):
         cols = 2048 * tiles
