@@ -597,8 +597,10 @@ __global__ __launch_bounds__(kWave * NW) void k_gemm_wide(GemmArgs a) {
       }
     } else if constexpr (kK15) {
       const uint32_t* rp = (const uint32_t*)(a.raw + 7 * (e / 8));  // 28 bytes, 4-aligned
-      const u32x4 v0 = wide_load<kK15>((const u32x4a4*)rp);
-      const u32x3 v1 = wide_load<kK15>((const u32x3a4*)(rp + 4));
+      // (non-temporal, as wide_load takes K15 loads; called directly so the
+      // pointer types keep their 4-byte alignment)
+      const u32x4 v0 = __builtin_nontemporal_load((const u32x4a4*)rp);
+      const u32x3 v1 = __builtin_nontemporal_load((const u32x3a4*)(rp + 4));
       w[0] = v0[0]; w[1] = v0[1]; w[2] = v0[2]; w[3] = v0[3];
       w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2];
     } else {
