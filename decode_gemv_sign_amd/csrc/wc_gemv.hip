@@ -292,9 +292,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv(GemvArgs a) {
 // wave ends first.  Measured at batch 4 on 6144 x 24576 (4 parts of 3
 // tiles): 82 against 87 us byte-split, 89 against 91 K15; 2 parts of 6 are
 // faster still (the launcher's numbers).  At batch 1 it was slower (57
-// against 50 with 4 parts), so batches 1 and 2 keep whole rows.
-template <int LAYOUT, int B, bool CMP, bool SPLIT, uint32_t SLOT = kRingSlotDwords>
-__global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) {
+// against 50 with 4 parts); with 2 parts it pays only for K15 on tensors
+// with dense escape rows (the launcher's rule).
+template <int LAYOUT, int B, bool CMP, bool SPLIT, uint32_t SLOT = kRingSlotDwords,
+          int WPB = kBlockThreads / kWave>
+__global__ __launch_bounds__(kWave * WPB) void k_decode_gemv_ring(GemvArgs a) {
   // 16-byte chunks of symbol run a slot takes ahead (wc_tile.h run_ahead)
   constexpr uint32_t kAheadChunks = (4 * SLOT - 3104) / 16;
   static_assert(kAheadChunks >= 66 && kAheadChunks <= 128, "slot sizes of the ring");
@@ -302,14 +304,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
   // tile is in registers)
   constexpr uint32_t kAheadCap = run_ahead_syms(kAheadChunks, LAYOUT);
   __shared__ uint32_t T2[256];
-  __shared__ __attribute__((aligned(16))) uint32_t ring0[kBlockThreads / kWave][SLOT];
-  __shared__ __attribute__((aligned(16))) uint32_t ring1[kBlockThreads / kWave][SLOT];
-  __shared__ float part_sum[kBlockThreads / kWave][SPLIT ? B : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t ring0[WPB][SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t ring1[WPB][SLOT];
+  __shared__ float part_sum[WPB][SPLIT ? B : 1];
 
   const int lane = lane_id();
   const int wib = wave_in_block();
-  const uint64_t wave = (uint64_t)blockIdx.x * (kBlockThreads / kWave) + (uint64_t)wib;
-  const uint64_t r0 = wave * a.rows_per_wave;
+  // SPLIT in 8-wave blocks: the block holds 8 / wpr whole rows, part-major
+  // (waves 0 .. rpb - 1 take part 0 of consecutive rows, and so on), so the
+  // waves of one part read the same x columns.  4-wave blocks keep a row's
+  // parts on neighbouring waves (rpb = 1), measured 2% faster there (K15,
+  // banded 6144 x 24576, batch 4).
+  constexpr bool kPartMajor = SPLIT && WPB == 8;
+  const uint32_t rpb = kPartMajor ? (uint32_t)WPB / a.wpr : 1u;
+  const uint64_t r0 = kPartMajor ? ((uint64_t)blockIdx.x * rpb + (uint32_t)wib % rpb) * a.wpr + (uint32_t)wib / rpb
+                                 : ((uint64_t)blockIdx.x * WPB + (uint64_t)wib) * a.rows_per_wave;
   // Every thread of the block builds its share of the pair table and
   // reaches the barrier after it (waves without rows, in the else branch);
   // waves with rows issue their first loads before that.
@@ -522,7 +531,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_decode_gemv_ring(GemvArgs a) 
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         float t = part_sum[wib][b];
-        for (uint32_t k = 1; k < a.wpr; ++k) t += part_sum[wib + k][b];
+        for (uint32_t k = 1; k < a.wpr; ++k) t += part_sum[wib + k * rpb][b];
         a.y[(uint64_t)b * rows_real + r0 / a.wpr] = t;
       }
     }
@@ -798,7 +807,20 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
         v.rows = a.rows * wpr;
         v.cols = a.cols / wpr;
         v.rows_per_wave = 1;
-        if (b == 4)
+        // Batches 3 and 4 in blocks of 8 waves (4 rows, part-major: the 4
+        // waves of a part read the same x columns), except K15 with more
+        // than one weight in 32 escaping, whose slow dense rows would hold
+        // twice the LDS until their block ends.  6144 x 24576 byte-split:
+        // banded batch 4 82.6 -> 81.6 us (batch 3 the same); N(0, 0.015)
+        // batch 3 69.2 -> 65.3; K15 N(0, 0.015) batch 4 81.7 -> 79.5, batch 3
+        // 70.4 -> 68.5; K15 banded batch 4 85.0 -> 86.6 (kept at 4).
+        const bool eight = b >= 3 && (LAYOUT == WC_LAYOUT_BYTESPLIT || 32u * a.n_esc <= a.rows * a.cols);
+        const dim3 g8((unsigned)((v.rows + 7) / 8)), t8(8 * kWave);
+        if (b == 4 && eight)
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true, kRingSlotDwords, 8>), g8, t8, 0, s, v);
+        else if (b == 3 && eight)
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, true, kRingSlotDwords, 8>), g8, t8, 0, s, v);
+        else if (b == 4)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
         else if (b == 3)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);

@@ -199,8 +199,9 @@ def test_gemv_shapes_and_batches(layout):
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("batch", [1, 3, 4])
 def test_gemv_split_rows(layout, batch):
-    """Batches 3 and 4, and K15 at batch 1 when more than one weight in 32
-    escapes (true here: one row is escape-dense), on rows of more than 4 whole tiles
+    """Batches 3 and 4 (8-wave blocks for byte-split, 4 for K15 here), and
+    K15 at batch 1 when more than one weight in 32 escapes (true here: one
+    row is escape-dense), on rows of more than 4 whole tiles
     (an even number) run each row as 2 parts on separate waves whose sums
     meet in LDS: odd row counts (a block with unused waves), an odd tile
     count (whole rows), both escape forms; bit-identical on a second
@@ -553,16 +554,17 @@ def test_workload_layerset_tensors(t):
 @pytest.mark.parametrize("t", [0, 48])
 def test_gemv_layerset_sampled(layout, t):
     """The layer set's 6144 x 24576 and 24576 x 6144 tensors (drawn on the
-    GPU) at batches 1, 4 and 16: byte-split at batch 4 takes the matrix
+    GPU) at batches 1, 3, 4 and 16: byte-split at batch 4 takes the matrix
     cores on grids this large (fewer than one weight in 64 escapes), K15
-    the LDS ring; 256 sampled rows against the oracle."""
+    the LDS ring (at batches 3 and 4 the 6144 x 24576 rows split in two, in
+    blocks of 8 waves); 256 sampled rows against the oracle."""
     _, (rows, cols), w = synth.layerset_tensor_device(t, DEV)
     h, c = wc.encode(w, layout)
     X = synth.vectors(2800 + t, 16, cols)
     sample = np.sort(np.random.default_rng(11 + t).choice(rows, 256, replace=False))
     Ws = w.view(rows, cols)[torch.from_numpy(sample).to(DEV)].cpu().numpy().view(np.uint16)
     y64, a = oracle.gemv_f64(np.ascontiguousarray(Ws), X)
-    for batch in (1, 4, 16):
+    for batch in (1, 3, 4, 16):
         y = wc.decode_gemv(h, c, rows, cols, dev16(X[:batch]))
         torch.cuda.synchronize()
         assert_gemv_close(y.cpu().numpy()[:, sample], y64[:batch], a[:batch],
