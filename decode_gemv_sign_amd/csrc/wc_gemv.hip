@@ -789,14 +789,17 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
       // Two parts measured faster than four (6144 x 24576 banded, batch 4:
       // 85.3 -> 82.7 us byte-split, 86.8 -> 84.9 K15; N(0, 0.015) K15 85.5 ->
       // 81.5) and, at batch 3, than whole rows (banded 76.3 -> 72.0, 79.5 ->
-      // 74.3); at batches 1 and 2 they cost 3-7% on tensors without dense
-      // escape rows, which keep whole rows.
+      // 74.3); at batches 1 and 2, in 4-wave blocks, they cost 3-7% on
+      // tensors without dense escape rows.
       // K15 at batch 1 splits escape-rich tensors (more than one weight in
       // 32), whose dense rows make long waves: 6144 x 24576 banded 56.7 ->
       // 55.7 us. Byte-split there keeps whole rows in the large ring slots
       // (50.5 us whole, 54.3 split).
       const uint64_t tpr = a.cols / kTile;
-      const bool split_b = b == 4 || b == 3 ||
+      // Byte-split at batch 2 splits too, in 8-wave blocks (6144 x 24576
+      // N(0, 0.015) 56.3 -> 54.5 us, banded 1-4% faster in two runs; K15 the
+      // same or slower there).
+      const bool split_b = b == 4 || b == 3 || (b == 2 && LAYOUT == WC_LAYOUT_BYTESPLIT) ||
                            (LAYOUT == WC_LAYOUT_K15 && b == 1 && 32u * a.n_esc > a.rows * a.cols);
       const uint32_t wpr = split_b && tpr > kSplitMinTiles && tpr % 2 == 0 ? 2u : 1u;
       const uint64_t waves = (a.rows + a.rows_per_wave - 1) / a.rows_per_wave;
@@ -807,24 +810,26 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
         v.rows = a.rows * wpr;
         v.cols = a.cols / wpr;
         v.rows_per_wave = 1;
-        // Batches 3 and 4 in blocks of 8 waves (4 rows, part-major: the 4
+        // Batches 2 to 4 in blocks of 8 waves (4 rows, part-major: the 4
         // waves of a part read the same x columns), except K15 with more
         // than one weight in 32 escaping, whose slow dense rows would hold
         // twice the LDS until their block ends.  6144 x 24576 byte-split:
         // banded batch 4 82.6 -> 81.6 us (batch 3 the same); N(0, 0.015)
         // batch 3 69.2 -> 65.3; K15 N(0, 0.015) batch 4 81.7 -> 79.5, batch 3
         // 70.4 -> 68.5; K15 banded batch 4 85.0 -> 86.6 (kept at 4).
-        const bool eight = b >= 3 && (LAYOUT == WC_LAYOUT_BYTESPLIT || 32u * a.n_esc <= a.rows * a.cols);
+        const bool eight = b >= 2 && (LAYOUT == WC_LAYOUT_BYTESPLIT || 32u * a.n_esc <= a.rows * a.cols);
         const dim3 g8((unsigned)((v.rows + 7) / 8)), t8(8 * kWave);
         if (b == 4 && eight)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true, kRingSlotDwords, 8>), g8, t8, 0, s, v);
         else if (b == 3 && eight)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, true, kRingSlotDwords, 8>), g8, t8, 0, s, v);
+        else if (b == 2 && eight)
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2, CMP, true, kRingSlotDwords, 8>), g8, t8, 0, s, v);
         else if (b == 4)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
         else if (b == 3)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
-        else
+        else  // batch 1 (batch 2 splits only in 8-wave blocks)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
       } else if (ring_big_slots(LAYOUT, b, waves, a.rows_per_wave * tpr)) {
         if constexpr (LAYOUT == WC_LAYOUT_BYTESPLIT)

@@ -197,11 +197,11 @@ def test_gemv_shapes_and_batches(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("batch", [1, 3, 4])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
 def test_gemv_split_rows(layout, batch):
-    """Batches 3 and 4 (8-wave blocks for byte-split, 4 for K15 here), and
-    K15 at batch 1 when more than one weight in 32 escapes (true here: one
-    row is escape-dense), on rows of more than 4 whole tiles
+    """Batches 3 and 4 (8-wave blocks for byte-split, 4 for K15 here),
+    byte-split at batch 2 (8-wave blocks), and K15 at batch 1 when more than
+    one weight in 32 escapes (true here: one row is escape-dense), on rows of more than 4 whole tiles
     (an even number) run each row as 2 parts on separate waves whose sums
     meet in LDS: odd row counts (a block with unused waves), an odd tile
     count (whole rows), both escape forms; bit-identical on a second
