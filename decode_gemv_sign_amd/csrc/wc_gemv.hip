@@ -817,7 +817,9 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
         // banded batch 4 82.6 -> 81.6 us (batch 3 the same); N(0, 0.015)
         // batch 3 69.2 -> 65.3; K15 N(0, 0.015) batch 4 81.7 -> 79.5, batch 3
         // 70.4 -> 68.5; K15 banded batch 4 85.0 -> 86.6 (kept at 4).
-        const bool eight = b >= 2 && (LAYOUT == WC_LAYOUT_BYTESPLIT || 32u * a.n_esc <= a.rows * a.cols);
+        // (a block must hold whole rows: wpr divides its wave count)
+        const bool eight = b >= 2 && 8u % wpr == 0 &&
+                           (LAYOUT == WC_LAYOUT_BYTESPLIT || 32u * a.n_esc <= a.rows * a.cols);
         const dim3 g8((unsigned)((v.rows + 7) / 8)), t8(8 * kWave);
         if (b == 4 && eight)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true, kRingSlotDwords, 8>), g8, t8, 0, s, v);
@@ -829,7 +831,9 @@ static void launch_fused_fast(const GemvArgs& a0, hipStream_t s) {
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 4, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
         else if (b == 3)
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 3, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
-        else  // batch 1 (batch 2 splits only in 8-wave blocks)
+        else if (b == 2)
+          hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 2, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
+        else
           hipLaunchKernelGGL((k_decode_gemv_ring<LAYOUT, 1, CMP, true>), wave_grid(v.rows, 1), t, 0, s, v);
       } else if (ring_big_slots(LAYOUT, b, waves, a.rows_per_wave * tpr)) {
         if constexpr (LAYOUT == WC_LAYOUT_BYTESPLIT)
